@@ -1,0 +1,196 @@
+"""Oracle-side packer/unpacker for the compressed-cache byte layout.
+
+TEST INFRASTRUCTURE (same rules as oracle.codec): written independently of the HIP
+library from the layout definition below, in plain Python/NumPy bit operations.
+
+The TurboAngle abstract (arXiv 2603.27467) stores codes but fixes no byte format; the
+format here is this library's own, chosen so that a 64-lane wave reads it coalesced.
+
+Layout of one layer's cache: [batch][kv_head][tile][tile bytes], tile = 64 token slots,
+tiles_per_seq = ceil(capacity / 64). P = d / 2 pairs, bk / bv = angle code widths.
+One tile holds six planes, in this order:
+
+  KA  key angle codes     token-major words: word w of token t at 4*(w*64 + t);
+                          token t's bit string (P*bk bits, LSB first) holds pair i's
+                          code in bits [i*bk, (i+1)*bk)
+  KR  key radius codes    token-major words: word w of token t at 4*(w*64 + t);
+                          byte j of word w is the 8-bit code of pair 4w + j
+  KS  key scale           64 fp16 values, token t at byte 2t
+  VA  value angle codes   pair-major words: word w of pair i at 4*(w*P + i);
+                          pair i's bit string (64*bv bits, LSB first) holds token t's
+                          code in bits [t*bv, (t+1)*bv)
+  VR  value radius codes  pair-major words: word w of pair i at 4*(w*P + i);
+                          token t's 4-bit code in bits [4t, 4t+4) of pair i's string
+  VP  value parameters    64 x (s_min fp16, s_max fp16), token t at byte 4t
+
+Bit strings are little-endian: bit b is bit (b mod 32) of word b // 32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import code_bits
+
+TILE = 64
+
+
+def plane_sizes(d: int, n_k: int, n_v: int) -> dict:
+    p = d // 2
+    bk, bv = code_bits(n_k), code_bits(n_v)
+    if (p * bk) % 32 or (p * bv) % 32 or p % 4:
+        raise ValueError("layout needs P*bits to fill whole 32-bit words (d >= 64)")
+    return {
+        "KA": TILE * p * bk // 8,
+        "KR": TILE * p,
+        "KS": 2 * TILE,
+        "VA": p * 2 * bv * 4,
+        "VR": p * 8 * 4,
+        "VP": 4 * TILE,
+    }
+
+
+def tile_bytes(d: int, n_k: int, n_v: int) -> int:
+    return sum(plane_sizes(d, n_k, n_v).values())
+
+
+def cache_bytes(d: int, n_k: int, n_v: int, batch: int, hkv: int, capacity: int) -> int:
+    tiles = (capacity + TILE - 1) // TILE
+    return batch * hkv * tiles * tile_bytes(d, n_k, n_v)
+
+
+def _offsets(d, n_k, n_v):
+    off, acc = {}, 0
+    for k, v in plane_sizes(d, n_k, n_v).items():
+        off[k] = acc
+        acc += v
+    return off
+
+
+def _bits_to_words(codes: np.ndarray, width: int) -> np.ndarray:
+    """Pack a 1-D array of codes into little-endian 32-bit words, LSB first."""
+    nbits = len(codes) * width
+    words = np.zeros((nbits + 31) // 32, dtype=np.uint64)
+    for idx, c in enumerate(codes.astype(np.uint64)):
+        pos = idx * width
+        w, sh = pos // 32, pos % 32
+        words[w] |= (c << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + width > 32:
+            words[w + 1] |= c >> np.uint64(32 - sh)
+    return words.astype(np.uint32)
+
+
+def _words_to_bits(words: np.ndarray, width: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.int64)
+    w64 = words.astype(np.uint64)
+    mask = (1 << width) - 1
+    for idx in range(count):
+        pos = idx * width
+        w, sh = pos // 32, pos % 32
+        v = int(w64[w]) >> sh
+        if sh + width > 32:
+            v |= int(w64[w + 1]) << (32 - sh)
+        out[idx] = v & mask
+    return out
+
+
+def pack_tile(d, n_k, n_v, k_angle, k_radius, k_scale, v_angle, v_radius, v_smin, v_smax):
+    """Pack up to 64 tokens of one (batch, kv head) into one tile's bytes.
+
+    k_angle, k_radius, v_angle, v_radius: int [ntok, P]; k_scale, v_smin, v_smax: [ntok]
+    float values that are exactly representable in fp16. Slots >= ntok are zero.
+    """
+    p = d // 2
+    bk, bv = code_bits(n_k), code_bits(n_v)
+    ntok = k_angle.shape[0]
+    off = _offsets(d, n_k, n_v)
+    buf = np.zeros(tile_bytes(d, n_k, n_v), dtype=np.uint8)
+    u32 = buf.view(np.uint32)
+
+    wk = p * bk // 32
+    for t in range(ntok):
+        words = _bits_to_words(k_angle[t], bk)
+        for w in range(wk):
+            u32[(off["KA"] // 4) + w * TILE + t] = words[w]
+        words = _bits_to_words(k_radius[t], 8)
+        for w in range(p // 4):
+            u32[(off["KR"] // 4) + w * TILE + t] = words[w]
+    ks = np.zeros(TILE, dtype=np.float16)
+    ks[:ntok] = np.asarray(k_scale, dtype=np.float64)
+    buf[off["KS"]:off["KS"] + 2 * TILE] = ks.view(np.uint8)
+
+    va = np.zeros((p, TILE), dtype=np.int64)
+    vr = np.zeros((p, TILE), dtype=np.int64)
+    va[:, :ntok] = v_angle.T
+    vr[:, :ntok] = v_radius.T
+    for i in range(p):
+        words = _bits_to_words(va[i], bv)
+        for w in range(2 * bv):
+            u32[(off["VA"] // 4) + w * p + i] = words[w]
+        words = _bits_to_words(vr[i], 4)
+        for w in range(8):
+            u32[(off["VR"] // 4) + w * p + i] = words[w]
+    vp = np.zeros((TILE, 2), dtype=np.float16)
+    vp[:ntok, 0] = np.asarray(v_smin, dtype=np.float64)
+    vp[:ntok, 1] = np.asarray(v_smax, dtype=np.float64)
+    buf[off["VP"]:off["VP"] + 4 * TILE] = vp.reshape(-1).view(np.uint8)
+    return buf
+
+
+def unpack_tile(d, n_k, n_v, buf, ntok=TILE) -> dict:
+    """Inverse of pack_tile for the first ntok token slots of one tile."""
+    p = d // 2
+    bk, bv = code_bits(n_k), code_bits(n_v)
+    off = _offsets(d, n_k, n_v)
+    buf = np.ascontiguousarray(np.asarray(buf, dtype=np.uint8))
+    u32 = buf.view(np.uint32)
+    wk = p * bk // 32
+
+    k_angle = np.empty((ntok, p), dtype=np.int64)
+    k_radius = np.empty((ntok, p), dtype=np.int64)
+    for t in range(ntok):
+        words = np.array([u32[(off["KA"] // 4) + w * TILE + t] for w in range(wk)])
+        k_angle[t] = _words_to_bits(words, bk, p)
+        words = np.array([u32[(off["KR"] // 4) + w * TILE + t] for w in range(p // 4)])
+        k_radius[t] = _words_to_bits(words, 8, p)
+    k_scale = buf[off["KS"]:off["KS"] + 2 * TILE].view(np.float16)[:ntok].astype(np.float64)
+
+    v_angle = np.empty((ntok, p), dtype=np.int64)
+    v_radius = np.empty((ntok, p), dtype=np.int64)
+    for i in range(p):
+        words = np.array([u32[(off["VA"] // 4) + w * p + i] for w in range(2 * bv)])
+        v_angle[:, i] = _words_to_bits(words, bv, TILE)[:ntok]
+        words = np.array([u32[(off["VR"] // 4) + w * p + i] for w in range(8)])
+        v_radius[:, i] = _words_to_bits(words, 4, TILE)[:ntok]
+    vp = buf[off["VP"]:off["VP"] + 4 * TILE].view(np.float16).reshape(TILE, 2)
+    return {
+        "k_angle": k_angle, "k_radius": k_radius, "k_scale": k_scale,
+        "v_angle": v_angle, "v_radius": v_radius,
+        "v_smin": vp[:ntok, 0].astype(np.float64), "v_smax": vp[:ntok, 1].astype(np.float64),
+    }
+
+
+def unpack_cache(cache: np.ndarray, d, n_k, n_v, batch, hkv, capacity, t0, ntok) -> dict:
+    """Unpack tokens [t0, t0 + ntok) of every (batch, kv head) from a whole layer's
+    cache bytes. Returns arrays shaped [batch, ntok, hkv, P] (codes) / [batch, ntok, hkv]."""
+    tb = tile_bytes(d, n_k, n_v)
+    tiles = (capacity + TILE - 1) // TILE
+    cache = np.asarray(cache, dtype=np.uint8).reshape(batch, hkv, tiles, tb)
+    p = d // 2
+    out = {k: np.empty((batch, ntok, hkv, p), dtype=np.int64)
+           for k in ("k_angle", "k_radius", "v_angle", "v_radius")}
+    for k in ("k_scale", "v_smin", "v_smax"):
+        out[k] = np.empty((batch, ntok, hkv), dtype=np.float64)
+    for b in range(batch):
+        for h in range(hkv):
+            for tile in range(t0 // TILE, (t0 + ntok + TILE - 1) // TILE if ntok else 0):
+                u = unpack_tile(d, n_k, n_v, cache[b, h, tile])
+                lo = max(t0, tile * TILE)
+                hi = min(t0 + ntok, tile * TILE + TILE)
+                src = slice(lo - tile * TILE, hi - tile * TILE)
+                dst = slice(lo - t0, hi - t0)
+                for k in ("k_angle", "k_radius", "v_angle", "v_radius"):
+                    out[k][b, dst, h] = u[k][src]
+                for k in ("k_scale", "v_smin", "v_smax"):
+                    out[k][b, dst, h] = u[k][src]
+    return out
