@@ -1,0 +1,238 @@
+"""Benchmark of the angle-quantised KV-cache hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, all layers:
+  encode   K/V [B, T, Hkv, d] fp16 -> packed cache (kvq_encode), every layer
+  attend   one decode query per sequence over the full compressed cache
+           (kvq_attn_prepare + kvq_attn_split + kvq_attn_merge), every layer
+  dequant  packed cache -> fp16 K/V (kvq_decode), every layer
+Inputs and caches are resident in HBM before timing starts. `value` is decode-attention
+throughput in GB/s of compressed cache read per second over the attention phase of a
+step (all layers, every launch and gap included). Phase times come from HIP events on
+the stream the library launches on. The split kernel (the dominant attention kernel)
+is bracketed by its own events for the roofline figure.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mistral7b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attn cache GB/s (% HBM peak); encode tokens/s"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mistral7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def record_bytes(d, n_k, n_v, tokens):
+    """Algorithmic compressed bytes of `tokens` token-heads (one record per token-head)."""
+    import rotated_angle_quantization_amd as kvq
+    return tokens * kvq.tile_bytes(d, n_k, n_v) // 64
+
+
+def cpu_baseline(cfg, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the same workload: decode
+    attention from packed bytes for one (batch, kv head) over a token prefix, and
+    encode of a token sample. Single-threaded BLAS."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import codec as oc
+    from oracle import layout as ol
+    from synthetic import layer_kv, query
+
+    layer = cfg.boosted_layers  # first non-boosted layer
+    n_k, n_v = cfg.bins(layer)
+    d, g = cfg.d, cfg.group
+    sg = oc.layer_signs(0, layer, d)
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        # a token prefix of one (batch 0, kv head 0) sequence, generated on the CPU
+        tokens = 4096
+        k, v = layer_kv(cfg, layer, "cpu", seq=tokens, batch=1)
+        q = query(cfg, layer, "cpu", batch=1)[:, :g]
+        xk = k[0, :, 0].double().numpy()
+        xv = v[0, :, 0].double().numpy()
+        # encode sample (oracle), then pack with the oracle's packer to get bytes
+        t0 = time.perf_counter()
+        ek, ev = oc.encode_k(xk, sg, n_k), oc.encode_v(xv, sg, n_v)
+        enc_s = time.perf_counter() - t0
+        tiles = []
+        for t in range(tokens // 64):
+            s = slice(t * 64, t * 64 + 64)
+            tiles.append(ol.pack_tile(d, n_k, n_v, ek["angle"][s], ek["radius"][s],
+                                      ek["scale"][s], ev["angle"][s], ev["radius"][s],
+                                      ev["s_min"][s], ev["s_max"][s]))
+        cache = np.stack(tiles)
+        # decode attention from bytes, repeated to fill the time budget
+        reps, att_s = 0, 0.0
+        qn = q.double().numpy()
+        while att_s < budget_s and reps < 1000:
+            t0 = time.perf_counter()
+            u = ol.unpack_tiles(cache, d, n_k, n_v)
+            u = {kk: vv.reshape((tokens,) + vv.shape[2:]) for kk, vv in u.items()}
+            kh = oc.dequant_k(u["k_angle"], u["k_radius"], u["k_scale"], n_k, sg)
+            vh = oc.dequant_v(u["v_angle"], u["v_radius"], u["v_smin"], u["v_smax"], n_v, sg)
+            oc.attention(qn, kh[None, :, None], vh[None, :, None])
+            att_s += time.perf_counter() - t0
+            reps += 1
+    gbps = reps * record_bytes(d, n_k, n_v, tokens) / att_s / 1e9
+    return {
+        "value": gbps, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{cfg.name} layer {layer}: oracle decode attention from packed bytes "
+                   f"(unpack + dequant + attention for G={g} query heads) over {tokens} "
+                   f"tokens of one (batch, kv head), repeated {reps}x in {att_s:.1f} s; "
+                   f"oracle encode of the same {tokens} K/V token-heads took {enc_s:.2f} s"),
+        "encode_token_heads_per_s": tokens / enc_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(no sharding or collectives); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rotated_angle_quantization_amd as kvq
+    from synthetic import get, layer_kv, query
+
+    cfg = get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, B, T, Hkv, Hq, d = cfg.layers, cfg.batch, cfg.seq, cfg.hkv, cfg.hq, cfg.d
+    print(f"[bench] workload {cfg.name}: L={L} B={B} T={T} Hkv={Hkv} Hq={Hq} d={d}",
+          file=sys.stderr, flush=True)
+
+    descs, caches, ks, vs, qs = [], [], [], [], []
+    for layer in range(L):
+        n_k, n_v = cfg.bins(layer)
+        desc = kvq.make_desc(d, Hkv, B, T, n_k, n_v, layer, 0)
+        descs.append(desc)
+        caches.append(kvq.alloc_cache(desc, dev))
+        k, v = layer_kv(cfg, layer, dev)
+        ks.append(k)
+        vs.append(v)
+        qs.append(query(cfg, layer, dev))
+    ws_bytes = max(kvq.attn_workspace_bytes(dd, Hq, T) for dd in descs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    kd = torch.empty((B, T, Hkv, d), dtype=torch.float16, device=dev)
+    vd = torch.empty_like(kd)
+    torch.cuda.synchronize()
+    cache_bytes_total = sum(c.numel() for c in caches)
+    attn_bytes = sum(record_bytes(d, *cfg.bins(layer), B * Hkv * T) for layer in range(L))
+    print(f"[bench] inputs ready: cache {cache_bytes_total / 1e9:.2f} GB "
+          f"({attn_bytes / 1e9:.3f} GB algorithmic per attention sweep)", file=sys.stderr,
+          flush=True)
+
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record):
+        e = [Ev() for _ in range(4)]
+        split_ev = [(Ev(), Ev()) for _ in range(L)]
+        e[0].record()
+        for layer in range(L):
+            kvq.encode(descs[layer], caches[layer], ks[layer], vs[layer], 0)
+        e[1].record()
+        for layer in range(L):
+            kvq.attn_prepare(descs[layer], qs[layer], T, ws)
+            split_ev[layer][0].record()
+            kvq.attn_split(descs[layer], caches[layer], Hq, T, ws)
+            split_ev[layer][1].record()
+            kvq.attn_merge(descs[layer], Hq, T, outs, ws)
+        e[2].record()
+        for layer in range(L):
+            kvq.decode(descs[layer], caches[layer], 0, T, out=(kd, vd))
+        e[3].record()
+        if record is not None:
+            record.append((e, split_ev))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e, _ in recs) / args.steps
+    att_ms = sum(e[1].elapsed_time(e[2]) for e, _ in recs) / args.steps
+    deq_ms = sum(e[2].elapsed_time(e[3]) for e, _ in recs) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[3]) for e, _ in recs) / args.steps
+    split_ms = [a.elapsed_time(b) for _, sp in recs for a, b in sp]
+    split_avg_ms = sum(split_ms) / len(split_ms)
+    split_bytes_avg = attn_bytes / L
+
+    attn_gbps = attn_bytes / (att_ms * 1e-3) / 1e9
+    achieved = split_bytes_avg / (split_avg_ms * 1e-3) / 1e9
+    tokens = B * T
+    result = {
+        "metric": METRIC,
+        "value": round(attn_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {L} layers, batch {B}, seq {T}, {Hkv} kv heads, "
+                         f"{Hq} query heads, d={d}, fp16 K/V, per-layer (n_K, n_V) = "
+                         f"{sorted(set(cfg.bins(x) for x in range(L)))}"),
+            "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
+            "encode_decisions": "f64", "attention_arithmetic": "f32",
+        },
+        "hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "encode_tokens_per_s": round(tokens / (enc_ms * 1e-3), 1),
+        "encode_ms": round(enc_ms, 4),
+        "attn_ms": round(att_ms, 4),
+        "dequant_ms": round(deq_ms, 4),
+        "dequant_out_GBps": round(2 * L * B * T * Hkv * d * 2 / (deq_ms * 1e-3) / 1e9, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "kernel": "attn_split_kernel (kvq_attn_split)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(split_avg_ms, 5),
+            "bytes_per_launch": split_bytes_avg,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle CPU baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * kvq.h - C ABI of libkvq: an angle-quantised, bit-packed KV cache for AMD MI355X
+ * (gfx950), with decode attention that runs directly on the packed codes.
+ *
+ * The codec is the one described in "TurboAngle: Near-Lossless KV Cache Compression
+ * via Uniform Angle Quantization" (arXiv 2603.27467), Abstract: each head vector is
+ * multiplied by a seeded random sign diagonal and put through a normalised fast
+ * Walsh-Hadamard transform; neighbouring coordinates are paired into (radius, angle);
+ * each angle is rounded to one of n evenly spaced directions (n set per layer and
+ * separately for K and V); key radii get 8 linear bits against a per-vector fp16
+ * scale, value radii 4 bits on a log scale between per-vector fp16 min and max.
+ * Attention reconstructs keys and values from the codes on the fly and never writes
+ * a dequantised cache, the property stressed for fused codec kernels in "OCTOPUS:
+ * Joint Triplet Quantization for KV Cache via Octahedral Parametrization" (TL;DR and
+ * Why it matters).
+ *
+ * Readings of steps the abstract leaves open (bin placement, tie rules, fp16
+ * parameters, sign generator, byte layout) are stated at each declaration.
+ *
+ * General conventions
+ *  - Every buffer is owned by the caller: the cache, inputs, outputs and workspace.
+ *    The library allocates no device memory, keeps no mutable global state and
+ *    never synchronises. All device pointers must come from hipMalloc-class
+ *    allocations on the current device.
+ *  - Device work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *    stream). KVQ_OK means the work was enqueued; kernel faults surface at the
+ *    caller's next synchronisation on that stream.
+ *  - Arguments are validated on the host before any HIP call; a rejected call
+ *    enqueues nothing. Calls are thread-safe and re-entrant.
+ *  - Inputs must be finite; non-finite values are outside the contract.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_TILE_TOKENS 64
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, stride or alignment */
+  KVQ_ERR_UNSUPPORTED = 2,      /* valid request that this build has no kernel for */
+  KVQ_ERR_CAPACITY = 3,         /* token range beyond the cache capacity */
+  KVQ_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required */
+  KVQ_ERR_HIP = 5               /* the HIP runtime rejected a launch */
+} kvq_status;
+
+typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+/*
+ * One layer's compressed cache. Plain data: read during a call, never retained.
+ *  head_dim     d; 64 or 128 (a power of two; the pairing needs d even).
+ *  num_kv_heads Hkv >= 1.  batch B >= 1.
+ *  capacity     token slots per (batch, kv head), >= 1; rounded up to whole tiles
+ *               of 64 slots in the byte layout.
+ *  n_bins_k/v   angle bins n for K and V, in [2, 256]; each code takes ceil(log2 n)
+ *               bits (per-layer early boost = a different pair per layer).
+ *  layer, seed  select the sign diagonal (see kvq_layer_signs).
+ */
+typedef struct {
+  uint32_t head_dim;
+  uint32_t num_kv_heads;
+  uint32_t batch;
+  uint32_t capacity;
+  uint32_t n_bins_k;
+  uint32_t n_bins_v;
+  uint32_t layer;
+  uint32_t reserved; /* must be 0 */
+  uint64_t seed;
+} kvq_layer_desc;
+
+int kvq_abi_version(void);
+const char* kvq_status_string(kvq_status status);
+
+/*
+ * Bytes of one layer's cache, or 0 if the descriptor is invalid. Host only.
+ *
+ * Byte layout (this library's own; the abstract fixes no format). P = d/2 pairs,
+ * bk = ceil(log2 n_bins_k), bv = ceil(log2 n_bins_v). The cache is
+ * [batch][kv_head][tile][tile_bytes], tile = 64 token slots. A tile holds, in order:
+ *   KA key angle codes   token-major 32-bit words: word w of slot t at 4*(w*64+t);
+ *                        slot t's bit string (P*bk bits) has pair i's code at bits
+ *                        [i*bk, (i+1)*bk)
+ *   KR key radius codes  token-major words, word w of slot t at 4*(w*64+t); byte j
+ *                        of word w = 8-bit code of pair 4w+j
+ *   KS key scale         fp16 per slot, slot t at 2t
+ *   VA value angle codes pair-major words: word w of pair i at 4*(w*P+i); pair i's
+ *                        bit string (64*bv bits) has slot t's code at [t*bv, (t+1)*bv)
+ *   VR value radius codes pair-major words: word w of pair i at 4*(w*P+i); slot t's
+ *                        4-bit code at bits [4t, 4t+4)
+ *   VP value parameters  (s_min fp16, s_max fp16) per slot, slot t at 4t
+ * Bit strings are little-endian (bit b = bit b%32 of word b/32). Key planes are
+ * token-major so a wave reads them with one lane per token; value planes are
+ * pair-major so a wave reads them with one lane per pair.
+ */
+size_t kvq_cache_bytes(const kvq_layer_desc* desc);
+
+/* Bytes of one 64-slot tile (see kvq_cache_bytes), or 0 if invalid. Host only. */
+size_t kvq_tile_bytes(uint32_t head_dim, uint32_t n_bins_k, uint32_t n_bins_v);
+
+/*
+ * The sign diagonal of (seed, layer), written to out_host[0..d) as +1 / -1.
+ * Host only. Reading of the abstract's random diagonal rotation: one diagonal per
+ * layer, shared by K, V and all heads, drawn with SplitMix64 (Steele, Lea, Flood,
+ * OOPSLA 2014): mix(z) adds 0x9E3779B97F4A7C15 then applies the two published
+ * xor-shift-multiply rounds; sign[i] = -1 iff bit 63 of mix(mix(seed ^ layer) + i)
+ * is set. d must be a power of two in [1, 4096].
+ */
+kvq_status kvq_layer_signs(uint64_t seed, uint32_t layer, uint32_t d, int8_t* out_host);
+
+/*
+ * Encode (append) tokens [t0, t0 + ntok) of K and V into the cache.
+ *
+ * k, v: device tensors of shape [B, ntok, Hkv, d] with element strides
+ * (stride_b, stride_t, stride_h) shared by k and v, and d contiguous; element
+ * [b, j, h, e] is at k + b*stride_b + j*stride_t + h*stride_h + e. dtype f16 or f32.
+ * Pointers must be aligned to two elements and the strides even.
+ *
+ * Per (token, kv head) vector x (TurboAngle, Abstract, with this library's readings):
+ *   y = H_d (sign * x) / sqrt(d)           natural (Sylvester) order
+ *   pair i = (y[2i], y[2i+1]); r = hypot; theta = atan2(y[2i+1], y[2i])
+ *   angle code = floor(theta * n / (2 pi) + 1/2) mod n; zero pair -> 0
+ *     (bin centres at 2 pi c / n)
+ *   keys:   s = fp16(max r) (round to nearest even, saturated at 65504);
+ *           radius code = clamp(floor(255 r / s + 1/2), 0, 255); s = 0 -> codes 0
+ *   values: s_max = fp16(max r), s_min = fp16(max(min r, 2^-14));
+ *           L = ln(s_max / s_min); code = 0 if r < s_min, else
+ *           clamp(floor(15 ln(r / s_min) / L + 1/2), 0, 15); s_max <= s_min -> 0
+ * All decisions are taken in IEEE binary64, so codes are reproducible across runs
+ * and launch shapes. Slots outside [t0, t0 + ntok) are left unchanged, so a
+ * chunked append produces the same bytes as a one-shot encode.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (d not 64/128), CAPACITY (t0 + ntok >
+ * capacity), HIP. ntok = 0 enqueues nothing and returns KVQ_OK.
+ */
+kvq_status kvq_encode(const kvq_layer_desc* desc, void* cache, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t stride_b, int64_t stride_t,
+                      int64_t stride_h, uint32_t t0, uint32_t ntok, void* hip_stream);
+
+/*
+ * Dequantise tokens [t0, t0 + ntok) back to vectors: x_hat = sign * H_d y_hat / sqrt(d)
+ * with y_hat[2i] = r_hat cos(2 pi c / n), y_hat[2i+1] = r_hat sin(2 pi c / n);
+ * key r_hat = code * s / 255; value r_hat = s_min * exp(code * L / 15) (s_max when
+ * s_max <= s_min). Arithmetic in fp32.
+ * k_out, v_out: contiguous device tensors [B, ntok, Hkv, d] of out_dtype.
+ * Errors: as kvq_encode.
+ */
+kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out,
+                      void* v_out, kvq_dtype out_dtype, uint32_t t0, uint32_t ntok,
+                      void* hip_stream);
+
+/*
+ * Decode attention for one new query token per sequence, straight from the codes:
+ *   o[b, h] = sum_j softmax_j(scale <q[b, h], k_hat[b, j, h/G]>) v_hat[b, j, h/G]
+ * over j < seq_len, G = Hq / Hkv (grouped-query attention: query head h reads kv
+ * head floor(h / G)). Scores are formed in the rotated domain (the query is rotated
+ * once; <q, k_hat> = <R q, y_hat_k>), probabilities weight rotated-domain values,
+ * and one inverse transform per output head brings o back. Work is split over the
+ * sequence (flash-decoding style) and partial (max, sum, vector) triples are merged
+ * with a log-sum-exp combine. fp32 arithmetic.
+ *
+ * q:   contiguous device tensor [B, Hq, d], q_dtype f16 or f32.
+ * out: contiguous device tensor [B, Hq, d], out_dtype f16 or f32.
+ * softmax_scale <= 0 selects 1/sqrt(d).
+ * workspace: device buffer of at least kvq_attn_workspace_bytes(desc, Hq, seq_len)
+ *   bytes, 256-byte aligned; scratch for the rotated query and split partials.
+ * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; angle codes of 6 to 8 bits
+ *   (n in [33, 256]) for K and V; 1 <= seq_len <= capacity.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
+ */
+size_t kvq_attn_workspace_bytes(const kvq_layer_desc* desc, uint32_t num_q_heads,
+                                uint32_t seq_len);
+
+kvq_status kvq_attn_decode(const kvq_layer_desc* desc, const void* cache, const void* q,
+                           kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t seq_len,
+                           float softmax_scale, void* out, kvq_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The three launches kvq_attn_decode makes, exposed so a caller can time or
+ * schedule them separately. Same arguments and rules as kvq_attn_decode; they must
+ * run in this order on one stream with the same workspace.
+ *   prepare: rotate and pre-scale the queries into the workspace
+ *   split:   stream the packed cache, write per-split partials to the workspace
+ *   merge:   combine the partials, apply the inverse transform, write `out`
+ */
+kvq_status kvq_attn_prepare(const kvq_layer_desc* desc, const void* q, kvq_dtype q_dtype,
+                            uint32_t num_q_heads, uint32_t seq_len, float softmax_scale,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+kvq_status kvq_attn_split(const kvq_layer_desc* desc, const void* cache,
+                          uint32_t num_q_heads, uint32_t seq_len, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
+kvq_status kvq_attn_merge(const kvq_layer_desc* desc, uint32_t num_q_heads, uint32_t seq_len,
+                          void* out, kvq_dtype out_dtype, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
+
+/* Number of sequence splits kvq_attn_split uses for this shape (host only; 0 if the
+ * arguments are invalid). Each split covers a whole number of 64-token tiles. */
+uint32_t kvq_attn_num_splits(const kvq_layer_desc* desc, uint32_t num_q_heads,
+                             uint32_t seq_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

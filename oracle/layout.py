@@ -170,27 +170,58 @@ def unpack_tile(d, n_k, n_v, buf, ntok=TILE) -> dict:
     }
 
 
+def _field(words: np.ndarray, pos: int, width: int) -> np.ndarray:
+    """Field [pos, pos + width) of little-endian word strings along the last axis."""
+    w, sh = pos // 32, pos % 32
+    v = words[..., w].astype(np.uint64) >> np.uint64(sh)
+    if sh + width > 32:
+        v |= words[..., w + 1].astype(np.uint64) << np.uint64(32 - sh)
+    return (v & np.uint64((1 << width) - 1)).astype(np.int64)
+
+
+def unpack_tiles(tiles: np.ndarray, d, n_k, n_v) -> dict:
+    """Vectorised unpack of whole tiles: tiles is uint8 [..., tile_bytes]; returns codes
+    shaped [..., 64, P] and parameters [..., 64] (same definitions as unpack_tile)."""
+    p = d // 2
+    bk, bv = code_bits(n_k), code_bits(n_v)
+    off = _offsets(d, n_k, n_v)
+    sizes = plane_sizes(d, n_k, n_v)
+    tiles = np.ascontiguousarray(tiles)
+    lead = tiles.shape[:-1]
+
+    def plane(name):
+        return tiles[..., off[name]:off[name] + sizes[name]]
+
+    ka = plane("KA").view(np.uint32).reshape(lead + (p * bk // 32, TILE))
+    ka = np.swapaxes(ka, -1, -2)  # [..., token, word]
+    kr = np.swapaxes(plane("KR").view(np.uint32).reshape(lead + (p // 4, TILE)), -1, -2)
+    va = np.swapaxes(plane("VA").view(np.uint32).reshape(lead + (2 * bv, p)), -1, -2)
+    vr = np.swapaxes(plane("VR").view(np.uint32).reshape(lead + (8, p)), -1, -2)
+    out = {
+        "k_angle": np.stack([_field(ka, i * bk, bk) for i in range(p)], axis=-1),
+        "k_radius": np.stack([_field(kr, i * 8, 8) for i in range(p)], axis=-1),
+        "v_angle": np.stack([_field(va, t * bv, bv) for t in range(TILE)], axis=-2),
+        "v_radius": np.stack([_field(vr, t * 4, 4) for t in range(TILE)], axis=-2),
+        "k_scale": plane("KS").view(np.float16).astype(np.float64),
+    }
+    vp = plane("VP").view(np.float16).reshape(lead + (TILE, 2)).astype(np.float64)
+    out["v_smin"] = vp[..., 0]
+    out["v_smax"] = vp[..., 1]
+    return out
+
+
 def unpack_cache(cache: np.ndarray, d, n_k, n_v, batch, hkv, capacity, t0, ntok) -> dict:
     """Unpack tokens [t0, t0 + ntok) of every (batch, kv head) from a whole layer's
     cache bytes. Returns arrays shaped [batch, ntok, hkv, P] (codes) / [batch, ntok, hkv]."""
     tb = tile_bytes(d, n_k, n_v)
     tiles = (capacity + TILE - 1) // TILE
     cache = np.asarray(cache, dtype=np.uint8).reshape(batch, hkv, tiles, tb)
-    p = d // 2
-    out = {k: np.empty((batch, ntok, hkv, p), dtype=np.int64)
-           for k in ("k_angle", "k_radius", "v_angle", "v_radius")}
-    for k in ("k_scale", "v_smin", "v_smax"):
-        out[k] = np.empty((batch, ntok, hkv), dtype=np.float64)
-    for b in range(batch):
-        for h in range(hkv):
-            for tile in range(t0 // TILE, (t0 + ntok + TILE - 1) // TILE if ntok else 0):
-                u = unpack_tile(d, n_k, n_v, cache[b, h, tile])
-                lo = max(t0, tile * TILE)
-                hi = min(t0 + ntok, tile * TILE + TILE)
-                src = slice(lo - tile * TILE, hi - tile * TILE)
-                dst = slice(lo - t0, hi - t0)
-                for k in ("k_angle", "k_radius", "v_angle", "v_radius"):
-                    out[k][b, dst, h] = u[k][src]
-                for k in ("k_scale", "v_smin", "v_smax"):
-                    out[k][b, dst, h] = u[k][src]
+    lo, hi = t0 // TILE, (t0 + ntok + TILE - 1) // TILE
+    u = unpack_tiles(cache[:, :, lo:hi], d, n_k, n_v)
+    out = {}
+    for k, v in u.items():
+        # [B, H, tiles, 64, ...] -> [B, tokens, H, ...]
+        v = v.reshape((batch, hkv, (hi - lo) * TILE) + v.shape[4:])
+        v = v[:, :, t0 - lo * TILE:t0 - lo * TILE + ntok]
+        out[k] = np.ascontiguousarray(np.swapaxes(v, 1, 2))
     return out

@@ -1,0 +1,12 @@
+"""kvq: angle-quantised KV cache and decode attention for AMD MI355X (gfx950).
+
+Python face of libkvq (C ABI in include/kvq.h). The codec follows "TurboAngle:
+Near-Lossless KV Cache Compression via Uniform Angle Quantization" (arXiv 2603.27467),
+Abstract. Importing this package loads libkvq.so and fails if it has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTS, KVQ_F16, KVQ_F32, KvqError, LayerDesc, abi_version, alloc_cache,
+    alloc_workspace, attn_decode, attn_merge, attn_num_splits, attn_prepare, attn_split,
+    attn_workspace_bytes, cache_bytes, decode, default_scale, encode, layer_signs, lib,
+    make_desc, tile_bytes)

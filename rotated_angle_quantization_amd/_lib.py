@@ -1,0 +1,208 @@
+"""ctypes binding of libkvq (include/kvq.h). Argument marshalling only: every step of
+encode, dequantise and attention runs in the library's HIP kernels. PyTorch provides
+device memory and the stream; there is no fallback path."""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libkvq.so not found at {LIB_PATH}; build it with "
+        "`python -m rotated_angle_quantization_amd.build` (hipcc, gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+KVQ_F16, KVQ_F32 = 0, 1
+STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE",
+          5: "HIP"}
+
+
+class LayerDesc(ctypes.Structure):
+    """kvq_layer_desc: one layer's cache geometry and codec parameters."""
+
+    _fields_ = [("head_dim", ctypes.c_uint32), ("num_kv_heads", ctypes.c_uint32),
+                ("batch", ctypes.c_uint32), ("capacity", ctypes.c_uint32),
+                ("n_bins_k", ctypes.c_uint32), ("n_bins_v", ctypes.c_uint32),
+                ("layer", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
+
+    def __repr__(self):
+        return (f"LayerDesc(d={self.head_dim}, hkv={self.num_kv_heads}, B={self.batch}, "
+                f"cap={self.capacity}, n=({self.n_bins_k},{self.n_bins_v}), "
+                f"layer={self.layer}, seed={self.seed})")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.kvq_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+_P = ctypes.POINTER(LayerDesc)
+_v = ctypes.c_void_p
+_u32, _u64, _i64, _f32, _sz = (ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                               ctypes.c_float, ctypes.c_size_t)
+
+_SIGS = {
+    "kvq_abi_version": (ctypes.c_int, []),
+    "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvq_cache_bytes": (_sz, [_P]),
+    "kvq_tile_bytes": (_sz, [_u32, _u32, _u32]),
+    "kvq_layer_signs": (ctypes.c_int, [_u64, _u32, _u32, ctypes.POINTER(ctypes.c_int8)]),
+    "kvq_encode": (ctypes.c_int, [_P, _v, _v, _v, ctypes.c_int, _i64, _i64, _i64, _u32, _u32,
+                                  _v]),
+    "kvq_decode": (ctypes.c_int, [_P, _v, _v, _v, ctypes.c_int, _u32, _u32, _v]),
+    "kvq_attn_workspace_bytes": (_sz, [_P, _u32, _u32]),
+    "kvq_attn_num_splits": (_u32, [_P, _u32, _u32]),
+    "kvq_attn_decode": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
+                                       ctypes.c_int, _v, _sz, _v]),
+    "kvq_attn_prepare": (ctypes.c_int, [_P, _v, ctypes.c_int, _u32, _u32, _f32, _v, _sz, _v]),
+    "kvq_attn_split": (ctypes.c_int, [_P, _v, _u32, _u32, _v, _sz, _v]),
+    "kvq_attn_merge": (ctypes.c_int, [_P, _u32, _u32, _v, ctypes.c_int, _v, _sz, _v]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KvqError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 or float32)")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_desc(head_dim, num_kv_heads, batch, capacity, n_bins_k, n_bins_v, layer=0,
+              seed=0) -> LayerDesc:
+    return LayerDesc(head_dim, num_kv_heads, batch, capacity, n_bins_k, n_bins_v, layer, 0,
+                     seed)
+
+
+def abi_version() -> int:
+    return lib.kvq_abi_version()
+
+
+def cache_bytes(desc: LayerDesc) -> int:
+    return lib.kvq_cache_bytes(ctypes.byref(desc))
+
+
+def tile_bytes(head_dim: int, n_bins_k: int, n_bins_v: int) -> int:
+    return lib.kvq_tile_bytes(head_dim, n_bins_k, n_bins_v)
+
+
+def layer_signs(seed: int, layer: int, d: int) -> list[int]:
+    buf = (ctypes.c_int8 * d)()
+    _check(lib.kvq_layer_signs(seed, layer, d, buf), "kvq_layer_signs")
+    return list(buf)
+
+
+def alloc_cache(desc: LayerDesc, device="cuda") -> torch.Tensor:
+    n = cache_bytes(desc)
+    if n == 0:
+        raise KvqError(1, "kvq_cache_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def encode(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+           t0: int = 0) -> None:
+    """Append K/V tokens [t0, t0 + ntok): k, v are [B, ntok, Hkv, d] with matching strides."""
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape, strides and dtype")
+    if k.dim() != 4 or k.stride(3) != 1:
+        raise ValueError("k/v must be [B, ntok, Hkv, d] with d contiguous")
+    ntok = k.shape[1]
+    _check(lib.kvq_encode(ctypes.byref(desc), cache.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          _dtype_code(k), k.stride(0), k.stride(1), k.stride(2), t0, ntok,
+                          _stream(cache.device)), "kvq_encode")
+
+
+def decode(desc: LayerDesc, cache: torch.Tensor, t0: int, ntok: int,
+           out_dtype=torch.float16, out: tuple | None = None):
+    """Dequantise tokens [t0, t0 + ntok) -> (k_hat, v_hat), each [B, ntok, Hkv, d]."""
+    shape = (desc.batch, ntok, desc.num_kv_heads, desc.head_dim)
+    if out is None:
+        k_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
+        v_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
+    else:
+        k_out, v_out = out
+    _check(lib.kvq_decode(ctypes.byref(desc), cache.data_ptr(), k_out.data_ptr(),
+                          v_out.data_ptr(), _dtype_code(k_out), t0, ntok,
+                          _stream(cache.device)), "kvq_decode")
+    return k_out, v_out
+
+
+def attn_workspace_bytes(desc: LayerDesc, num_q_heads: int, seq_len: int) -> int:
+    return lib.kvq_attn_workspace_bytes(ctypes.byref(desc), num_q_heads, seq_len)
+
+
+def attn_num_splits(desc: LayerDesc, num_q_heads: int, seq_len: int) -> int:
+    return lib.kvq_attn_num_splits(ctypes.byref(desc), num_q_heads, seq_len)
+
+
+def alloc_workspace(desc: LayerDesc, num_q_heads: int, seq_len: int, device="cuda"):
+    n = attn_workspace_bytes(desc, num_q_heads, seq_len)
+    if n == 0:
+        raise KvqError(1, "kvq_attn_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
+                softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None):
+    """o[b, h] = softmax(scale q.k_hat) v_hat over the first seq_len cached tokens.
+    q: contiguous [B, Hq, d] (fp16 or fp32); returns [B, Hq, d]."""
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, hq, seq_len, q.device)
+    _check(lib.kvq_attn_decode(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
+                               _dtype_code(q), hq, seq_len, float(softmax_scale),
+                               out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
+                               workspace.numel(), _stream(q.device)), "kvq_attn_decode")
+    return out
+
+
+def attn_prepare(desc, q, seq_len, workspace, softmax_scale=0.0):
+    _check(lib.kvq_attn_prepare(ctypes.byref(desc), q.data_ptr(), _dtype_code(q), q.shape[1],
+                                seq_len, float(softmax_scale), workspace.data_ptr(),
+                                workspace.numel(), _stream(q.device)), "kvq_attn_prepare")
+
+
+def attn_split(desc, cache, num_q_heads, seq_len, workspace):
+    _check(lib.kvq_attn_split(ctypes.byref(desc), cache.data_ptr(), num_q_heads, seq_len,
+                              workspace.data_ptr(), workspace.numel(),
+                              _stream(cache.device)), "kvq_attn_split")
+
+
+def attn_merge(desc, num_q_heads, seq_len, out, workspace):
+    _check(lib.kvq_attn_merge(ctypes.byref(desc), num_q_heads, seq_len, out.data_ptr(),
+                              _dtype_code(out), workspace.data_ptr(), workspace.numel(),
+                              _stream(out.device)), "kvq_attn_merge")
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

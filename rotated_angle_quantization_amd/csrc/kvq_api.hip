@@ -1,0 +1,293 @@
+// C ABI of libkvq: host-side validation, sign generation, sizing and dispatch.
+// Nothing here touches the device before every argument has been checked.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+// SplitMix64 output function (Steele, Lea, Flood, OOPSLA 2014): add the golden
+// gamma, then two xor-shift-multiply rounds, all modulo 2^64.
+uint64_t splitmix64_mix(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+bool is_pow2(uint32_t v) { return v && !(v & (v - 1)); }
+
+SignMask sign_mask(uint64_t seed, uint32_t layer, uint32_t d) {
+  SignMask m;
+  memset(&m, 0, sizeof(m));
+  const uint64_t base = splitmix64_mix(seed ^ (uint64_t)layer);
+  for (uint32_t i = 0; i < d; ++i)
+    if (splitmix64_mix(base + i) >> 63) m.w[i >> 6] |= 1ull << (i & 63);
+  return m;
+}
+
+// Structural validity of a descriptor (independent of what kernels exist).
+bool desc_ok(const kvq_layer_desc* d) {
+  if (!d) return false;
+  if (d->reserved != 0) return false;
+  if (d->head_dim < 64 || d->head_dim > 256 || !is_pow2(d->head_dim)) return false;
+  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0) return false;
+  if (d->n_bins_k < 2 || d->n_bins_k > 256 || d->n_bins_v < 2 || d->n_bins_v > 256)
+    return false;
+  return true;
+}
+
+bool head_dim_supported(uint32_t d) { return d == 64 || d == 128; }
+
+int tiles_per_seq(const kvq_layer_desc* d) {
+  return (int)((d->capacity + kTile - 1) / kTile);
+}
+
+TileGeom geom_of(const kvq_layer_desc* d) {
+  return tile_geom((int)d->head_dim, code_bits(d->n_bins_k), code_bits(d->n_bins_v));
+}
+
+CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
+  CodecArgs a;
+  a.batch = (int)d->batch;
+  a.hkv = (int)d->num_kv_heads;
+  a.tiles_per_seq = tiles_per_seq(d);
+  a.t0 = (int)t0;
+  a.ntok = (int)ntok;
+  a.tile_lo = (int)(t0 / kTile);
+  a.tiles_touched = (int)((t0 + ntok + kTile - 1) / kTile) - a.tile_lo;
+  a.n_k = (int)d->n_bins_k;
+  a.n_v = (int)d->n_bins_v;
+  a.bk = code_bits(d->n_bins_k);
+  a.bv = code_bits(d->n_bins_v);
+  a.inv_sqrt_d = 1.0 / sqrt((double)d->head_dim);
+  a.k_bins_per_rad = (double)d->n_bins_k / kTwoPi;
+  a.v_bins_per_rad = (double)d->n_bins_v / kTwoPi;
+  a.sign = sign_mask(d->seed, d->layer, d->head_dim);
+  return a;
+}
+
+// Sequence split for decode attention: aim for about 2048 workgroups over the whole
+// launch, at least 4 tiles (one per wave) per split, and no empty split.
+void split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tiles_per_split) {
+  const int ntiles = (int)((seq_len + kTile - 1) / kTile);
+  const int target_wgs = 2048;
+  int s = (int)((target_wgs + units - 1) / units);
+  int max_s = (ntiles + 3) / 4;
+  if (max_s < 1) max_s = 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  int tps = (ntiles + s - 1) / s;
+  *tiles_per_split = tps;
+  *nsplit = (ntiles + tps - 1) / tps;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct AttnLayout {
+  size_t qrot, ml, acc, total;
+};
+
+AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit) {
+  AttnLayout l;
+  const size_t bh = (size_t)d->batch * hq;
+  l.qrot = 0;
+  l.ml = align256(l.qrot + bh * d->head_dim * sizeof(float));
+  l.acc = align256(l.ml + bh * (size_t)nsplit * 2 * sizeof(float));
+  l.total = align256(l.acc + bh * (size_t)nsplit * d->head_dim * sizeof(float));
+  return l;
+}
+
+kvq_status attn_check(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (hq == 0 || hq % d->num_kv_heads) return KVQ_ERR_INVALID_ARGUMENT;
+  if (seq_len == 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (seq_len > d->capacity) return KVQ_ERR_CAPACITY;
+  const uint32_t g = hq / d->num_kv_heads;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
+  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
+  if (bk < 6 || bk > 8 || bv < 6 || bv > 8) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, float scale,
+                     void* workspace, size_t workspace_bytes, AttnArgs* a) {
+  kvq_status st = attn_check(d, hq, seq_len);
+  if (st != KVQ_OK) return st;
+  int nsplit, tps;
+  split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  const AttnLayout l = attn_layout(d, hq, nsplit);
+  if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < l.total)
+    return KVQ_ERR_WORKSPACE;
+  a->batch = (int)d->batch;
+  a->hkv = (int)d->num_kv_heads;
+  a->hq = (int)hq;
+  a->group = (int)(hq / d->num_kv_heads);
+  a->seq_len = (int)seq_len;
+  a->tiles_per_seq = tiles_per_seq(d);
+  a->ntiles = (int)((seq_len + kTile - 1) / kTile);
+  a->nsplit = nsplit;
+  a->tiles_per_split = tps;
+  a->n_k = (int)d->n_bins_k;
+  a->n_v = (int)d->n_bins_v;
+  a->bk = code_bits(d->n_bins_k);
+  a->bv = code_bits(d->n_bins_v);
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
+  a->q_scale = (float)(sc * 1.4426950408889634 / 255.0);
+  a->inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
+  a->sign = sign_mask(d->seed, d->layer, d->head_dim);
+  char* base = (char*)workspace;
+  a->qrot = (float*)(base + l.qrot);
+  a->part_ml = (float*)(base + l.ml);
+  a->part_acc = (float*)(base + l.acc);
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case KVQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t kvq_tile_bytes(uint32_t head_dim, uint32_t n_bins_k, uint32_t n_bins_v) {
+  if (head_dim < 64 || head_dim > 256 || !is_pow2(head_dim)) return 0;
+  if (n_bins_k < 2 || n_bins_k > 256 || n_bins_v < 2 || n_bins_v > 256) return 0;
+  return (size_t)tile_geom((int)head_dim, code_bits(n_bins_k), code_bits(n_bins_v)).bytes;
+}
+
+size_t kvq_cache_bytes(const kvq_layer_desc* d) {
+  if (!desc_ok(d)) return 0;
+  return (size_t)d->batch * d->num_kv_heads * (size_t)tiles_per_seq(d) *
+         kvq_tile_bytes(d->head_dim, d->n_bins_k, d->n_bins_v);
+}
+
+kvq_status kvq_layer_signs(uint64_t seed, uint32_t layer, uint32_t d, int8_t* out_host) {
+  if (!out_host || !is_pow2(d) || d > 4096) return KVQ_ERR_INVALID_ARGUMENT;
+  const uint64_t base = splitmix64_mix(seed ^ (uint64_t)layer);
+  for (uint32_t i = 0; i < d; ++i) out_host[i] = (splitmix64_mix(base + i) >> 63) ? -1 : 1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_encode(const kvq_layer_desc* d, void* cache, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t sb, int64_t st, int64_t sh, uint32_t t0,
+                      uint32_t ntok, void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !k || !v) return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const CodecArgs a = codec_args(d, t0, ntok);
+  return hip_status(launch_encode(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
+                                  in_dtype == KVQ_F32, sb, st, sh, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, void* v_out,
+                      kvq_dtype out_dtype, uint32_t t0, uint32_t ntok, void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != KVQ_F16 && out_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !k_out || !v_out) return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = out_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k_out % (2 * esz)) || ((uintptr_t)v_out % (2 * esz)))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const CodecArgs a = codec_args(d, t0, ntok);
+  return hip_status(launch_decode(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
+                                  k_out, v_out, out_dtype == KVQ_F32, (hipStream_t)stream));
+}
+
+uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
+  if (!desc_ok(d) || hq == 0 || hq % d->num_kv_heads || seq_len == 0 || seq_len > d->capacity)
+    return 0;
+  int nsplit, tps;
+  split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  return (uint32_t)nsplit;
+}
+
+size_t kvq_attn_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
+  const uint32_t s = kvq_attn_num_splits(d, hq, seq_len);
+  if (!s) return 0;
+  return attn_layout(d, hq, (int)s).total;
+}
+
+kvq_status kvq_attn_prepare(const kvq_layer_desc* d, const void* q, kvq_dtype q_dtype,
+                            uint32_t hq, uint32_t seq_len, float scale, void* ws,
+                            size_t ws_bytes, void* stream) {
+  AttnArgs a;
+  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!q || (q_dtype != KVQ_F16 && q_dtype != KVQ_F32)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(
+      launch_attn_prepare(a, (int)d->head_dim, q, q_dtype == KVQ_F32, (hipStream_t)stream));
+}
+
+kvq_status kvq_attn_split(const kvq_layer_desc* d, const void* cache, uint32_t hq,
+                          uint32_t seq_len, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a;
+  kvq_status st = attn_args(d, hq, seq_len, 0.0f, ws, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!cache) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_attn_split(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
+                                      (hipStream_t)stream));
+}
+
+kvq_status kvq_attn_merge(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, void* out,
+                          kvq_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a;
+  kvq_status st = attn_args(d, hq, seq_len, 0.0f, ws, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!out || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  return hip_status(
+      launch_attn_merge(a, (int)d->head_dim, out, out_dtype == KVQ_F32, (hipStream_t)stream));
+}
+
+kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const void* q,
+                           kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, float scale,
+                           void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                           void* stream) {
+  // Validate everything before the first launch so a rejected call enqueues nothing.
+  AttnArgs a;
+  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!cache || !q || !out) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  const int dim = (int)d->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_attn_prepare(a, dim, q, q_dtype == KVQ_F32, s);
+  if (e == hipSuccess) e = launch_attn_split(a, dim, geom_of(d), (const uint8_t*)cache, s);
+  if (e == hipSuccess) e = launch_attn_merge(a, dim, out, out_dtype == KVQ_F32, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Private definitions shared by the libkvq HIP sources: tile geometry, the per-layer
+// sign mask and the kernel launchers the C ABI dispatches to.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kTile = KVQ_TILE_TOKENS;  // token slots per tile
+constexpr int kMaxHeadDim = 128;
+
+// Angle code width for n bins: ceil(log2 n).
+inline int code_bits(uint32_t n) {
+  int b = 0;
+  while ((1u << b) < n) ++b;
+  return b;
+}
+
+// Byte geometry of one tile (see the layout comment in kvq.h).
+struct TileGeom {
+  int d, pairs, bk, bv;
+  int ka, kr, ks, va, vr, vp, bytes;  // plane byte offsets and total tile bytes
+  int wka, wkr, wva, wvr;             // words per token (K planes) or per pair (V)
+};
+
+inline TileGeom tile_geom(int d, int bk, int bv) {
+  TileGeom g;
+  g.d = d;
+  g.pairs = d / 2;
+  g.bk = bk;
+  g.bv = bv;
+  g.wka = g.pairs * bk / 32;
+  g.wkr = g.pairs / 4;
+  g.wva = 2 * bv;
+  g.wvr = 8;
+  g.ka = 0;
+  g.kr = g.ka + kTile * g.wka * 4;
+  g.ks = g.kr + kTile * g.wkr * 4;
+  g.va = g.ks + 2 * kTile;
+  g.vr = g.va + g.pairs * g.wva * 4;
+  g.vp = g.vr + g.pairs * g.wvr * 4;
+  g.bytes = g.vp + 4 * kTile;
+  return g;
+}
+
+// Sign diagonal as a bit mask: bit e set <=> sign[e] = -1. d <= 256.
+struct SignMask {
+  uint64_t w[4];
+};
+
+// Runtime parameters of one encode/decode launch.
+struct CodecArgs {
+  int batch, hkv, tiles_per_seq;
+  int t0, ntok;               // token range
+  int tile_lo, tiles_touched;  // first tile and count of tiles the range touches
+  int n_k, n_v, bk, bv;
+  double inv_sqrt_d;        // fp64 value of 1/sqrt(d)
+  double k_bins_per_rad;    // n_k / (2 pi) in fp64
+  double v_bins_per_rad;    // n_v / (2 pi) in fp64
+  SignMask sign;
+};
+
+hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cache,
+                         const void* k, const void* v, bool f32_in, int64_t sb, int64_t st,
+                         int64_t sh, hipStream_t stream);
+
+hipError_t launch_decode(const CodecArgs& a, int d, TileGeom geom, const uint8_t* cache,
+                         void* k_out, void* v_out, bool f32_out, hipStream_t stream);
+
+// Decode attention.
+struct AttnArgs {
+  int batch, hkv, hq, group;
+  int seq_len, tiles_per_seq, ntiles, nsplit, tiles_per_split;
+  int n_k, n_v, bk, bv;
+  float q_scale;       // softmax scale * log2(e) / 255, folded into the rotated query
+  float inv_sqrt_d;    // fp32 1/sqrt(d)
+  SignMask sign;
+  float* qrot;         // [B, Hq, d]
+  float* part_ml;      // [B, Hq, nsplit, 2]
+  float* part_acc;     // [B, Hq, nsplit, d]
+};
+
+hipError_t launch_attn_prepare(const AttnArgs& a, int d, const void* q, bool f32_q,
+                               hipStream_t stream);
+hipError_t launch_attn_split(const AttnArgs& a, int d, TileGeom geom, const uint8_t* cache,
+                             hipStream_t stream);
+hipError_t launch_attn_merge(const AttnArgs& a, int d, void* out, bool f32_out,
+                             hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header
+declares, and its host-only helpers and argument validation behave as documented.
+Only error paths (which return before any HIP call) and ntok = 0 are exercised."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+from oracle import codec as oc
+from oracle import layout as ol
+
+kvq = pytest.importorskip("rotated_angle_quantization_amd")
+lib = kvq.lib
+
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = 0, 1, 2, 3, 4
+FAKE = 0x10000  # aligned non-null address; never dereferenced on the paths tested
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 13
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(kvq.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert kvq.abi_version() == 1
+    for s in range(6):
+        assert lib.kvq_status_string(s)
+    assert lib.kvq_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("nk,nv", [(128, 64), (256, 256), (2, 3), (100, 33), (64, 128)])
+def test_tile_and_cache_bytes_match_layout_definition(d, nk, nv):
+    assert kvq.tile_bytes(d, nk, nv) == ol.tile_bytes(d, nk, nv)
+    desc = kvq.make_desc(d, 3, 2, 100, nk, nv)
+    assert kvq.cache_bytes(desc) == ol.cache_bytes(d, nk, nv, 2, 3, 100)
+
+
+def test_invalid_descriptors_size_zero():
+    assert kvq.tile_bytes(96, 128, 64) == 0
+    assert kvq.tile_bytes(32, 128, 64) == 0
+    assert kvq.tile_bytes(128, 1, 64) == 0
+    assert kvq.tile_bytes(128, 128, 257) == 0
+    for bad in (dict(head_dim=48), dict(num_kv_heads=0), dict(batch=0), dict(capacity=0),
+                dict(n_bins_k=300), dict(reserved=1)):
+        desc = kvq.make_desc(128, 8, 1, 64, 128, 64)
+        for k, v in bad.items():
+            setattr(desc, k, v)
+        assert kvq.cache_bytes(desc) == 0, bad
+
+
+@pytest.mark.parametrize("seed,layer,d", [(0, 0, 64), (0, 5, 128), (12345, 31, 128),
+                                          (2**63 + 7, 79, 256), (1, 2**31, 64)])
+def test_library_signs_equal_oracle_signs(seed, layer, d):
+    assert kvq.layer_signs(seed, layer, d) == oc.layer_signs(seed, layer, d).astype(int).tolist()
+
+
+def _enc(desc, k=FAKE, v=FAKE, dtype=0, sb=0, st=0, sh=0, t0=0, ntok=1, cache=FAKE):
+    return lib.kvq_encode(ctypes.byref(desc), cache, k, v, dtype, sb, st, sh, t0, ntok, None)
+
+
+def test_encode_validation():
+    desc = kvq.make_desc(128, 8, 1, 128, 128, 64)
+    assert _enc(desc, ntok=0) == OK  # nothing to do, no device call
+    assert _enc(desc, t0=100, ntok=29) == CAPACITY
+    assert _enc(desc, k=None) == INVALID
+    assert _enc(desc, cache=None) == INVALID
+    assert _enc(desc, dtype=7) == INVALID
+    assert _enc(desc, k=FAKE + 2) == INVALID  # fp16 pairs need 4-byte alignment
+    assert _enc(desc, dtype=1, k=FAKE + 4) == INVALID  # fp32 pairs need 8 bytes
+    assert _enc(desc, st=3) == INVALID  # odd stride
+    assert _enc(desc, sh=-2) == INVALID
+    d256 = kvq.make_desc(256, 8, 1, 128, 128, 64)
+    assert _enc(d256) == UNSUPPORTED
+    assert lib.kvq_encode(None, FAKE, FAKE, FAKE, 0, 0, 0, 0, 0, 1, None) == INVALID
+
+
+def test_decode_validation():
+    desc = kvq.make_desc(64, 2, 1, 64, 128, 64)
+    dec = lambda **kw: lib.kvq_decode(ctypes.byref(desc), kw.get("cache", FAKE),
+                                      kw.get("k", FAKE), kw.get("v", FAKE), kw.get("dt", 0),
+                                      kw.get("t0", 0), kw.get("ntok", 1), None)
+    assert dec(ntok=0) == OK
+    assert dec(t0=60, ntok=5) == CAPACITY
+    assert dec(k=None) == INVALID
+    assert dec(dt=2) == INVALID
+    assert dec(v=FAKE + 2) == INVALID
+
+
+def _attn(desc, hq=32, seq=100, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, qdt=0, odt=0,
+          cache=FAKE):
+    return lib.kvq_attn_decode(ctypes.byref(desc), cache, q, qdt, hq, seq, 0.0, out, odt, ws,
+                               ws_bytes, None)
+
+
+def test_attention_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    assert _attn(desc, hq=36) == INVALID  # not a multiple of Hkv
+    assert _attn(desc, hq=24) == UNSUPPORTED  # G = 3
+    assert _attn(desc, hq=128) == UNSUPPORTED  # G = 16
+    assert _attn(desc, seq=0) == INVALID
+    assert _attn(desc, seq=257) == CAPACITY
+    assert _attn(desc, ws=None) == WORKSPACE
+    assert _attn(desc, ws=FAKE + 64) == WORKSPACE  # needs 256-byte alignment
+    need = kvq.attn_workspace_bytes(desc, 32, 100)
+    assert need > 0
+    assert _attn(desc, ws_bytes=need - 1) == WORKSPACE
+    assert _attn(desc, q=None) == INVALID
+    assert _attn(desc, out=FAKE + 2) == INVALID
+    assert _attn(desc, qdt=3) == INVALID
+    assert _attn(desc, cache=None) == INVALID
+    small = kvq.make_desc(128, 8, 2, 256, 32, 64)  # 5-bit key angle codes
+    assert _attn(small) == UNSUPPORTED
+    d64 = kvq.make_desc(64, 4, 1, 256, 256, 33)  # 8-bit / 6-bit: supported shape
+    assert _attn(d64, hq=32, ws=None) == WORKSPACE
+
+
+def test_split_plan_covers_sequence_without_empty_splits():
+    for bsz, hkv, seq in [(1, 1, 1), (1, 1, 64), (1, 4, 4096), (4, 8, 32768), (1, 8, 131072),
+                          (64, 8, 8192), (3, 2, 1000), (1, 1, 65)]:
+        desc = kvq.make_desc(128, hkv, bsz, seq, 128, 64)
+        s = kvq.attn_num_splits(desc, hkv, seq)
+        ntiles = (seq + 63) // 64
+        assert 1 <= s <= ntiles
+        tps = -(-ntiles // s)
+        assert (s - 1) * tps < ntiles <= s * tps  # last split is non-empty
+        assert kvq.attn_workspace_bytes(desc, hkv * 4, seq) >= 4 * bsz * hkv * 4 * s * 130
+
+
+def test_layer_signs_validation():
+    buf = (ctypes.c_int8 * 8)()
+    assert lib.kvq_layer_signs(0, 0, 6, buf) == INVALID
+    assert lib.kvq_layer_signs(0, 0, 8, None) == INVALID
+    assert lib.kvq_layer_signs(0, 0, 8, buf) == OK
+    assert set(np.array(buf)) <= {-1, 1}

@@ -91,3 +91,18 @@ def test_unpack_cache_ranges():
         a = ref[1, 0, tok // 64]
         assert np.array_equal(out["k_angle"][1, j, 0], a["k_angle"][tok % 64])
         assert np.array_equal(out["v_radius"][1, j, 0], a["v_radius"][tok % 64])
+
+
+def test_vectorised_unpack_matches_per_tile_unpack():
+    rng = np.random.default_rng(11)
+    for d, nk, nv in [(64, 128, 64), (128, 256, 256), (128, 100, 37)]:
+        tb = ol.tile_bytes(d, nk, nv)
+        tiles = rng.integers(0, 256, (3, tb), dtype=np.uint8)
+        # keep the fp16 parameter planes finite
+        fast = ol.unpack_tiles(tiles, d, nk, nv)
+        for t in range(3):
+            slow = ol.unpack_tile(d, nk, nv, tiles[t])
+            for key in ("k_angle", "k_radius", "v_angle", "v_radius"):
+                assert np.array_equal(fast[key][t], slow[key]), key
+            for key in ("k_scale", "v_smin", "v_smax"):
+                np.testing.assert_array_equal(fast[key][t], slow[key])
