@@ -72,13 +72,22 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
   return a;
 }
 
-// Sequence split for decode attention: aim for about 2048 workgroups over the whole
-// launch, at least 4 tiles (one per wave) per split, and no empty split.
-void split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tiles_per_split) {
+// Whether decode attention uses the LDS key-score table for this shape.
+bool use_key_table(const kvq_layer_desc* d, uint32_t hq) {
+  const int g = (int)(hq / d->num_kv_heads);
+  return key_table_bytes((int)d->head_dim, g, code_bits(d->n_bins_k)) <= kKeyTableMaxBytes;
+}
+
+// Sequence split for decode attention. Workgroups have 8 waves that each stream whole
+// tiles; aim for one workgroup per compute unit when the key table fills the LDS
+// (256 workgroups), two otherwise, with at least 8 tiles (one per wave) per split and
+// no empty split.
+void split_plan(uint32_t units, uint32_t seq_len, bool key_table, int* nsplit,
+                int* tiles_per_split) {
   const int ntiles = (int)((seq_len + kTile - 1) / kTile);
-  const int target_wgs = 2048;
+  const int target_wgs = key_table ? 256 : 512;
   int s = (int)((target_wgs + units - 1) / units);
-  int max_s = (ntiles + 3) / 4;
+  int max_s = (ntiles + 7) / 8;
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -121,7 +130,8 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   kvq_status st = attn_check(d, hq, seq_len);
   if (st != KVQ_OK) return st;
   int nsplit, tps;
-  split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  const bool kt = use_key_table(d, hq);
+  split_plan(d->batch * d->num_kv_heads, seq_len, kt, &nsplit, &tps);
   const AttnLayout l = attn_layout(d, hq, nsplit);
   if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < l.total)
     return KVQ_ERR_WORKSPACE;
@@ -138,6 +148,7 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->n_v = (int)d->n_bins_v;
   a->bk = code_bits(d->n_bins_k);
   a->bv = code_bits(d->n_bins_v);
+  a->key_table = kt ? 1 : 0;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
   a->q_scale = (float)(sc * 1.4426950408889634 / 255.0);
   a->inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
@@ -226,7 +237,7 @@ uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_
   if (!desc_ok(d) || hq == 0 || hq % d->num_kv_heads || seq_len == 0 || seq_len > d->capacity)
     return 0;
   int nsplit, tps;
-  split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  split_plan(d->batch * d->num_kv_heads, seq_len, use_key_table(d, hq), &nsplit, &tps);
   return (uint32_t)nsplit;
 }
 

@@ -52,21 +52,40 @@ __device__ __forceinline__ void fwht_pairs_f32(float& a, float& b, int p) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
+
+// DPP lane moves within rows of 16: xor 1, xor 2 (quad permutes), then the half-row
+// and row mirrors, which pair lanes whose partial results are already row-uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, 0));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Wave-wide max / sum: four DPP steps make each row of 16 uniform, then the four row
+// results are combined from scalar registers (readlane), so the result is uniform.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)),
+               fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
+}
+
+// 2^x with the hardware instruction; arguments here are either <= 0 (softmax) or
+// log2 of fp16-range radii, so no range scaling is needed (underflow gives 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Field `idx` of width B from a register-resident little-endian word string; with
 // idx a compile-time constant this is one bit-field extract (or an align + mask when
@@ -121,203 +140,329 @@ __global__ __launch_bounds__(64) void attn_prepare_kernel(AttnArgs a, const void
 
 // ---------------------------------------------------------------------------- split
 
+// Value lanes: a wave is 4 rows x 16 columns. Row r takes the 16 token slots
+// [16r, 16r + 16) of a tile one per step; column c takes P / 16 consecutive pairs.
+constexpr int kRows = 4, kCols = 16, kStepTokens = kTile / kRows;
+
 template <int D, int G, int BK, int BV>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a,
+struct SplitCfg {
+  using GE = Geo<D, BK, BV>;
+  static constexpr int P = D / 2;
+  static constexpr int NKT = 1 << BK;         // key-table rows per pair (codes < 2^bk)
+  static constexpr int PPL = P / kCols;        // value pairs per lane
+  // value-angle words per pair covering one row's 16 tokens; odd widths may start
+  // half-way into a word and are realigned after loading
+  static constexpr int VAW = (BV & 1) ? (kStepTokens * BV + 16 + 31) / 32 : kStepTokens * BV / 32;
+  static constexpr int TAB_BYTES = P * NKT * G * 4;
+};
+
+// Registers of one tile: key planes in token-per-lane order, value planes in the
+// row/column order above.
+template <int D, int G, int BK, int BV>
+struct TileRegs {
+  using C = SplitCfg<D, G, BK, BV>;
+  uint32_t ka[C::GE::WKA], kr[C::GE::WKR], ks, vp;
+  uint32_t va[C::PPL][C::VAW], vr[C::PPL][2];
+};
+
+template <int D, int G, int BK, int BV>
+__device__ __forceinline__ void load_tile(TileRegs<D, G, BK, BV>& t, const uint8_t* tp,
+                                          int lane, int row, int col) {
+  using C = SplitCfg<D, G, BK, BV>;
+  using GE = typename C::GE;
+  constexpr int P = C::P, PPL = C::PPL;
+  const uint32_t* w32 = reinterpret_cast<const uint32_t*>(tp);
+#pragma unroll
+  for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
+#pragma unroll
+  for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
+  t.ks = reinterpret_cast<const uint16_t*>(tp + GE::OFF_KS)[lane];
+  t.vp = w32[GE::OFF_VP / 4 + lane];
+  const int w0 = (row * kStepTokens * BV) >> 5;
+#pragma unroll
+  for (int w = 0; w < C::VAW; ++w) {
+    const uint32_t* src = w32 + GE::OFF_VA / 4 + (w0 + w) * P + col * PPL;
+    if (PPL == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      t.va[0][w] = v.x; t.va[1 % PPL][w] = v.y; t.va[2 % PPL][w] = v.z; t.va[3 % PPL][w] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      t.va[0][w] = v.x; t.va[1 % PPL][w] = v.y;
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t* src = w32 + GE::OFF_VR / 4 + (2 * row + w) * P + col * PPL;
+    if (PPL == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      t.vr[0][w] = v.x; t.vr[1 % PPL][w] = v.y; t.vr[2 % PPL][w] = v.z; t.vr[3 % PPL][w] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      t.vr[0][w] = v.x; t.vr[1 % PPL][w] = v.y;
+    }
+  }
+}
+
+__device__ __forceinline__ float bperm_f(int byte_addr, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
+}
+
+// KT: scores read a per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) +
+// q~_h,2i+1 sin(2 pi c / n) from LDS, one FMA per (pair, head); otherwise scores
+// use the cos/sin table and the rotated query from scalar registers.
+template <int D, int G, int BK, int BV, bool KT>
+__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
                                                          const uint8_t* __restrict__ cache,
                                                          const float* __restrict__ qrot) {
-  using GE = Geo<D, BK, BV>;
-  constexpr int P = GE::P;
-  constexpr int NT = (P == 64) ? 64 : 32;  // value tokens per lane per tile
-  constexpr int WVA = NT * BV / 32;        // value-angle words per lane
-  constexpr int WVR = NT * 4 / 32;         // value-radius words per lane
-
-  __shared__ float2 lut_k[256], lut_v[256];
-  __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ float s_acc[4][G][D];
+  using C = SplitCfg<D, G, BK, BV>;
+  using GE = typename C::GE;
+  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = 8;
+  constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
+  constexpr int UNION_BYTES = (KT && C::TAB_BYTES > MERGE_BYTES) ? C::TAB_BYTES : MERGE_BYTES;
+  __shared__ __align__(16) char s_union[UNION_BYTES];
+  __shared__ float2 lut_k[NKT], lut_v[1 << BV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
+  const float* qg = qrot + (size_t)bk * G * D;
 
-  for (int c = tid; c < 256; c += 256) {
-    double s, co;
-    float2 ek = make_float2(0.f, 0.f), ev = make_float2(0.f, 0.f);
-    if (c < a.n_k) {
-      sincospi(2.0 * c / a.n_k, &s, &co);
-      ek = make_float2((float)co, (float)s);
-    }
-    if (c < a.n_v) {
-      sincospi(2.0 * c / a.n_v, &s, &co);
-      ev = make_float2((float)co, (float)s);
-    }
-    lut_k[c] = ek;
-    lut_v[c] = ev;
+  // cos/sin of the bin centres 2 pi c / n; rows past n are only ever read for slots
+  // past the sequence end and are zeroed
+  for (int c = tid; c < NKT; c += NW * 64) {
+    float sn = 0.f, co = 0.f;
+    if (c < a.n_k) sincospif(2.0f * (float)c / (float)a.n_k, &sn, &co);
+    lut_k[c] = make_float2(co, sn);
+  }
+  for (int c = tid; c < (1 << BV); c += NW * 64) {
+    float sn = 0.f, co = 0.f;
+    if (c < a.n_v) sincospif(2.0f * (float)c / (float)a.n_v, &sn, &co);
+    lut_v[c] = make_float2(co, sn);
   }
   __syncthreads();
+  float* ktab = reinterpret_cast<float*>(s_union);
+  if (KT) {
+    // NW*64 threads: each owns one pair (q~ loaded once) and a stride of codes
+    constexpr int TPP = NW * 64 / P;  // threads per pair
+    const int i = tid / TPP, c0 = tid % TPP;
+    float qa[G], qb[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      qa[g] = qg[g * D + 2 * i];
+      qb[g] = qg[g * D + 2 * i + 1];
+    }
+    for (int c = c0; c < NKT; c += TPP) {
+      const float2 cs = lut_k[c];
+      float tv[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) tv[g] = fmaf(qa[g], cs.x, qb[g] * cs.y);
+      float* dst = ktab + (i * NKT + c) * G;
+#pragma unroll
+      for (int g = 0; g < G; g += (G >= 4 ? 4 : G)) {
+        if (G >= 4)
+          *reinterpret_cast<float4*>(dst + g) = make_float4(tv[g], tv[(g + 1) % G], tv[(g + 2) % G], tv[(g + 3) % G]);
+        else if (G == 2)
+          *reinterpret_cast<float2*>(dst) = make_float2(tv[0], tv[1 % G]);
+        else
+          dst[0] = tv[0];
+      }
+    }
+    __syncthreads();
+  }
 
-  const float* qg = qrot + (size_t)bk * G * D;
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
+  const int vshift = (row * kStepTokens * BV) & 31;  // 0, or 16 for odd widths
 
-  const int vpair = lane % P, vhalf = lane / P;  // value lane -> (pair, token half)
-
-  float m[G], l[G], acc0[G], acc1[G];
+  float m[G], l[G];
+  float2 acc[G][PPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
-    acc0[g] = 0.f;
-    acc1[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) acc[g][j] = make_float2(0.f, 0.f);
   }
 
-  for (int tile = tile_begin + wave; tile < tile_end; tile += 4) {
-    const uint8_t* tp = base + (size_t)tile * GE::BYTES;
+  TileRegs<D, G, BK, BV> cur, nxt;
+  int tile = tile_begin + wave;
+  if (tile < tile_end) load_tile(cur, base + (size_t)tile * GE::BYTES, lane, row, col);
+  for (; tile < tile_end; tile += NW) {
+    if (tile + NW < tile_end) load_tile(nxt, base + (size_t)(tile + NW) * GE::BYTES, lane, row, col);
     const int nvalid = min(a.seq_len - tile * kTile, kTile);
+    const bool valid = lane < nvalid;
 
     // ---- keys: lane = token slot
-    uint32_t ka[GE::WKA], kr[GE::WKR];
-#pragma unroll
-    for (int w = 0; w < GE::WKA; ++w) ka[w] = reinterpret_cast<const uint32_t*>(tp)[w * kTile + lane];
-#pragma unroll
-    for (int w = 0; w < GE::WKR; ++w)
-      kr[w] = reinterpret_cast<const uint32_t*>(tp + GE::OFF_KR)[w * kTile + lane];
-    const float kscale =
-        __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(tp + GE::OFF_KS)[lane]));
-    // value-plane words for this lane (issued early to overlap with the key math)
-    uint32_t va[WVA], vr[WVR];
-#pragma unroll
-    for (int w = 0; w < WVA; ++w)
-      va[w] = reinterpret_cast<const uint32_t*>(tp + GE::OFF_VA)[(w + vhalf * WVA) * P + vpair];
-#pragma unroll
-    for (int w = 0; w < WVR; ++w)
-      vr[w] = reinterpret_cast<const uint32_t*>(tp + GE::OFF_VR)[(w + vhalf * WVR) * P + vpair];
-    const uint32_t vpar = reinterpret_cast<const uint32_t*>(tp + GE::OFF_VP)[lane];
-
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
-    // q~ is read with scalar loads in chunks of CH pairs (2 * G * CH = 64 SGPRs); the
-    // empty asm makes the chunk's base opaque so the loads are not hoisted out of the
-    // tile loop (512+ live values would spill).
-    constexpr int CH = 32 / G < P ? 32 / G : P;
+    if (KT) {
 #pragma unroll
-    for (int i0 = 0; i0 < P; i0 += CH) {
-      const float* qc = qg + 2 * i0;
-      asm volatile("" : "+s"(qc));
+      for (int i = 0; i < P; ++i) {
+        const uint32_t c = field<BK>(cur.ka, i);
+        const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        const float* t = ktab + (i * NKT + c) * G;
+        float tv[G];
+        if (G >= 4) {
 #pragma unroll
-      for (int ii = 0; ii < CH; ++ii) {
-        const int i = i0 + ii;
-        const uint32_t c = field<BK>(ka, i);
-        const float rho = (float)((kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-        const float2 cs = lut_k[c];
-        const float x = rho * cs.x, y = rho * cs.y;
+          for (int g = 0; g < G; g += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(t + g);
+            tv[g] = v.x; tv[(g + 1) % G] = v.y; tv[(g + 2) % G] = v.z; tv[(g + 3) % G] = v.w;
+          }
+        } else if (G == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(t);
+          tv[0] = v.x; tv[1 % G] = v.y;
+        } else {
+          tv[0] = t[0];
+        }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-          sc[g] = fmaf(x, qc[g * D + 2 * ii], fmaf(y, qc[g * D + 2 * ii + 1], sc[g]));
+        for (int g = 0; g < G; ++g) sc[g] = fmaf(rho, tv[g], sc[g]);
+      }
+    } else {
+      // q~ in chunks of CH pairs through scalar loads (2 * G * CH = 64 SGPRs); the
+      // empty asm keeps the loads inside the tile loop
+      constexpr int CH = 32 / G < P ? 32 / G : P;
+#pragma unroll
+      for (int i0 = 0; i0 < P; i0 += CH) {
+        int qoff = 2 * i0;
+        asm volatile("" : "+s"(qoff));
+        const float* qc = qg + qoff;
+#pragma unroll
+        for (int ii = 0; ii < CH; ++ii) {
+          const int i = i0 + ii;
+          const uint32_t c = field<BK>(cur.ka, i);
+          const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+          const float2 cs = lut_k[c];
+          const float x = rho * cs.x, y = rho * cs.y;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            sc[g] = fmaf(x, qc[g * D + 2 * ii], fmaf(y, qc[g * D + 2 * ii + 1], sc[g]));
+        }
       }
     }
-    const bool valid = lane < nvalid;
+    const float kscale = __half2float(__ushort_as_half((uint16_t)cur.ks));
+
+    // ---- online softmax (base 2) per head; pr = p * r0 with the value vector's base
+    // radius r0 (s_min, or s_max when s_max <= s_min); slots past the end get 0
     float pr[G];
+    float beta = 0.f, r0 = 0.f;
+    {
+      const float smin = __half2float(__ushort_as_half((uint16_t)(cur.vp & 0xFFFFu)));
+      const float smax = __half2float(__ushort_as_half((uint16_t)(cur.vp >> 16)));
+      r0 = smax;
+      if (smax > smin) {
+        r0 = smin;
+        beta = (__log2f(smax) - __log2f(smin)) * (1.0f / 15.0f);
+      }
+      if (!valid) {
+        r0 = 0.f;
+        beta = 0.f;
+      }
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float s = valid ? sc[g] * kscale : -INFINITY;
       const float mnew = fmaxf(m[g], wave_max(s));
-      const float alpha = exp2f(m[g] - mnew);
-      const float pv = exp2f(s - mnew);
+      const float alpha = fast_exp2(m[g] - mnew);
+      const float pv = fast_exp2(s - mnew);
       l[g] = l[g] * alpha + wave_sum(pv);
-      acc0[g] *= alpha;
-      acc1[g] *= alpha;
       m[g] = mnew;
-      pr[g] = pv;
-    }
-
-    // ---- per-token value radius parameters (lane = token): r = 2^(lg + rho * beta)
-    float lg = 0.f, beta = 0.f;
-    if (valid) {
-      const float smin = __half2float(__ushort_as_half((uint16_t)(vpar & 0xFFFFu)));
-      const float smax = __half2float(__ushort_as_half((uint16_t)(vpar >> 16)));
-      if (smax > smin) {
-        lg = __log2f(smin);
-        beta = (__log2f(smax) - lg) * (1.0f / 15.0f);
-      } else {
-        lg = __log2f(smax);
+      pr[g] = pv * r0;
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        acc[g][j].x *= alpha;
+        acc[g][j].y *= alpha;
       }
     }
 
-    // ---- values: lane = pair (d = 64: the two half-waves take tokens j and j + 32)
+    // ---- values: lane (row, col); step k handles token slot 16 row + k
+    uint32_t va[PPL][C::VAW];
 #pragma unroll
-    for (int jj = 0; jj < NT; ++jj) {
-      if (jj >= nvalid) break;
-      float lgj, bj, pj[G];
-      if (NT == 64) {
-        lgj = readlane_f(lg, jj);
-        bj = readlane_f(beta, jj);
+    for (int j = 0; j < PPL; ++j) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) pj[g] = readlane_f(pr[g], jj);
-      } else {
-        const float l0 = readlane_f(lg, jj), l1 = readlane_f(lg, jj + 32);
-        const float b0 = readlane_f(beta, jj), b1 = readlane_f(beta, jj + 32);
-        lgj = vhalf ? l1 : l0;
-        bj = vhalf ? b1 : b0;
+      for (int w = 0; w < C::VAW; ++w) {
+        if (BV & 1)
+          va[j][w] = w + 1 < C::VAW ? __builtin_amdgcn_alignbit(cur.va[j][w + 1], cur.va[j][w], vshift)
+                                    : (cur.va[j][w] >> vshift);
+        else
+          va[j][w] = cur.va[j][w];
+      }
+    }
+    const int src0 = row * kStepTokens * 4;  // bpermute byte address of the row's slot 0
+#pragma unroll
+    for (int k = 0; k < kStepTokens; ++k) {
+      const int src = src0 + 4 * k;
+      float pj[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) pj[g] = bperm_f(src, pr[g]);
+      const float bj = bperm_f(src, beta);
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const uint32_t c = field<BV>(va[j], k);
+        const uint32_t rho = (cur.vr[j][k >> 3] >> (4 * (k & 7))) & 0xFu;
+        const float r = fast_exp2((float)rho * bj);
+        const float2 cs = lut_v[c];
+        const float vx = r * cs.x, vy = r * cs.y;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float p0 = readlane_f(pr[g], jj), p1 = readlane_f(pr[g], jj + 32);
-          pj[g] = vhalf ? p1 : p0;
+          acc[g][j].x = fmaf(pj[g], vx, acc[g][j].x);
+          acc[g][j].y = fmaf(pj[g], vy, acc[g][j].y);
         }
       }
-      const uint32_t c = field<BV>(va, jj);
-      const uint32_t rho = (vr[jj >> 3] >> (4 * (jj & 7))) & 0xFu;
-      const float r = exp2f(fmaf((float)rho, bj, lgj));
-      const float2 cs = lut_v[c];
-      const float vx = r * cs.x, vy = r * cs.y;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        acc0[g] = fmaf(pj[g], vx, acc0[g]);
-        acc1[g] = fmaf(pj[g], vy, acc1[g]);
-      }
     }
+    cur = nxt;
   }
 
-  // ---- merge the four waves, then this split's partial per query head
-  if (P == 32) {
+  // ---- rows hold partial sums for the same pairs: fold them into row 0
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      acc0[g] += __shfl_xor(acc0[g], 32);
-      acc1[g] += __shfl_xor(acc1[g], 32);
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      acc[g][j].x += __shfl_xor(acc[g][j].x, 16);
+      acc[g][j].y += __shfl_xor(acc[g][j].y, 16);
+      acc[g][j].x += __shfl_xor(acc[g][j].x, 32);
+      acc[g][j].y += __shfl_xor(acc[g][j].y, 32);
     }
   }
+  __syncthreads();  // every wave is done with the key table; reuse it for merging
+  float* s_ml = reinterpret_cast<float*>(s_union);         // [NW][G][2]
+  float* s_acc = s_ml + NW * G * 2;                          // [NW][G][D]
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = m[g];
-      s_l[wave][g] = l[g];
+      s_ml[(wave * G + g) * 2] = m[g];
+      s_ml[(wave * G + g) * 2 + 1] = l[g];
     }
   }
-  if (lane < P) {
+  if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      s_acc[wave][g][2 * lane] = acc0[g];
-      s_acc[wave][g][2 * lane + 1] = acc1[g];
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const int e = 2 * (col * PPL + j);
+        *reinterpret_cast<float2*>(s_acc + (wave * G + g) * D + e) = acc[g][j];
+      }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
     const int g = idx / D, e = idx % D;
-    float mm = s_m[0][g];
+    float mm = s_ml[g * 2];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mm = fmaxf(mm, s_m[w][g]);
+    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, s_ml[(w * G + g) * 2]);
     float ll = 0.f, aa = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(s_m[w][g] - mm);
-      ll += s_l[w][g] * f;
-      aa += s_acc[w][g][e] * f;
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(s_ml[(w * G + g) * 2] - mm);
+      ll += s_ml[(w * G + g) * 2 + 1] * f;
+      aa += s_acc[(w * G + g) * D + e] * f;
     }
-    const size_t row = ((size_t)bk * G + g) * a.nsplit + split;
-    a.part_acc[row * D + e] = aa;
+    const size_t rowi = ((size_t)bk * G + g) * a.nsplit + split;
+    a.part_acc[rowi * D + e] = aa;
     if (e == 0) {
-      a.part_ml[2 * row] = mm;
-      a.part_ml[2 * row + 1] = ll;
+      a.part_ml[2 * rowi] = mm;
+      a.part_ml[2 * rowi + 1] = ll;
     }
   }
 }
@@ -325,30 +470,47 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a,
 // ---------------------------------------------------------------------------- merge
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* __restrict__ out,
-                                                        int f32_out) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, void* __restrict__ out,
+                                                         int f32_out) {
   constexpr int P = D / 2;
+  __shared__ float s_red[4];
+  __shared__ float2 s_acc[4][P];
+  __shared__ float s_l[4];
   const int bh = blockIdx.x;  // b * hq + h
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* ml = a.part_ml + (size_t)bh * a.nsplit * 2;
   const float* acc = a.part_acc + (size_t)bh * a.nsplit * D;
+  // global max over the splits
   float mloc = -INFINITY;
-  for (int s = lane; s < a.nsplit; s += 64) mloc = fmaxf(mloc, ml[2 * s]);
-  const float mm = wave_max(mloc);
-  float lloc = 0.f;
-  for (int s = lane; s < a.nsplit; s += 64) lloc += ml[2 * s + 1] * exp2f(ml[2 * s] - mm);
-  const float ll = wave_sum(lloc);
-  if (lane >= P) return;
-  float a0 = 0.f, a1 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float f = exp2f(ml[2 * s] - mm);
-    const float2 v = reinterpret_cast<const float2*>(acc + (size_t)s * D)[lane];
-    a0 = fmaf(f, v.x, a0);
-    a1 = fmaf(f, v.y, a1);
+  for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
+  mloc = wave_max(mloc);
+  if (lane == 0) s_red[wave] = mloc;
+  __syncthreads();
+  const float mm = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  // wave w sums splits w, w + 4, ...; lane p owns pair p (two output elements)
+  float a0 = 0.f, a1 = 0.f, ll = 0.f;
+  if (lane < P) {
+    for (int s = wave; s < a.nsplit; s += 4) {
+      const float f = fast_exp2(ml[2 * s] - mm);
+      const float2 v = reinterpret_cast<const float2*>(acc + (size_t)s * D)[lane];
+      a0 = fmaf(f, v.x, a0);
+      a1 = fmaf(f, v.y, a1);
+      ll = fmaf(f, ml[2 * s + 1], ll);
+    }
+    s_acc[wave][lane] = make_float2(a0, a1);
   }
-  const float inv_l = 1.0f / ll;
-  a0 *= inv_l;
-  a1 *= inv_l;
+  if (lane == 0) s_l[wave] = ll;
+  __syncthreads();
+  if (wave != 0 || lane >= P) return;
+  float2 t = s_acc[0][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    t.x += s_acc[w][lane].x;
+    t.y += s_acc[w][lane].y;
+  }
+  const float inv_l = 1.0f / ((s_l[0] + s_l[1]) + (s_l[2] + s_l[3]));
+  a0 = t.x * inv_l;
+  a1 = t.y * inv_l;
   fwht_pairs_f32<P>(a0, a1, lane);
   const int e0 = 2 * lane;
   a0 *= a.inv_sqrt_d;
@@ -362,15 +524,29 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* __rest
     reinterpret_cast<__half2*>(out)[off >> 1] = __floats2half2_rn(a0, a1);
 }
 
+template <int D, int G, int BK, int BV>
+hipError_t split_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+  if constexpr (SplitCfg<D, G, BK, BV>::TAB_BYTES <= kKeyTableMaxBytes) {
+    if (a.key_table) {
+      hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, true>), grid, dim3(512), 0, s, a,
+                         cache, a.qrot);
+      return hipGetLastError();
+    }
+  }
+  if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
+  hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, false>), grid, dim3(512), 0, s, a, cache,
+                     a.qrot);
+  return hipGetLastError();
+}
+
 template <int D, int G, int BK>
 hipError_t split_bv(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   switch (a.bv) {
-    case 6: hipLaunchKernelGGL((attn_split_kernel<D, G, BK, 6>), grid, dim3(256), 0, s, a, cache, a.qrot); break;
-    case 7: hipLaunchKernelGGL((attn_split_kernel<D, G, BK, 7>), grid, dim3(256), 0, s, a, cache, a.qrot); break;
-    case 8: hipLaunchKernelGGL((attn_split_kernel<D, G, BK, 8>), grid, dim3(256), 0, s, a, cache, a.qrot); break;
+    case 6: return split_launch<D, G, BK, 6>(a, cache, grid, s);
+    case 7: return split_launch<D, G, BK, 7>(a, cache, grid, s);
+    case 8: return split_launch<D, G, BK, 8>(a, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int D, int G>
@@ -419,7 +595,7 @@ hipError_t launch_attn_split(const AttnArgs& a, int d, TileGeom geom, const uint
 
 hipError_t launch_attn_merge(const AttnArgs& a, int d, void* out, bool f32_out,
                              hipStream_t stream) {
-  const dim3 grid((unsigned)(a.batch * a.hq)), block(64);
+  const dim3 grid((unsigned)(a.batch * a.hq)), block(256);
   if (d == 64)
     hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, 0, stream, a, out, (int)f32_out);
   else if (d == 128)

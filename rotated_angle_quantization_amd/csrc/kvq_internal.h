@@ -75,6 +75,7 @@ struct AttnArgs {
   int batch, hkv, hq, group;
   int seq_len, tiles_per_seq, ntiles, nsplit, tiles_per_split;
   int n_k, n_v, bk, bv;
+  int key_table;       // 1: scores read a per-workgroup query table in LDS
   float q_scale;       // softmax scale * log2(e) / 255, folded into the rotated query
   float inv_sqrt_d;    // fp32 1/sqrt(d)
   SignMask sign;
@@ -82,6 +83,11 @@ struct AttnArgs {
   float* part_ml;      // [B, Hq, nsplit, 2]
   float* part_acc;     // [B, Hq, nsplit, d]
 };
+
+// Bytes of the per-workgroup key-score table (pairs x 2^bk codes x heads x fp32) and
+// the largest table the split kernel keeps in LDS.
+constexpr int kKeyTableMaxBytes = 128 * 1024;
+inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (1L << bk) * group * 4; }
 
 hipError_t launch_attn_prepare(const AttnArgs& a, int d, const void* q, bool f32_q,
                                hipStream_t stream);
