@@ -38,7 +38,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (used to "
+                         "scale rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: reads and writes exactly mib MiB once."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def record_bytes(d, n_k, n_v, tokens):
@@ -111,6 +126,10 @@ def main():
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
               "(no sharding or collectives); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import torch
 

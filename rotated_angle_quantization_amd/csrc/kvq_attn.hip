@@ -219,13 +219,27 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
   constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = 8;
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
   constexpr int UNION_BYTES = (KT && C::TAB_BYTES > MERGE_BYTES) ? C::TAB_BYTES : MERGE_BYTES;
-  __shared__ __align__(16) char s_union[UNION_BYTES];
-  __shared__ float2 lut_k[NKT], lut_v[1 << BV];
+  // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
+  // instruction's immediate offset; the key table (or the merge buffers) above them
+  constexpr int LUTK_OFF = 0, LUTV_OFF = NKT * 8, UNION_OFF = LUTV_OFF + (1 << BV) * 8;
+  __shared__ __align__(16) char smem[UNION_OFF + UNION_BYTES];
+  float2* lut_k = reinterpret_cast<float2*>(smem + LUTK_OFF);
+  float2* lut_v = reinterpret_cast<float2*>(smem + LUTV_OFF);
+  char* s_union = smem + UNION_OFF;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
   const float* qg = qrot + (size_t)bk * G * D;
+
+  // The first tile's loads go out before the tables are built, so their latency
+  // overlaps the set-up.
+  const int tile_begin = split * a.tiles_per_split;
+  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
+  const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
+  TileRegs<D, G, BK, BV> cur, nxt;
+  int tile = tile_begin + wave;
+  if (tile < tile_end) load_tile(cur, base + (size_t)tile * GE::BYTES, lane, row, col);
 
   // cos/sin of the bin centres 2 pi c / n; rows past n are only ever read for slots
   // past the sequence end and are zeroed
@@ -270,11 +284,13 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
     __syncthreads();
   }
 
-  const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
-  const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
   const int vshift = (row * kStepTokens * BV) & 31;  // 0, or 16 for odd widths
 
+  // Online softmax state per head: m = running reference (base-2 log units), l = per-lane
+  // partial sums of p (reduced once at the end). The reference is only raised when a
+  // score exceeds it by more than kLazy, so p <= 2^kLazy and most tiles skip the
+  // wave-wide max and the rescale.
+  constexpr float kLazy = 8.0f;
   float m[G], l[G];
   float2 acc[G][PPL];
 #pragma unroll
@@ -285,9 +301,6 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
     for (int j = 0; j < PPL; ++j) acc[g][j] = make_float2(0.f, 0.f);
   }
 
-  TileRegs<D, G, BK, BV> cur, nxt;
-  int tile = tile_begin + wave;
-  if (tile < tile_end) load_tile(cur, base + (size_t)tile * GE::BYTES, lane, row, col);
   for (; tile < tile_end; tile += NW) {
     if (tile + NW < tile_end) load_tile(nxt, base + (size_t)(tile + NW) * GE::BYTES, lane, row, col);
     const int nvalid = min(a.seq_len - tile * kTile, kTile);
@@ -343,8 +356,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
     }
     const float kscale = __half2float(__ushort_as_half((uint16_t)cur.ks));
 
-    // ---- online softmax (base 2) per head; pr = p * r0 with the value vector's base
-    // radius r0 (s_min, or s_max when s_max <= s_min); slots past the end get 0
+    // ---- softmax weights; pr = p * r0 with the value vector's base radius r0 (s_min,
+    // or s_max when s_max <= s_min); slots past the end get 0
     float pr[G];
     float beta = 0.f, r0 = 0.f;
     {
@@ -363,17 +376,20 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float s = valid ? sc[g] * kscale : -INFINITY;
-      const float mnew = fmaxf(m[g], wave_max(s));
-      const float alpha = fast_exp2(m[g] - mnew);
-      const float pv = fast_exp2(s - mnew);
-      l[g] = l[g] * alpha + wave_sum(pv);
-      m[g] = mnew;
-      pr[g] = pv * r0;
+      {
+        const float mnew = fmaxf(m[g], wave_max(s));
+        const float alpha = fast_exp2(m[g] - mnew);
+        l[g] *= alpha;
 #pragma unroll
-      for (int j = 0; j < PPL; ++j) {
-        acc[g][j].x *= alpha;
-        acc[g][j].y *= alpha;
+        for (int j = 0; j < PPL; ++j) {
+          acc[g][j].x *= alpha;
+          acc[g][j].y *= alpha;
+        }
+        m[g] = mnew;
       }
+      const float pv = fast_exp2(s - m[g]);
+      l[g] += pv;
+      pr[g] = pv * r0;
     }
 
     // ---- values: lane (row, col); step k handles token slot 16 row + k
@@ -389,6 +405,16 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
           va[j][w] = cur.va[j][w];
       }
     }
+    // 4-bit radius codes as bytes: low nibbles and high nibbles of each word
+    uint32_t vlo[PPL][2], vhi[PPL][2];
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        vlo[j][w] = cur.vr[j][w] & 0x0F0F0F0Fu;
+        vhi[j][w] = (cur.vr[j][w] >> 4) & 0x0F0F0F0Fu;
+      }
+    }
     const int src0 = row * kStepTokens * 4;  // bpermute byte address of the row's slot 0
 #pragma unroll
     for (int k = 0; k < kStepTokens; ++k) {
@@ -400,8 +426,9 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
 #pragma unroll
       for (int j = 0; j < PPL; ++j) {
         const uint32_t c = field<BV>(va[j], k);
-        const uint32_t rho = (cur.vr[j][k >> 3] >> (4 * (k & 7))) & 0xFu;
-        const float r = fast_exp2((float)rho * bj);
+        const uint32_t nib = (k & 1) ? vhi[j][k >> 3] : vlo[j][k >> 3];
+        const float rho = (float)((nib >> (8 * ((k >> 1) & 3))) & 0xFFu);
+        const float r = fast_exp2(rho * bj);
         const float2 cs = lut_v[c];
         const float vx = r * cs.x, vy = r * cs.y;
 #pragma unroll
@@ -413,6 +440,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
     }
     cur = nxt;
   }
+#pragma unroll
+  for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
 
   // ---- rows hold partial sums for the same pairs: fold them into row 0
 #pragma unroll
