@@ -5,17 +5,22 @@
 // Quantization" (arXiv 2603.27467), Abstract. Readings (bin placement, ties, fp16
 // parameters, log-radius floor) are documented with kvq_encode in kvq.h.
 //
-// Every decision that turns a real number into an integer (angle bin, radius level,
-// fp16 rounding of the per-vector parameters) is taken in IEEE binary64, so the codes
-// do not depend on launch shape and agree with a float64 reference except where an
-// angle falls within rounding distance of a bin boundary.
+// Exactness. The transform runs in binary64; for fp16 inputs every partial sum is
+// exact there (at most ~40 significant bits), so the rotated pairs equal a float64
+// reference's. Each integer decision (angle bin, key and value radius level) is first
+// taken from fp32 estimates whose error is bounded; when the estimate lies within that
+// bound (times a safety factor) of a decision boundary, the decision is recomputed
+// with the binary64 formula. Per-vector fp16 parameters are always formed in
+// binary64. So the codes match a float64 reference except where a float64 angle
+// itself sits within rounding distance of a bin boundary.
 //
-// Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens). A lane owns
-// one coordinate pair of a vector (d = 128: one vector per step; d = 64: two vectors
-// per step, one per half-wave), so the transform's first stage is in-lane and the
-// others are cross-lane exchanges. Codes of the whole tile are staged in LDS as bytes
-// and then packed: key planes with one lane per token, value planes with one lane
-// per pair, matching the layout's word order so every store is a coalesced dword.
+// Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens); a lane owns a
+// quarter of one vector (d/4 consecutive elements), so 16 tokens are coded per step.
+// The transform's first log2(d/4) stages are in-lane; the last two exchange with
+// lanes xor 1 and xor 2 through DPP quad permutes. Per-vector maxima, minima and
+// parameters are reduced over the quad. Codes of the tile are staged in LDS as bytes
+// and then packed: key planes one lane per token, value planes one lane per pair,
+// matching the layout's word order so every store is a coalesced dword.
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
@@ -44,78 +49,65 @@ __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
   return (m.w[e >> 6] >> (e & 63)) & 1ull;
 }
 
-// In-place Walsh-Hadamard transform of one vector held as (a, b) = elements
-// (2p, 2p+1) in lane p of a P-lane group: stage h = 1 is in-lane, stage h = 2m pairs
-// lane p with lane p ^ m. Natural (Sylvester) output order.
-template <int P>
-__device__ __forceinline__ void fwht_pairs(double& a, double& b, int p) {
-  const double s = a + b, t = a - b;
-  a = s;
-  b = t;
-#pragma unroll
-  for (int m = 1; m < P; m <<= 1) {
-    const double pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-    if (p & m) {
-      a = pa - a;
-      b = pb - b;
-    } else {
-      a = a + pa;
-      b = b + pb;
-    }
-  }
+// Lane exchange inside a quad (lanes 4k..4k+3) of a double: xor 1 or xor 2.
+template <int CTRL>
+__device__ __forceinline__ double quad_xor(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 
-template <int P>
-__device__ __forceinline__ double group_max(double x) {
-#pragma unroll
-  for (int m = 1; m < P; m <<= 1) x = fmax(x, __shfl_xor(x, m));
-  return x;
-}
+constexpr int kRow = 68;  // LDS row stride (bytes) of the per-token code staging
 
-template <int P>
-__device__ __forceinline__ double group_min(double x) {
-#pragma unroll
-  for (int m = 1; m < P; m <<= 1) x = fmin(x, __shfl_xor(x, m));
-  return x;
-}
-
-// Uniform angle quantiser: nearest of n centres 2 pi c / n; zero pair -> 0.
-__device__ __forceinline__ int angle_code(double r, double theta, double bins_per_rad, int n) {
-  if (r == 0.0) return 0;
-  int c = (int)floor(theta * bins_per_rad + 0.5);
+// Uniform angle quantiser in binary64: nearest of n centres 2 pi c / n.
+__device__ __forceinline__ int angle_code_f64(double a, double b, double bins_per_rad, int n) {
+  int c = (int)floor(atan2(b, a) * bins_per_rad + 0.5);
   c %= n;
   if (c < 0) c += n;
   return c;
 }
 
-__device__ __forceinline__ void load_pair(const void* base, bool f32, int64_t off, double& x0,
-                                          double& x1) {
-  if (f32) {
-    const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(base) + off);
-    x0 = v.x;
-    x1 = v.y;
+// Angle code of a nonzero pair. Estimate: theta32 = atan2f of the fp32-rounded pair
+// (rounding moves the angle by <= 2^-24 rad, atan2f by a few ulp, <= ~1.2e-6 rad in
+// all), c = nearest centre, and the distance to the bin edge is measured in radians
+// through an fp32 residual theta32 - c * (2 pi / n) (rounding of the bin width adds
+// <= c * 2^-24 * 2 pi / n < 4e-7 rad). Within kAngleMargin of an edge the binary64
+// formula decides.
+constexpr float kAngleMargin = 8e-6f;  // rad, >= 4x the estimate's worst-case error
+__device__ __forceinline__ int angle_code(double a, double b, double bins_per_rad, int n,
+                                          float bins_per_rad_f, float bin_rad_f) {
+  const float th = atan2f((float)b, (float)a);
+  const float cf = rintf(th * bins_per_rad_f);
+  const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
+  const float edge = 0.5f * bin_rad_f - fabsf(res);
+  int c;
+  if (edge < kAngleMargin) {
+    c = angle_code_f64(a, b, bins_per_rad, n);
   } else {
-    const __half2 v = *reinterpret_cast<const __half2*>(static_cast<const __half*>(base) + off);
-    x0 = __half2float(__low2half(v));
-    x1 = __half2float(__high2half(v));
+    c = (int)cf % n;
+    if (c < 0) c += n;
   }
+  return c;
 }
 
-constexpr int kRow = 68;  // LDS row stride (bytes) of the per-token code staging
-
-template <int D>
+template <int D, bool F32IN>
 __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
                                                     uint8_t* __restrict__ cache,
                                                     const void* __restrict__ kin,
-                                                    const void* __restrict__ vin, int f32_in,
+                                                    const void* __restrict__ vin,
                                                     int64_t sb, int64_t st, int64_t sh) {
-  constexpr int P = D / 2;
-  constexpr int VPW = 64 / P;  // vectors per wave step
+  constexpr int P = D / 2;    // pairs per vector
+  constexpr int E = D / 4;    // elements per lane
+  constexpr int PL = E / 2;   // pairs per lane
+  constexpr int TPS = 16;     // tokens per step (4 lanes each)
   __shared__ uint8_t s_kc[kTile][kRow], s_kr[kTile][kRow], s_vc[kTile][kRow], s_vr[kTile][kRow];
   __shared__ uint16_t s_ks[kTile];
   __shared__ uint32_t s_vp[kTile];
 
   const int lane = threadIdx.x;
+  const int tq = lane >> 2, q = lane & 3;  // token within the step, quarter of the vector
   const int tile_rel = blockIdx.x % a.tiles_touched;
   const int bh = blockIdx.x / a.tiles_touched;
   const int b = bh / a.hkv, h = bh % a.hkv;
@@ -124,57 +116,147 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
   const int j_lo = max(a.t0 - tok_base, 0);
   const int j_hi = min(a.t0 + a.ntok - tok_base, kTile);
 
-  const int p = lane % P;    // pair index within the vector
-  const int sub = lane / P;  // which vector of the wave step
-  const int e0 = 2 * p;
-  const double sg0 = sign_neg(a.sign, e0) ? -1.0 : 1.0;
-  const double sg1 = sign_neg(a.sign, e0 + 1) ? -1.0 : 1.0;
+  // this lane's sign bits (elements q*E .. q*E+E-1); for fp16 input, per-pair xor masks
+  // on the fp16 sign bits (bits 15 and 31 of a packed pair)
+  const uint32_t sbits = (uint32_t)(a.sign.w[(q * E) >> 6] >> ((q * E) & 63)) &
+                         (E == 32 ? 0xFFFFFFFFu : ((1u << E) - 1u));
+  uint32_t hmask[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k)
+    hmask[k] = (((sbits >> (2 * k)) & 1u) << 15) | (((sbits >> (2 * k + 1)) & 1u) << 31);
+  const double qsgn1 = (q & 1) ? -1.0 : 1.0, qsgn2 = (q & 2) ? -1.0 : 1.0;
+  const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;
+  const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
 
-  for (int jb = j_lo; jb < j_hi; jb += VPW) {
-    const int j = jb + sub;
+  for (int jb = j_lo; jb < j_hi; jb += TPS) {
+    const int j = jb + tq;
     const bool act = j < j_hi;
-    double k0 = 0.0, k1 = 0.0, v0 = 0.0, v1 = 0.0;
-    if (act) {
-      const int64_t off =
-          (int64_t)b * sb + (int64_t)(tok_base + j - a.t0) * st + (int64_t)h * sh + e0;
-      load_pair(kin, f32_in, off, k0, k1);
-      load_pair(vin, f32_in, off, v0, v1);
-    }
-    // keys
-    k0 *= sg0;
-    k1 *= sg1;
-    fwht_pairs<P>(k0, k1, p);
-    k0 *= a.inv_sqrt_d;
-    k1 *= a.inv_sqrt_d;
-    const double kr = hypot(k0, k1);
-    const int kc = angle_code(kr, atan2(k1, k0), a.k_bins_per_rad, a.n_k);
-    const double ks = fp16_round_pos(fmin(group_max<P>(kr), kFp16Max));
-    int krho = 0;
-    if (ks > 0.0) krho = (int)fmin(fmax(floor(255.0 * kr / ks + 0.5), 0.0), 255.0);
-    // values
-    v0 *= sg0;
-    v1 *= sg1;
-    fwht_pairs<P>(v0, v1, p);
-    v0 *= a.inv_sqrt_d;
-    v1 *= a.inv_sqrt_d;
-    const double vr = hypot(v0, v1);
-    const int vc = angle_code(vr, atan2(v1, v0), a.v_bins_per_rad, a.n_v);
-    const double vmax = group_max<P>(vr), vmin = group_min<P>(vr);
-    const double smax = fp16_round_pos(fmin(vmax, kFp16Max));
-    const double smin = fp16_round_pos(fmin(fmax(vmin, kFp16MinNormal), kFp16Max));
-    int vrho = 0;
-    if (smax > smin && vr >= smin) {
-      const double lam = log(smax / smin);
-      vrho = (int)fmin(fmax(floor(15.0 * log(vr / smin) / lam + 0.5), 0.0), 15.0);
-    }
-    if (act) {
-      s_kc[j][p] = (uint8_t)kc;
-      s_kr[j][p] = (uint8_t)krho;
-      s_vc[j][p] = (uint8_t)vc;
-      s_vr[j][p] = (uint8_t)vrho;
-      if (p == 0) {
-        s_ks[j] = fp16_bits(ks);
-        s_vp[j] = (uint32_t)fp16_bits(smin) | ((uint32_t)fp16_bits(smax) << 16);
+    // lanes past the range read the last valid row and discard it
+    const int jr = act ? j : j_hi - 1;
+    const int64_t row_off =
+        (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + q * E;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const void* src = kv == 0 ? kin : vin;
+      // load, apply the sign diagonal, widen to binary64
+      double y[E];
+      if (F32IN) {
+        const float* p = static_cast<const float*>(src) + row_off;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float f = p[e];
+          if (!act) f = 0.f;
+          if ((sbits >> e) & 1u) f = -f;
+          y[e] = (double)f;
+        }
+      } else {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const __half*>(src) + row_off);
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+          uint32_t w = p[k];
+          w = (act ? w : 0u) ^ hmask[k];
+          y[2 * k] = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
+          y[2 * k + 1] = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
+        }
+      }
+      // Walsh-Hadamard: in-lane stages, then lanes xor 1 and xor 2 (natural order)
+#pragma unroll
+      for (int hs = 1; hs < E; hs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          if (i & hs) continue;
+          const double u = y[i], v = y[i + hs];
+          y[i] = u + v;
+          y[i + hs] = u - v;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] = fma(y[i], qsgn1, quad_xor<kQuadXor1>(y[i]));
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] = fma(y[i], qsgn2, quad_xor<kQuadXor2>(y[i]));
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] *= a.inv_sqrt_d;
+
+      double r2[PL];
+      double mx = 0.0, mn = INFINITY;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        r2[k] = fma(y[2 * k + 1], y[2 * k + 1], y[2 * k] * y[2 * k]);
+        mx = fmax(mx, r2[k]);
+        mn = fmin(mn, r2[k]);
+      }
+      mx = fmax(mx, quad_xor<kQuadXor1>(mx));
+      mx = fmax(mx, quad_xor<kQuadXor2>(mx));
+
+      uint8_t cc[PL], rr[PL];
+      if (kv == 0) {
+        // keys: s = fp16(max r); level = floor(255 r / s + 1/2). Estimate from fp32
+        // (sqrtf of the rounded r^2, times 255/s): relative error <= 4 * 2^-24, i.e.
+        // <= 6.1e-5 in level units; kLevelMargin = 2.5e-4 levels.
+        const double s = fp16_round_pos(fmin(sqrt(mx), kFp16Max));
+        const float sc255 = s > 0.0 ? (float)(255.0 / s) : 0.f;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.k_bins_per_rad,
+                                                          a.n_k, kbpr, kbin);
+          int rho = 0;
+          if (s > 0.0) {
+            const float t = sqrtf((float)r2[k]) * sc255 + 0.5f;
+            const float fl = floorf(t);
+            if (fminf(t - fl, fl + 1.0f - t) < 2.5e-4f)
+              rho = (int)floor(255.0 * sqrt(r2[k]) / s + 0.5);
+            else
+              rho = (int)fl;
+            rho = min(max(rho, 0), 255);
+          }
+          rr[k] = (uint8_t)rho;
+        }
+        if (act && q == 0) s_ks[j] = fp16_bits(s);
+      } else {
+        // values: s_max = fp16(max r), s_min = fp16(max(min r, 2^-14)); level =
+        // floor(15 ln(r / s_min) / L + 1/2), L = ln(s_max / s_min). Estimate:
+        // 7.5 log2f(r^2 / s_min^2) / log2(s_max / s_min) from fp32; its error is
+        // bounded by (7.5 / L2) (3 * 2^-24 / ln 2 + ulp(|log2|)) plus the rounding of
+        // the sum, which the margin below covers with a factor of >= 4.
+        mn = fmin(mn, quad_xor<kQuadXor1>(mn));
+        mn = fmin(mn, quad_xor<kQuadXor2>(mn));
+        const double smax = fp16_round_pos(fmin(sqrt(mx), kFp16Max));
+        const double smin = fp16_round_pos(fmin(fmax(sqrt(mn), kFp16MinNormal), kFp16Max));
+        const bool spread = smax > smin;
+        const double lam = spread ? log(smax / smin) : 1.0;
+        const double smin2 = smin * smin;
+        const float l2f = (float)(lam * 1.4426950408889634);
+        const float scale = 7.5f / l2f;
+        const float inv_smin2 = (float)(1.0 / smin2);
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.v_bins_per_rad,
+                                                          a.n_v, vbpr, vbin);
+          int rho = 0;
+          if (spread && r2[k] >= smin2) {
+            const float lr = __log2f((float)r2[k] * inv_smin2);
+            const float t = lr * scale + 0.5f;
+            const float fl = floorf(t);
+            const float margin = scale * (1e-6f + 5e-7f * fabsf(lr)) + 1e-5f;
+            if (fminf(t - fl, fl + 1.0f - t) < margin)
+              rho = (int)floor(15.0 * log(sqrt(r2[k]) / smin) / lam + 0.5);
+            else
+              rho = (int)fl;
+            rho = min(max(rho, 0), 15);
+          }
+          rr[k] = (uint8_t)rho;
+        }
+        if (act && q == 0)
+          s_vp[j] = (uint32_t)fp16_bits(smin) | ((uint32_t)fp16_bits(smax) << 16);
+      }
+      if (act) {
+        uint8_t* dc = kv == 0 ? &s_kc[j][q * PL] : &s_vc[j][q * PL];
+        uint8_t* dr = kv == 0 ? &s_kr[j][q * PL] : &s_vr[j][q * PL];
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+          dc[k] = cc[k];
+          dr[k] = rr[k];
+        }
       }
     }
   }
@@ -266,12 +348,14 @@ hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cach
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64);
-  if (d == 64)
-    hipLaunchKernelGGL(encode_kernel<64>, grid, block, 0, stream, a, geom, cache, k, v,
-                       (int)f32_in, sb, st, sh);
+  if (d == 64 && f32_in)
+    hipLaunchKernelGGL((encode_kernel<64, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+  else if (d == 64)
+    hipLaunchKernelGGL((encode_kernel<64, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+  else if (d == 128 && f32_in)
+    hipLaunchKernelGGL((encode_kernel<128, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
   else if (d == 128)
-    hipLaunchKernelGGL(encode_kernel<128>, grid, block, 0, stream, a, geom, cache, k, v,
-                       (int)f32_in, sb, st, sh);
+    hipLaunchKernelGGL((encode_kernel<128, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
