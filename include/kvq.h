@@ -132,9 +132,12 @@ kvq_status kvq_layer_signs(uint64_t seed, uint32_t layer, uint32_t d, int8_t* ou
  *   values: s_max = fp16(max r), s_min = fp16(max(min r, 2^-14));
  *           L = ln(s_max / s_min); code = 0 if r < s_min, else
  *           clamp(floor(15 ln(r / s_min) / L + 1/2), 0, 15); s_max <= s_min -> 0
- * All decisions are taken in IEEE binary64, so codes are reproducible across runs
- * and launch shapes. Slots outside [t0, t0 + ntok) are left unchanged, so a
- * chunked append produces the same bytes as a one-shot encode.
+ * The transform and the fp16 parameters are computed in IEEE binary64. Each code is
+ * taken from an fp32 estimate only when the estimate is farther from the decision
+ * boundary than its worst-case error; otherwise the binary64 formula above decides.
+ * Codes are therefore those of a binary64 evaluation, reproducible across runs and
+ * launch shapes. Slots outside [t0, t0 + ntok) are left unchanged, so a chunked
+ * append produces the same bytes as a one-shot encode.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (d not 64/128), CAPACITY (t0 + ntok >
  * capacity), HIP. ntok = 0 enqueues nothing and returns KVQ_OK.
  */
@@ -147,7 +150,8 @@ kvq_status kvq_encode(const kvq_layer_desc* desc, void* cache, const void* k, co
  * with y_hat[2i] = r_hat cos(2 pi c / n), y_hat[2i+1] = r_hat sin(2 pi c / n);
  * key r_hat = code * s / 255; value r_hat = s_min * exp(code * L / 15) (s_max when
  * s_max <= s_min). Arithmetic in fp32.
- * k_out, v_out: contiguous device tensors [B, ntok, Hkv, d] of out_dtype.
+ * k_out, v_out: contiguous device tensors [B, ntok, Hkv, d] of out_dtype, 16-byte
+ * aligned (rows are written as 8- and 16-byte vectors).
  * Errors: as kvq_encode.
  */
 kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out,

@@ -225,9 +225,7 @@ kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, v
   if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
   if (ntok == 0) return KVQ_OK;
   if (!cache || !k_out || !v_out) return KVQ_ERR_INVALID_ARGUMENT;
-  const size_t esz = out_dtype == KVQ_F32 ? 4 : 2;
-  if (((uintptr_t)k_out % (2 * esz)) || ((uintptr_t)v_out % (2 * esz)))
-    return KVQ_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)k_out % 16) || ((uintptr_t)v_out % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   const CodecArgs a = codec_args(d, t0, ntok);
   return hip_status(launch_decode(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
                                   k_out, v_out, out_dtype == KVQ_F32, (hipStream_t)stream));

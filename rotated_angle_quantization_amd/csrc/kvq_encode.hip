@@ -15,7 +15,8 @@
 // itself sits within rounding distance of a bin boundary.
 //
 // Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens); a lane owns a
-// quarter of one vector (d/4 consecutive elements), so 16 tokens are coded per step.
+// quarter of one vector (d/4 elements in interleaved 8-element chunks), so 16 tokens
+// are coded per step.
 // The transform's first log2(d/4) stages are in-lane; the last two exchange with
 // lanes xor 1 and xor 2 through DPP quad permutes. Per-vector maxima, minima and
 // parameters are reduced over the quad. Codes of the tile are staged in LDS as bytes
@@ -116,10 +117,15 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
   const int j_lo = max(a.t0 - tok_base, 0);
   const int j_hi = min(a.t0 + a.ntok - tok_base, kTile);
 
-  // this lane's sign bits (elements q*E .. q*E+E-1); for fp16 input, per-pair xor masks
-  // on the fp16 sign bits (bits 15 and 31 of a packed pair)
-  const uint32_t sbits = (uint32_t)(a.sign.w[(q * E) >> 6] >> ((q * E) & 63)) &
-                         (E == 32 ? 0xFFFFFFFFu : ((1u << E) - 1u));
+  // Lane q of a token's quad owns the 8-element chunks m*4 + q (elements
+  // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
+  // element strides 1, 2, 4 and 32, 64; strides 8 and 16 are the quad exchanges. Local
+  // bit 8m + r of sbits is the sign of element 32m + 8q + r; for fp16 input the per-pair
+  // xor masks flip the fp16 sign bits (bits 15 and 31 of a packed pair).
+  uint32_t sbits = 0;
+#pragma unroll
+  for (int m = 0; m < E / 8; ++m)
+    sbits |= (uint32_t)((a.sign.w[(32 * m + 8 * q) >> 6] >> ((32 * m + 8 * q) & 63)) & 0xFFu) << (8 * m);
   uint32_t hmask[PL];
 #pragma unroll
   for (int k = 0; k < PL; ++k)
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
     // lanes past the range read the last valid row and discard it
     const int jr = act ? j : j_hi - 1;
     const int64_t row_off =
-        (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + q * E;
+        (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const void* src = kv == 0 ? kin : vin;
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
         const float* p = static_cast<const float*>(src) + row_off;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          float f = p[e];
+          float f = p[32 * (e >> 3) + (e & 7)];
           if (!act) f = 0.f;
           if ((sbits >> e) & 1u) f = -f;
           y[e] = (double)f;
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
         const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const __half*>(src) + row_off);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          uint32_t w = p[k];
+          uint32_t w = p[16 * (k >> 2) + (k & 3)];
           w = (act ? w : 0u) ^ hmask[k];
           y[2 * k] = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
           y[2 * k + 1] = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
@@ -250,12 +256,14 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
           s_vp[j] = (uint32_t)fp16_bits(smin) | ((uint32_t)fp16_bits(smax) << 16);
       }
       if (act) {
-        uint8_t* dc = kv == 0 ? &s_kc[j][q * PL] : &s_vc[j][q * PL];
-        uint8_t* dr = kv == 0 ? &s_kr[j][q * PL] : &s_vr[j][q * PL];
+        // local pair k is pair 16 (k / 4) + 4 q + k % 4 of the vector
+        uint8_t* dc = kv == 0 ? s_kc[j] : s_vc[j];
+        uint8_t* dr = kv == 0 ? s_kr[j] : s_vr[j];
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          dc[k] = cc[k];
-          dr[k] = rr[k];
+          const int i = 16 * (k >> 2) + 4 * q + (k & 3);
+          dc[i] = cc[k];
+          dr[i] = rr[k];
         }
       }
     }

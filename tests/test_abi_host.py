@@ -97,6 +97,7 @@ def test_decode_validation():
     assert dec(k=None) == INVALID
     assert dec(dt=2) == INVALID
     assert dec(v=FAKE + 2) == INVALID
+    assert dec(k=FAKE + 8) == INVALID  # outputs must be 16-byte aligned
 
 
 def _attn(desc, hq=32, seq=100, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, qdt=0, odt=0,
