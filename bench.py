@@ -56,6 +56,35 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def split_kernel_name(d, group, n_k, n_v):
+    """Name of the split-kernel instantiation the library launches for this shape (the
+    key-score table is used when P * 2^bk * G * 4 bytes fit in 128 KiB of LDS)."""
+    bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
+    kt = (d // 2) * (1 << bk) * group * 4 <= 128 * 1024
+    return f"attn_split_kernel<{d}, {group}, {bk}, {bv}, {'true' if kt else 'false'}>"
+
+
+def split_traffic(cfg):
+    """Calibrated HBM bytes per split launch from the committed rocprofv3 counter
+    record, or None if the record is for another workload or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_split_{cfg.name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    total = 0.0
+    for layer in range(cfg.layers):
+        name = split_kernel_name(cfg.d, cfg.group, *cfg.bins(layer))
+        if name not in rec["per_kernel"]:
+            return None
+        total += rec["per_kernel"][name]["bytes"]
+    return total / cfg.layers
+
+
 def record_bytes(d, n_k, n_v, tokens):
     """Algorithmic compressed bytes of `tokens` token-heads (one record per token-head)."""
     import rotated_angle_quantization_amd as kvq
@@ -242,7 +271,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": split_traffic(cfg),
             "avg_launch_ms": round(split_avg_ms, 5),
             "bytes_per_launch": split_bytes_avg,
         },
