@@ -62,39 +62,62 @@ constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 
 constexpr int kRow = 68;  // LDS row stride (bytes) of the per-token code staging
 
-// Uniform angle quantiser in binary64: nearest of n centres 2 pi c / n.
-__device__ __forceinline__ int angle_code_f64(double a, double b, double bins_per_rad, int n) {
-  int c = (int)floor(atan2(b, a) * bins_per_rad + 0.5);
+// atan(z) on [0, 1]: odd polynomial z * sum_k c_k z^2k, least-squares fitted to atan
+// (measured maximum error 2.5e-7 rad on [0, 1]; 3.5e-7 rad evaluated in fp32).
+__device__ __forceinline__ float atan01(float z) {
+  const float s = z * z;
+  float p = 0.006806020624935627f;
+  p = fmaf(p, s, -0.03358602523803711f);
+  p = fmaf(p, s, 0.07960157096385956f);
+  p = fmaf(p, s, -0.13232044875621796f);
+  p = fmaf(p, s, 0.19807438552379608f);
+  p = fmaf(p, s, -0.3331731855869293f);
+  p = fmaf(p, s, 0.9999960660934448f);
+  return p * z;
+}
+
+// Angle of a nonzero pair in fp32, by octant reduction: |error| <= 3.5e-7 (polynomial)
+// + 1.2e-7 (z = min/max through the reciprocal) + 6e-8 (rounding the pair to fp32)
+// + 2.4e-7 (the two reflections about pi/2 and pi) < 8e-7 rad.
+__device__ __forceinline__ float angle_f32(float a, float b) {
+  const float ax = fabsf(a), ay = fabsf(b);
+  const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
+  const float p = atan01(mn * __builtin_amdgcn_rcpf(mx));
+  float t = ay > ax ? 1.5707963267948966f - p : p;
+  t = a < 0.f ? 3.141592653589793f - t : t;
+  return b < 0.f ? -t : t;
+}
+
+// Angle code of a nonzero pair: nearest of n centres 2 pi c / n, i.e.
+// floor(theta n / (2 pi) + 1/2) mod n. The fp32 estimate theta32 (error < 8e-7 rad)
+// gives the centre cf and the distance to the nearest bin edge through the residual
+// theta32 - cf * (2 pi / n) (rounding of the bin width adds < 4e-7 rad). When that
+// distance is below kAngleMargin the pair is compared in binary64 with the edge's
+// direction (bedge[k] = (cos, sin) of (k + 1/2) 2 pi / n): on or past the edge means
+// the upper bin, as the floor above gives at an exact half.
+constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
+__device__ __forceinline__ int angle_code(double a, double b, int n, float bins_per_rad_f,
+                                          float bin_rad_f, const double2* bedge) {
+  const float th = angle_f32((float)a, (float)b);
+  const float cf = rintf(th * bins_per_rad_f);
+  const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
+  int c = (int)cf;
+  if (__builtin_expect(0.5f * bin_rad_f - fabsf(res) < kAngleMargin, 0)) {
+    const int k = res > 0.f ? c : c - 1;  // edge between centres k and k + 1
+    int kk = k % n;
+    if (kk < 0) kk += n;
+    const double2 e = bedge[kk];
+    c = fma(e.x, b, -e.y * a) >= 0.0 ? k + 1 : k;
+  }
   c %= n;
   if (c < 0) c += n;
   return c;
 }
 
-// Angle code of a nonzero pair. Estimate: theta32 = atan2f of the fp32-rounded pair
-// (rounding moves the angle by <= 2^-24 rad, atan2f by a few ulp, <= ~1.2e-6 rad in
-// all), c = nearest centre, and the distance to the bin edge is measured in radians
-// through an fp32 residual theta32 - c * (2 pi / n) (rounding of the bin width adds
-// <= c * 2^-24 * 2 pi / n < 4e-7 rad). Within kAngleMargin of an edge the binary64
-// formula decides.
-constexpr float kAngleMargin = 8e-6f;  // rad, >= 4x the estimate's worst-case error
-__device__ __forceinline__ int angle_code(double a, double b, double bins_per_rad, int n,
-                                          float bins_per_rad_f, float bin_rad_f) {
-  const float th = atan2f((float)b, (float)a);
-  const float cf = rintf(th * bins_per_rad_f);
-  const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
-  const float edge = 0.5f * bin_rad_f - fabsf(res);
-  int c;
-  if (edge < kAngleMargin) {
-    c = angle_code_f64(a, b, bins_per_rad, n);
-  } else {
-    c = (int)cf % n;
-    if (c < 0) c += n;
-  }
-  return c;
-}
+constexpr int kEncWaves = 4;  // waves (tiles) per workgroup, sharing the edge tables
 
 template <int D, bool F32IN>
-__global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
+__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, TileGeom g,
                                                     uint8_t* __restrict__ cache,
                                                     const void* __restrict__ kin,
                                                     const void* __restrict__ vin,
@@ -103,19 +126,38 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
   constexpr int E = D / 4;    // elements per lane
   constexpr int PL = E / 2;   // pairs per lane
   constexpr int TPS = 16;     // tokens per step (4 lanes each)
-  __shared__ uint8_t s_kc[kTile][kRow], s_kr[kTile][kRow], s_vc[kTile][kRow], s_vr[kTile][kRow];
-  __shared__ uint16_t s_ks[kTile];
-  __shared__ uint32_t s_vp[kTile];
+  __shared__ uint8_t s_code[kEncWaves][4][kTile][kRow];  // key angle, key radius, value angle, value radius
+  __shared__ uint16_t s_ks_all[kEncWaves][kTile];
+  __shared__ uint32_t s_vp_all[kEncWaves][kTile];
+  __shared__ double2 s_kedge[256], s_vedge[256];  // bin edges (k + 1/2) 2 pi / n
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tq = lane >> 2, q = lane & 3;  // token within the step, quarter of the vector
-  const int tile_rel = blockIdx.x % a.tiles_touched;
-  const int bh = blockIdx.x / a.tiles_touched;
+  for (int k = threadIdx.x; k < 256; k += kEncWaves * 64) {
+    double sn, co;
+    sincospi((2.0 * k + 1.0) / a.n_k, &sn, &co);
+    s_kedge[k] = make_double2(co, sn);
+    sincospi((2.0 * k + 1.0) / a.n_v, &sn, &co);
+    s_vedge[k] = make_double2(co, sn);
+  }
+  __syncthreads();
+  uint8_t(*s_kc)[kRow] = s_code[wave][0];
+  uint8_t(*s_kr)[kRow] = s_code[wave][1];
+  uint8_t(*s_vc)[kRow] = s_code[wave][2];
+  uint8_t(*s_vr)[kRow] = s_code[wave][3];
+  uint16_t* s_ks = s_ks_all[wave];
+  uint32_t* s_vp = s_vp_all[wave];
+  // one tile per wave; waves past the last tile do no work (but take the barrier)
+  const int task = blockIdx.x * kEncWaves + wave;
+  const int ntasks = a.batch * a.hkv * a.tiles_touched;
+  const bool live = task < ntasks;
+  const int tile_rel = task % a.tiles_touched;
+  const int bh = live ? task / a.tiles_touched : 0;
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int tile = a.tile_lo + tile_rel;
   const int tok_base = tile * kTile;
   const int j_lo = max(a.t0 - tok_base, 0);
-  const int j_hi = min(a.t0 + a.ntok - tok_base, kTile);
+  const int j_hi = live ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
 
   // Lane q of a token's quad owns the 8-element chunks m*4 + q (elements
   // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
@@ -131,7 +173,7 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
   for (int k = 0; k < PL; ++k)
     hmask[k] = (((sbits >> (2 * k)) & 1u) << 15) | (((sbits >> (2 * k + 1)) & 1u) << 31);
   const double qsgn1 = (q & 1) ? -1.0 : 1.0, qsgn2 = (q & 2) ? -1.0 : 1.0;
-  const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;
+  const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;  // n / (2 pi)
   const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
 
   for (int jb = j_lo; jb < j_hi; jb += TPS) {
@@ -196,23 +238,27 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
 
       uint8_t cc[PL], rr[PL];
       if (kv == 0) {
-        // keys: s = fp16(max r); level = floor(255 r / s + 1/2). Estimate from fp32
-        // (sqrtf of the rounded r^2, times 255/s): relative error <= 4 * 2^-24, i.e.
-        // <= 6.1e-5 in level units; kLevelMargin = 2.5e-4 levels.
+        // keys: s = fp16(max r); level = floor(255 r / s + 1/2). Estimate in fp32:
+        // hardware sqrt (<= 2 ulp) of the rounded r^2, times 255/s: relative error
+        // < 4e-7, i.e. < 1.1e-4 levels with the final rounding. Within 5e-4 of a
+        // half-integer the level is decided by comparing r^2 with ((m - 1/2) s / 255)^2
+        // in binary64.
         const double s = fp16_round_pos(fmin(sqrt(mx), kFp16Max));
         const float sc255 = s > 0.0 ? (float)(255.0 / s) : 0.f;
+        const double s_255 = s / 255.0;
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.k_bins_per_rad,
-                                                          a.n_k, kbpr, kbin);
+          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_k, kbpr, kbin,
+                                                          s_kedge);
           int rho = 0;
           if (s > 0.0) {
-            const float t = sqrtf((float)r2[k]) * sc255 + 0.5f;
-            const float fl = floorf(t);
-            if (fminf(t - fl, fl + 1.0f - t) < 2.5e-4f)
-              rho = (int)floor(255.0 * sqrt(r2[k]) / s + 0.5);
-            else
-              rho = (int)fl;
+            const float t = __builtin_amdgcn_sqrtf((float)r2[k]) * sc255 + 0.5f;
+            const float m = rintf(t);
+            rho = (int)floorf(t);
+            if (__builtin_expect(fabsf(t - m) < 5e-4f, 0)) {
+              const double thr = ((double)m - 0.5) * s_255;
+              rho = r2[k] >= thr * thr ? (int)m : (int)m - 1;
+            }
             rho = min(max(rho, 0), 255);
           }
           rr[k] = (uint8_t)rho;
@@ -236,18 +282,17 @@ __global__ __launch_bounds__(64) void encode_kernel(CodecArgs a, TileGeom g,
         const float inv_smin2 = (float)(1.0 / smin2);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.v_bins_per_rad,
-                                                          a.n_v, vbpr, vbin);
+          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_v, vbpr, vbin,
+                                                          s_vedge);
           int rho = 0;
           if (spread && r2[k] >= smin2) {
             const float lr = __log2f((float)r2[k] * inv_smin2);
             const float t = lr * scale + 0.5f;
             const float fl = floorf(t);
             const float margin = scale * (1e-6f + 5e-7f * fabsf(lr)) + 1e-5f;
-            if (fminf(t - fl, fl + 1.0f - t) < margin)
+            rho = (int)fl;
+            if (__builtin_expect(fminf(t - fl, fl + 1.0f - t) < margin, 0))
               rho = (int)floor(15.0 * log(sqrt(r2[k]) / smin) / lam + 0.5);
-            else
-              rho = (int)fl;
             rho = min(max(rho, 0), 15);
           }
           rr[k] = (uint8_t)rho;
@@ -355,7 +400,7 @@ hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cach
   const long long blocks = (long long)a.batch * a.hkv * a.tiles_touched;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(64);
+  const dim3 grid((unsigned)((blocks + kEncWaves - 1) / kEncWaves)), block(kEncWaves * 64);
   if (d == 64 && f32_in)
     hipLaunchKernelGGL((encode_kernel<64, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
   else if (d == 64)

@@ -371,3 +371,29 @@ def test_radius_decoders_hit_the_interval_ends():
     assert lv[0] == pytest.approx(0.125, rel=1e-15)
     assert lv[15] == pytest.approx(8.0, rel=1e-14)
     np.testing.assert_allclose(lv[1:] / lv[:-1], 64.0 ** (1 / 15), rtol=1e-13)
+
+
+def test_exact_tie_has_two_correct_codes():
+    """A pair exactly on a bin edge (only angles at multiples of pi/4 can be): with
+    n = 100 an edge sits at 45 degrees (12.5 bins). The rule floor(t + 1/2) sends the
+    exact tie to bin 13; float64 evaluation of t lands just below 12.5 and gives 12.
+    Both bins meet at the edge, so the parity rule accepts either."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from parity import compare_codes
+    n = 100
+    r, th = oc.polar(np.array([[0.75, 0.75]]))
+    t = oc.angle_position(th, n)
+    assert abs(t[0, 0] - 12.5) < 1e-12
+    assert oc.angle_codes(r, th, n)[0, 0] in (12, 13)
+    enc = {"angle": oc.angle_codes(r, th, n), "theta": th, "r": r, "n": n,
+           "near_boundary": oc.angle_near_boundary(th, n), "radius": np.zeros((1, 1), int),
+           "scale": np.zeros(1), "s_min": np.zeros(1), "s_max": np.zeros(1)}
+    for code in (12, 13):
+        got = {"k_angle": np.array([[code]]), "v_angle": np.array([[code]]),
+               "k_radius": np.zeros((1, 1), int), "v_radius": np.zeros((1, 1), int),
+               "k_scale": np.zeros(1), "v_smin": np.zeros(1), "v_smax": np.zeros(1)}
+        assert compare_codes(got, enc, enc)["pairs"] == 2
+    got["k_angle"] = np.array([[14]])
+    with pytest.raises(AssertionError):
+        compare_codes(got, enc, enc)
