@@ -36,10 +36,14 @@ constexpr double kFp16Subnormal = 5.9604644775390625e-08;  // 2^-24
 // Nearest fp16 value of a non-negative x <= 65504, ties to even, computed exactly in
 // binary64: the fp16 spacing at x is 2^(e-10) (2^-24 below the normal range), so
 // rint(x / q) * q rounds to 11 significant bits with no double rounding.
+__device__ __forceinline__ double pow2(int e) {  // 2^e for -1022 <= e <= 1023
+  return __longlong_as_double((long long)(e + 1023) << 52);
+}
 __device__ __forceinline__ double fp16_round_pos(double x) {
   if (x == 0.0) return 0.0;
-  const double q = x < kFp16MinNormal ? kFp16Subnormal : ldexp(1.0, ilogb(x) - 10);
-  return rint(x / q) * q;
+  // 2^(e-10) with x in [2^e, 2^(e+1)); frexp's exponent is e + 1
+  const int e = x < kFp16MinNormal ? -14 : __builtin_amdgcn_frexp_exp(x) - 1;
+  return rint(x * pow2(10 - e)) * pow2(e - 10);  // scaling by powers of two is exact
 }
 
 __device__ __forceinline__ uint16_t fp16_bits(double exact_fp16_value) {
@@ -101,17 +105,15 @@ __device__ __forceinline__ int angle_code(double a, double b, int n, float bins_
   const float th = angle_f32((float)a, (float)b);
   const float cf = rintf(th * bins_per_rad_f);
   const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
-  int c = (int)cf;
+  int c = (int)cf;  // in [-n/2, n/2]
   if (__builtin_expect(0.5f * bin_rad_f - fabsf(res) < kAngleMargin, 0)) {
     const int k = res > 0.f ? c : c - 1;  // edge between centres k and k + 1
-    int kk = k % n;
-    if (kk < 0) kk += n;
+    const int kk = k < 0 ? k + n : (k >= n ? k - n : k);
     const double2 e = bedge[kk];
     c = fma(e.x, b, -e.y * a) >= 0.0 ? k + 1 : k;
   }
-  c %= n;
-  if (c < 0) c += n;
-  return c;
+  c = c < 0 ? c + n : c;
+  return c >= n ? c - n : c;
 }
 
 constexpr int kEncWaves = 4;  // waves (tiles) per workgroup, sharing the edge tables
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         // half-integer the level is decided by comparing r^2 with ((m - 1/2) s / 255)^2
         // in binary64.
         const double s = fp16_round_pos(fmin(sqrt(mx), kFp16Max));
-        const float sc255 = s > 0.0 ? (float)(255.0 / s) : 0.f;
-        const double s_255 = s / 255.0;
+        const float sc255 = s > 0.0 ? 255.0f * __builtin_amdgcn_rcpf((float)s) : 0.f;
+        const double s_255 = s * (1.0 / 255.0);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
           cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_k, kbpr, kbin,
@@ -275,24 +277,28 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         const double smax = fp16_round_pos(fmin(sqrt(mx), kFp16Max));
         const double smin = fp16_round_pos(fmin(fmax(sqrt(mn), kFp16MinNormal), kFp16Max));
         const bool spread = smax > smin;
-        const double lam = spread ? log(smax / smin) : 1.0;
         const double smin2 = smin * smin;
-        const float l2f = (float)(lam * 1.4426950408889634);
-        const float scale = 7.5f / l2f;
-        const float inv_smin2 = (float)(1.0 / smin2);
+        // log2(s_max / s_min) from the fp32 ratio (s_max, s_min are fp16 values, exact
+        // in fp32): error < 4e-7 absolute
+        const float l2f = spread ? __log2f((float)smax * __builtin_amdgcn_rcpf((float)smin)) : 1.f;
+        const float scale = 7.5f * __builtin_amdgcn_rcpf(l2f);
+        const float inv_smin2 = __builtin_amdgcn_rcpf((float)smin2);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
           cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_v, vbpr, vbin,
                                                           s_vedge);
           int rho = 0;
           if (spread && r2[k] >= smin2) {
+            // lr = log2(r^2 / s_min^2) <= 2 l2; t = 7.5 lr / l2 + 1/2. With absolute
+            // errors <= 7e-7 (lr) and 4e-7 (l2), |dt| <= 7.5 (7e-7 + 2 * 4e-7) / l2 plus
+            // ~1e-6 of fp32 rounding; the margin below is more than twice that.
             const float lr = __log2f((float)r2[k] * inv_smin2);
             const float t = lr * scale + 0.5f;
             const float fl = floorf(t);
-            const float margin = scale * (1e-6f + 5e-7f * fabsf(lr)) + 1e-5f;
+            const float margin = scale * (4e-6f + 1e-6f * fabsf(lr)) + 2e-5f;
             rho = (int)fl;
             if (__builtin_expect(fminf(t - fl, fl + 1.0f - t) < margin, 0))
-              rho = (int)floor(15.0 * log(sqrt(r2[k]) / smin) / lam + 0.5);
+              rho = (int)floor(15.0 * log(sqrt(r2[k]) / smin) / log(smax / smin) + 0.5);
             rho = min(max(rho, 0), 15);
           }
           rr[k] = (uint8_t)rho;
