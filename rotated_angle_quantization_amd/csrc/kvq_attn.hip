@@ -13,15 +13,23 @@
 //
 // Three launches on one stream:
 //   prepare  q~ = R q, pre-multiplied by softmax_scale * log2(e) / 255, into the
-//            workspace (read back by the split kernel through scalar loads).
-//   split    grid (splits, batch * kv heads), 4 waves per workgroup; each wave
-//            streams whole 64-token tiles. Keys: one lane per token, codes unpacked
-//            from registers with compile-time bit offsets, cos/sin from an LDS table,
-//            q~ from SGPRs. Online softmax per wave (base-2). Values: one lane per
-//            pair, probabilities broadcast with readlane, rotated-domain accumulate.
-//            Waves merge through LDS; each split writes (max, sum, acc[d]) per head.
+//            workspace.
+//   split    grid (splits, batch * kv heads); each wave streams whole 64-token tiles
+//            (12 waves per workgroup with the key table, else 8). Keys: one lane per
+//            token; the score of pair i is one FMA per head against a per-workgroup
+//            LDS table T[i][code][head] = q~_2i cos + q~_2i+1 sin (or, when the table
+//            would not fit, cos/sin from a small LDS table times q~ from SGPRs).
+//            Online softmax per wave in base 2. Values: lanes are 4 rows x 16
+//            columns; each step takes one token per row, its weights broadcast along
+//            the row with DPP, its 16 radius levels computed once per row and gathered
+//            with a lane permute, cos/sin from LDS. Waves merge through LDS; each split
+//            writes (max, sum, acc[d]) per head.
 //   merge    per (batch, query head): log-sum-exp combine of the splits, divide,
 //            inverse transform, sign, store.
+//
+// The split kernel is bound by VALU issue, not by HBM: every (token, pair) of a tile
+// costs G FMAs for the score and 2G for the value sum, and a wave64 FP32 FMA occupies
+// a SIMD for four cycles on this chip.
 #include <hip/hip_fp16.h>
 #include <math.h>
 
@@ -165,24 +173,34 @@ struct TileRegs {
   uint32_t va[C::PPL][C::VAW], vr[C::PPL][2];
 };
 
+// Key planes of one tile (lane = token slot).
 template <int D, int G, int BK, int BV>
-__device__ __forceinline__ void load_tile(TileRegs<D, G, BK, BV>& t, const uint8_t* tp,
-                                          int lane, int row, int col) {
-  using C = SplitCfg<D, G, BK, BV>;
-  using GE = typename C::GE;
-  constexpr int P = C::P, PPL = C::PPL;
+__device__ __forceinline__ void load_tile_keys(TileRegs<D, G, BK, BV>& t, const uint8_t* tp,
+                                               int lane) {
+  using GE = typename SplitCfg<D, G, BK, BV>::GE;
   const uint32_t* w32 = reinterpret_cast<const uint32_t*>(tp);
 #pragma unroll
   for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
 #pragma unroll
   for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
   t.ks = reinterpret_cast<const uint16_t*>(tp + GE::OFF_KS)[lane];
+}
+
+// Value planes of one tile in the row/column order of the value lanes, plus the
+// per-token radius parameters (lane = token slot).
+template <int D, int G, int BK, int BV>
+__device__ __forceinline__ void load_tile_values(TileRegs<D, G, BK, BV>& t, const uint8_t* tp,
+                                                 int lane, int row, int col) {
+  using C = SplitCfg<D, G, BK, BV>;
+  using GE = typename C::GE;
+  constexpr int P = C::P, PPL = C::PPL;
+  const uint32_t* w32 = reinterpret_cast<const uint32_t*>(tp);
   t.vp = w32[GE::OFF_VP / 4 + lane];
   const int w0 = (row * kStepTokens * BV) >> 5;
 #pragma unroll
   for (int w = 0; w < C::VAW; ++w) {
     const uint32_t* src = w32 + GE::OFF_VA / 4 + (w0 + w) * P + col * PPL;
-    if (PPL == 4) {
+    if constexpr (PPL == 4) {
       const uint4 v = *reinterpret_cast<const uint4*>(src);
       t.va[0][w] = v.x; t.va[1 % PPL][w] = v.y; t.va[2 % PPL][w] = v.z; t.va[3 % PPL][w] = v.w;
     } else {
@@ -193,7 +211,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D, G, BK, BV>& t, const uint8
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const uint32_t* src = w32 + GE::OFF_VR / 4 + (2 * row + w) * P + col * PPL;
-    if (PPL == 4) {
+    if constexpr (PPL == 4) {
       const uint4 v = *reinterpret_cast<const uint4*>(src);
       t.vr[0][w] = v.x; t.vr[1 % PPL][w] = v.y; t.vr[2 % PPL][w] = v.z; t.vr[3 % PPL][w] = v.w;
     } else {
@@ -203,20 +221,64 @@ __device__ __forceinline__ void load_tile(TileRegs<D, G, BK, BV>& t, const uint8
   }
 }
 
+// G consecutive floats from LDS (16-byte aligned when G >= 4).
+template <int G>
+__device__ __forceinline__ void load_row(float (&tv)[G], const float* t) {
+  if constexpr (G >= 4) {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(t + g);
+      tv[g] = v.x; tv[g + 1] = v.y; tv[g + 2] = v.z; tv[g + 3] = v.w;
+    }
+  } else if constexpr (G == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(t);
+    tv[0] = v.x; tv[1] = v.y;
+  } else {
+    tv[0] = t[0];
+  }
+}
+
+// Broadcast lane 16 * row + k to every lane of its row of 16 (DPP row_newbcast).
+__device__ __forceinline__ float row_bcast(float v, int k) {
+  const int x = __float_as_int(v);
+  int r;
+  switch (k) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false); break;
+    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false); break;
+    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false); break;
+    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false); break;
+    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false); break;
+    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, false); break;
+    case 9: r = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, false); break;
+    case 10: r = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, false); break;
+    case 11: r = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, false); break;
+    case 12: r = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, false); break;
+    case 13: r = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, false); break;
+    case 14: r = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
 __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
 }
+
+// Waves per split workgroup: 12 (three per SIMD) when the key table is used with up to
+// four heads per kv head, which leaves the kernel under 168 VGPRs; otherwise 8.
+constexpr int split_waves(bool key_table, int group) { return key_table && group <= 4 ? 12 : 8; }
 
 // KT: scores read a per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) +
 // q~_h,2i+1 sin(2 pi c / n) from LDS, one FMA per (pair, head); otherwise scores
 // use the cos/sin table and the rotated query from scalar registers.
 template <int D, int G, int BK, int BV, bool KT>
-__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
-                                                         const uint8_t* __restrict__ cache,
-                                                         const float* __restrict__ qrot) {
+__global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
+    AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot) {
   using C = SplitCfg<D, G, BK, BV>;
   using GE = typename C::GE;
-  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = 8;
+  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KT, G);
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
   constexpr int UNION_BYTES = (KT && C::TAB_BYTES > MERGE_BYTES) ? C::TAB_BYTES : MERGE_BYTES;
   // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
@@ -227,19 +289,20 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
   float2* lut_v = reinterpret_cast<float2*>(smem + LUTV_OFF);
   char* s_union = smem + UNION_OFF;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
   const float* qg = qrot + (size_t)bk * G * D;
 
-  // The first tile's loads go out before the tables are built, so their latency
+  // The first tile's key loads go out before the tables are built, so their latency
   // overlaps the set-up.
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
-  TileRegs<D, G, BK, BV> cur, nxt;
+  TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
-  if (tile < tile_end) load_tile(cur, base + (size_t)tile * GE::BYTES, lane, row, col);
+  if (tile < tile_end) load_tile_keys(cur, base + (size_t)tile * GE::BYTES, lane);
 
   // cos/sin of the bin centres 2 pi c / n; rows past n are only ever read for slots
   // past the sequence end and are zeroed
@@ -302,7 +365,11 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
   }
 
   for (; tile < tile_end; tile += NW) {
-    if (tile + NW < tile_end) load_tile(nxt, base + (size_t)(tile + NW) * GE::BYTES, lane, row, col);
+    // No register double-buffering: several waves per SIMD cover each other's load
+    // latency, and the value planes are only requested once the scores are done, which
+    // keeps the register count low enough for that occupancy.
+    const uint8_t* tp = base + (size_t)tile * GE::BYTES;
+    if (tile != tile_begin + wave) load_tile_keys(cur, tp, lane);
     const int nvalid = min(a.seq_len - tile * kTile, kTile);
     const bool valid = lane < nvalid;
 
@@ -311,26 +378,32 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
     if (KT) {
+      // Software pipeline over blocks of KB pairs: the table reads of block b + 1 are
+      // issued before the FMAs of block b, so the LDS latency overlaps arithmetic
+      // (the scheduling fences keep the compiler from re-serialising them).
+      constexpr int KB = 4, NKB = P / KB;
+      float tb[2][KB][G];
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const uint32_t c = field<BK>(cur.ka, i);
-        const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-        const float* t = ktab + (i * NKT + c) * G;
-        float tv[G];
-        if (G >= 4) {
+      for (int blk = 0; blk <= NKB; ++blk) {
+        if (blk < NKB) {
 #pragma unroll
-          for (int g = 0; g < G; g += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(t + g);
-            tv[g] = v.x; tv[(g + 1) % G] = v.y; tv[(g + 2) % G] = v.z; tv[(g + 3) % G] = v.w;
+          for (int ii = 0; ii < KB; ++ii) {
+            const int i = blk * KB + ii;
+            const uint32_t c = field<BK>(cur.ka, i);
+            load_row<G>(tb[blk & 1][ii], ktab + (i * NKT + c) * G);
           }
-        } else if (G == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(t);
-          tv[0] = v.x; tv[1 % G] = v.y;
-        } else {
-          tv[0] = t[0];
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (blk > 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[g] = fmaf(rho, tv[g], sc[g]);
+          for (int ii = 0; ii < KB; ++ii) {
+            const int i = (blk - 1) * KB + ii;
+            const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+#pragma unroll
+            for (int g = 0; g < G; ++g) sc[g] = fmaf(rho, tb[(blk - 1) & 1][ii][g], sc[g]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       // q~ in chunks of CH pairs through scalar loads (2 * G * CH = 64 SGPRs); the
@@ -354,6 +427,7 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
         }
       }
     }
+    load_tile_values(cur, tp, lane, row, col);
     const float kscale = __half2float(__ushort_as_half((uint16_t)cur.ks));
 
     // ---- softmax weights; pr = p * r0 with the value vector's base radius r0 (s_min,
@@ -405,31 +479,34 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
           va[j][w] = cur.va[j][w];
       }
     }
-    // 4-bit radius codes as bytes: low nibbles and high nibbles of each word
-    uint32_t vlo[PPL][2], vhi[PPL][2];
+    // Radius levels: at step k the 16 lanes of a row compute the 16 possible radii
+    // 2^(level * beta) of their token (lane col takes level col), and each lane gathers
+    // the levels of its pairs with a lane permute. The gather addresses are bytes
+    // 4 * (16 row + level): low nibbles (even slots) and high nibbles (odd slots).
+    uint32_t alo[PPL][2], ahi[PPL][2];
+    const uint32_t rowb = 0x01010101u * (uint32_t)(64 * row);
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        vlo[j][w] = cur.vr[j][w] & 0x0F0F0F0Fu;
-        vhi[j][w] = (cur.vr[j][w] >> 4) & 0x0F0F0F0Fu;
+        alo[j][w] = ((cur.vr[j][w] & 0x0F0F0F0Fu) << 2) | rowb;
+        ahi[j][w] = ((cur.vr[j][w] >> 2) & 0x3C3C3C3Cu) | rowb;
       }
     }
-    const int src0 = row * kStepTokens * 4;  // bpermute byte address of the row's slot 0
+    const float colf = (float)col;
 #pragma unroll
     for (int k = 0; k < kStepTokens; ++k) {
-      const int src = src0 + 4 * k;
+      // token slot 16 row + k: its softmax weights and radius step broadcast along the
+      // row with DPP; the lane's level gathered from the row's 16 computed levels
       float pj[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) pj[g] = bperm_f(src, pr[g]);
-      const float bj = bperm_f(src, beta);
+      for (int g = 0; g < G; ++g) pj[g] = row_bcast(pr[g], k);
+      const float lev = fast_exp2(colf * row_bcast(beta, k));
 #pragma unroll
       for (int j = 0; j < PPL; ++j) {
-        const uint32_t c = field<BV>(va[j], k);
-        const uint32_t nib = (k & 1) ? vhi[j][k >> 3] : vlo[j][k >> 3];
-        const float rho = (float)((nib >> (8 * ((k >> 1) & 3))) & 0xFFu);
-        const float r = fast_exp2(rho * bj);
-        const float2 cs = lut_v[c];
+        const float2 cs = lut_v[field<BV>(va[j], k)];
+        const uint32_t aw = (k & 1) ? ahi[j][k >> 3] : alo[j][k >> 3];
+        const float r = bperm_f((int)((aw >> (8 * ((k >> 1) & 3))) & 0xFFu), lev);
         const float vx = r * cs.x, vy = r * cs.y;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -438,7 +515,6 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a,
         }
       }
     }
-    cur = nxt;
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
@@ -557,13 +633,13 @@ template <int D, int G, int BK, int BV>
 hipError_t split_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   if constexpr (SplitCfg<D, G, BK, BV>::TAB_BYTES <= kKeyTableMaxBytes) {
     if (a.key_table) {
-      hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, true>), grid, dim3(512), 0, s, a,
+      hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, true>), grid, dim3(split_waves(true, G) * 64), 0, s, a,
                          cache, a.qrot);
       return hipGetLastError();
     }
   }
   if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
-  hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, false>), grid, dim3(512), 0, s, a, cache,
+  hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, false>), grid, dim3(split_waves(false, G) * 64), 0, s, a, cache,
                      a.qrot);
   return hipGetLastError();
 }
