@@ -238,27 +238,28 @@ __device__ __forceinline__ void load_row(float (&tv)[G], const float* t) {
   }
 }
 
-// Broadcast lane 16 * row + k to every lane of its row of 16 (DPP row_newbcast).
+// Broadcast lane 16 * row + k to every lane of its row of 16 (DPP row_newbcast). Every
+// source lane is valid, so the bound-control bit only spares a move of the old value.
 __device__ __forceinline__ float row_bcast(float v, int k) {
   const int x = __float_as_int(v);
   int r;
   switch (k) {
-    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false); break;
-    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false); break;
-    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false); break;
-    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false); break;
-    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false); break;
-    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false); break;
-    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, false); break;
-    case 9: r = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, false); break;
-    case 10: r = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, false); break;
-    case 11: r = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, false); break;
-    case 12: r = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, false); break;
-    case 13: r = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, false); break;
-    case 14: r = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, true); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, true); break;
+    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, true); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, true); break;
+    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, true); break;
+    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, true); break;
+    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, true); break;
+    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, true); break;
+    case 9: r = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, true); break;
+    case 10: r = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, true); break;
+    case 11: r = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, true); break;
+    case 12: r = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, true); break;
+    case 13: r = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, true); break;
+    case 14: r = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, true); break;
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, true); break;
   }
   return __int_as_float(r);
 }
@@ -506,7 +507,8 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
       for (int j = 0; j < PPL; ++j) {
         const float2 cs = lut_v[field<BV>(va[j], k)];
         const uint32_t aw = (k & 1) ? ahi[j][k >> 3] : alo[j][k >> 3];
-        const float r = bperm_f((int)((aw >> (8 * ((k >> 1) & 3))) & 0xFFu), lev);
+        // the permute reads only address bits 2..7, so the byte needs no masking
+        const float r = bperm_f((int)(aw >> (8 * ((k >> 1) & 3))), lev);
         const float vx = r * cs.x, vy = r * cs.y;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
