@@ -3,13 +3,13 @@
 One step = the whole path over one batch of synthetic input, all layers:
   encode   K/V [B, T, Hkv, d] fp16 -> packed cache (kvq_encode), every layer
   attend   one decode query per sequence over the full compressed cache
-           (kvq_attn_prepare + kvq_attn_split + kvq_attn_merge), every layer
+           (kvq_attn_decode: one kernel launch), every layer
   dequant  packed cache -> fp16 K/V (kvq_decode), every layer
 Inputs and caches are resident in HBM before timing starts. `value` is decode-attention
 throughput in GB/s of compressed cache read per second over the attention phase of a
 step (all layers, every launch and gap included). Phase times come from HIP events on
-the stream the library launches on. The split kernel (the dominant attention kernel)
-is bracketed by its own events for the roofline figure.
+the stream the library launches on. Each attention launch (the dominant kernel) is
+also bracketed by its own events for the roofline figure.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mistral7b]
 """
@@ -56,20 +56,20 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def split_kernel_name(d, group, n_k, n_v):
-    """Name of the split-kernel instantiation the library launches for this shape (the
-    key-score table is used when P * 2^bk * G * 4 bytes fit in 128 KiB of LDS)."""
+def attn_kernel_name(d, group, n_k, n_v):
+    """Name of the attention-kernel instantiation the library launches for this shape
+    (the key-score table is used when P * 2^bk * G * 4 bytes fit in 128 KiB of LDS)."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
     kt = (d // 2) * (1 << bk) * group * 4 <= 128 * 1024
-    return f"attn_split_kernel<{d}, {group}, {bk}, {bv}, {'true' if kt else 'false'}>"
+    return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {'true' if kt else 'false'}>"
 
 
-def split_traffic(cfg):
-    """Calibrated HBM bytes per split launch from the committed rocprofv3 counter
+def attn_traffic(cfg):
+    """Calibrated HBM bytes per attention launch from the committed rocprofv3 counter
     record, or None if the record is for another workload or the kernel source has
     changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"attn_split_{cfg.name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"attn_decode_{cfg.name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -78,7 +78,7 @@ def split_traffic(cfg):
         return None
     total = 0.0
     for layer in range(cfg.layers):
-        name = split_kernel_name(cfg.d, cfg.group, *cfg.bins(layer))
+        name = attn_kernel_name(cfg.d, cfg.group, *cfg.bins(layer))
         if name not in rec["per_kernel"]:
             return None
         total += rec["per_kernel"][name]["bytes"]
@@ -183,7 +183,7 @@ def main():
         vs.append(v)
         qs.append(query(cfg, layer, dev))
     ws_bytes = max(kvq.attn_workspace_bytes(dd, Hq, T) for dd in descs)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled once, reused
     outs = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
     kd = torch.empty((B, T, Hkv, d), dtype=torch.float16, device=dev)
     vd = torch.empty_like(kd)
@@ -198,23 +198,21 @@ def main():
 
     def step(record):
         e = [Ev() for _ in range(4)]
-        split_ev = [(Ev(), Ev()) for _ in range(L)]
+        attn_ev = [(Ev(), Ev()) for _ in range(L)]
         e[0].record()
         for layer in range(L):
             kvq.encode(descs[layer], caches[layer], ks[layer], vs[layer], 0)
         e[1].record()
         for layer in range(L):
-            kvq.attn_prepare(descs[layer], qs[layer], T, ws)
-            split_ev[layer][0].record()
-            kvq.attn_split(descs[layer], caches[layer], Hq, T, ws)
-            split_ev[layer][1].record()
-            kvq.attn_merge(descs[layer], Hq, T, outs, ws)
+            attn_ev[layer][0].record()
+            kvq.attn_decode(descs[layer], caches[layer], qs[layer], T, workspace=ws, out=outs)
+            attn_ev[layer][1].record()
         e[2].record()
         for layer in range(L):
             kvq.decode(descs[layer], caches[layer], 0, T, out=(kd, vd))
         e[3].record()
         if record is not None:
-            record.append((e, split_ev))
+            record.append((e, attn_ev))
 
     for _ in range(args.warmup):
         step(None)
@@ -230,12 +228,12 @@ def main():
     att_ms = sum(e[1].elapsed_time(e[2]) for e, _ in recs) / args.steps
     deq_ms = sum(e[2].elapsed_time(e[3]) for e, _ in recs) / args.steps
     step_ms = sum(e[0].elapsed_time(e[3]) for e, _ in recs) / args.steps
-    split_ms = [a.elapsed_time(b) for _, sp in recs for a, b in sp]
-    split_avg_ms = sum(split_ms) / len(split_ms)
-    split_bytes_avg = attn_bytes / L
+    launch_ms = [a.elapsed_time(b) for _, sp in recs for a, b in sp]
+    launch_avg_ms = sum(launch_ms) / len(launch_ms)
+    launch_bytes_avg = attn_bytes / L
 
     attn_gbps = attn_bytes / (att_ms * 1e-3) / 1e9
-    achieved = split_bytes_avg / (split_avg_ms * 1e-3) / 1e9
+    achieved = launch_bytes_avg / (launch_avg_ms * 1e-3) / 1e9
     tokens = B * T
     result = {
         "metric": METRIC,
@@ -265,15 +263,15 @@ def main():
         "dequant_out_GBps": round(2 * L * B * T * Hkv * d * 2 / (deq_ms * 1e-3) / 1e9, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "attn_split_kernel (kvq_attn_split)",
+            "kernel": "attn_decode_kernel (kvq_attn_decode)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": split_traffic(cfg),
-            "avg_launch_ms": round(split_avg_ms, 5),
-            "bytes_per_launch": split_bytes_avg,
+            "traffic": attn_traffic(cfg),
+            "avg_launch_ms": round(launch_avg_ms, 5),
+            "bytes_per_launch": launch_bytes_avg,
         },
     }
     if not args.no_cpu_baseline:

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -165,14 +165,18 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  * head floor(h / G)). Scores are formed in the rotated domain (the query is rotated
  * once; <q, k_hat> = <R q, y_hat_k>), probabilities weight rotated-domain values,
  * and one inverse transform per output head brings o back. Work is split over the
- * sequence (flash-decoding style) and partial (max, sum, vector) triples are merged
- * with a log-sum-exp combine. fp32 arithmetic.
+ * sequence (flash-decoding style); the last workgroup of each (batch, kv head) to
+ * finish merges the partial (max, sum, vector) triples with a log-sum-exp combine, so
+ * the whole operation is one kernel launch. fp32 arithmetic.
  *
  * q:   contiguous device tensor [B, Hq, d], q_dtype f16 or f32.
  * out: contiguous device tensor [B, Hq, d], out_dtype f16 or f32.
  * softmax_scale <= 0 selects 1/sqrt(d).
  * workspace: device buffer of at least kvq_attn_workspace_bytes(desc, Hq, seq_len)
- *   bytes, 256-byte aligned; scratch for the rotated query and split partials.
+ *   bytes, 256-byte aligned, owned by the caller. It must be zero-filled once after
+ *   allocation; every call that completes leaves it ready for the next (its split
+ *   counters back at zero). It holds the rotated queries and split partials. Calls
+ *   that share one workspace must not run concurrently (one stream).
  * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; angle codes of 6 to 8 bits
  *   (n in [33, 256]) for K and V; 1 <= seq_len <= capacity.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
@@ -185,26 +189,9 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* desc, const void* cache, const 
                            float softmax_scale, void* out, kvq_dtype out_dtype,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/*
- * The three launches kvq_attn_decode makes, exposed so a caller can time or
- * schedule them separately. Same arguments and rules as kvq_attn_decode; they must
- * run in this order on one stream with the same workspace.
- *   prepare: rotate and pre-scale the queries into the workspace
- *   split:   stream the packed cache, write per-split partials to the workspace
- *   merge:   combine the partials, apply the inverse transform, write `out`
- */
-kvq_status kvq_attn_prepare(const kvq_layer_desc* desc, const void* q, kvq_dtype q_dtype,
-                            uint32_t num_q_heads, uint32_t seq_len, float softmax_scale,
-                            void* workspace, size_t workspace_bytes, void* hip_stream);
-kvq_status kvq_attn_split(const kvq_layer_desc* desc, const void* cache,
-                          uint32_t num_q_heads, uint32_t seq_len, void* workspace,
-                          size_t workspace_bytes, void* hip_stream);
-kvq_status kvq_attn_merge(const kvq_layer_desc* desc, uint32_t num_q_heads, uint32_t seq_len,
-                          void* out, kvq_dtype out_dtype, void* workspace,
-                          size_t workspace_bytes, void* hip_stream);
-
-/* Number of sequence splits kvq_attn_split uses for this shape (host only; 0 if the
- * arguments are invalid). Each split covers a whole number of 64-token tiles. */
+/* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
+ * this shape (host only; 0 if the arguments are invalid). Each split covers a whole
+ * number of 64-token tiles. */
 uint32_t kvq_attn_num_splits(const kvq_layer_desc* desc, uint32_t num_q_heads,
                              uint32_t seq_len);
 

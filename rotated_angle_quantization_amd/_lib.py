@@ -65,9 +65,6 @@ _SIGS = {
     "kvq_attn_num_splits": (_u32, [_P, _u32, _u32]),
     "kvq_attn_decode": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
                                        ctypes.c_int, _v, _sz, _v]),
-    "kvq_attn_prepare": (ctypes.c_int, [_P, _v, ctypes.c_int, _u32, _u32, _f32, _v, _sz, _v]),
-    "kvq_attn_split": (ctypes.c_int, [_P, _v, _u32, _u32, _v, _sz, _v]),
-    "kvq_attn_merge": (ctypes.c_int, [_P, _u32, _u32, _v, ctypes.c_int, _v, _sz, _v]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -162,10 +159,12 @@ def attn_num_splits(desc: LayerDesc, num_q_heads: int, seq_len: int) -> int:
 
 
 def alloc_workspace(desc: LayerDesc, num_q_heads: int, seq_len: int, device="cuda"):
+    """Zero-filled attention workspace (the library keeps its split counters at zero
+    between calls, so it can be reused for any later call that fits)."""
     n = attn_workspace_bytes(desc, num_q_heads, seq_len)
     if n == 0:
         raise KvqError(1, "kvq_attn_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
@@ -184,24 +183,6 @@ def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: 
                                out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
                                workspace.numel(), _stream(q.device)), "kvq_attn_decode")
     return out
-
-
-def attn_prepare(desc, q, seq_len, workspace, softmax_scale=0.0):
-    _check(lib.kvq_attn_prepare(ctypes.byref(desc), q.data_ptr(), _dtype_code(q), q.shape[1],
-                                seq_len, float(softmax_scale), workspace.data_ptr(),
-                                workspace.numel(), _stream(q.device)), "kvq_attn_prepare")
-
-
-def attn_split(desc, cache, num_q_heads, seq_len, workspace):
-    _check(lib.kvq_attn_split(ctypes.byref(desc), cache.data_ptr(), num_q_heads, seq_len,
-                              workspace.data_ptr(), workspace.numel(),
-                              _stream(cache.device)), "kvq_attn_split")
-
-
-def attn_merge(desc, num_q_heads, seq_len, out, workspace):
-    _check(lib.kvq_attn_merge(ctypes.byref(desc), num_q_heads, seq_len, out.data_ptr(),
-                              _dtype_code(out), workspace.data_ptr(), workspace.numel(),
-                              _stream(out.device)), "kvq_attn_merge")
 
 
 def default_scale(d: int) -> float:

@@ -78,10 +78,9 @@ bool use_key_table(const kvq_layer_desc* d, uint32_t hq) {
   return key_table_bytes((int)d->head_dim, g, code_bits(d->n_bins_k)) <= kKeyTableMaxBytes;
 }
 
-// Sequence split for decode attention. Workgroups have 8 waves that each stream whole
-// tiles; aim for one workgroup per compute unit when the key table fills the LDS
-// (256 workgroups), two otherwise, with at least 8 tiles (one per wave) per split and
-// no empty split.
+// Sequence split for decode attention. Each wave of a workgroup streams whole tiles; aim
+// for one workgroup per compute unit when the key table fills the LDS (256 workgroups),
+// two otherwise, with at least 8 tiles per split and no empty split.
 void split_plan(uint32_t units, uint32_t seq_len, bool key_table, int* nsplit,
                 int* tiles_per_split) {
   const int ntiles = (int)((seq_len + kTile - 1) / kTile);
@@ -99,13 +98,17 @@ void split_plan(uint32_t units, uint32_t seq_len, bool key_table, int* nsplit,
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct AttnLayout {
-  size_t qrot, ml, acc, total;
+  size_t tickets, qrot, ml, acc, total;
 };
 
+// Workspace: split tickets (must read zero before a call; every call leaves them zero),
+// the rotated queries, then the per-split partial results.
 AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit) {
   AttnLayout l;
+  const size_t units = (size_t)d->batch * d->num_kv_heads;
   const size_t bh = (size_t)d->batch * hq;
-  l.qrot = 0;
+  l.tickets = 0;
+  l.qrot = align256(units * sizeof(unsigned));
   l.ml = align256(l.qrot + bh * d->head_dim * sizeof(float));
   l.acc = align256(l.ml + bh * (size_t)nsplit * 2 * sizeof(float));
   l.total = align256(l.acc + bh * (size_t)nsplit * d->head_dim * sizeof(float));
@@ -154,6 +157,7 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
   a->sign = sign_mask(d->seed, d->layer, d->head_dim);
   char* base = (char*)workspace;
+  a->tickets = (unsigned*)(base + l.tickets);
   a->qrot = (float*)(base + l.qrot);
   a->part_ml = (float*)(base + l.ml);
   a->part_acc = (float*)(base + l.acc);
@@ -245,44 +249,10 @@ size_t kvq_attn_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t s
   return attn_layout(d, hq, (int)s).total;
 }
 
-kvq_status kvq_attn_prepare(const kvq_layer_desc* d, const void* q, kvq_dtype q_dtype,
-                            uint32_t hq, uint32_t seq_len, float scale, void* ws,
-                            size_t ws_bytes, void* stream) {
-  AttnArgs a;
-  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
-  if (st != KVQ_OK) return st;
-  if (!q || (q_dtype != KVQ_F16 && q_dtype != KVQ_F32)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  return hip_status(
-      launch_attn_prepare(a, (int)d->head_dim, q, q_dtype == KVQ_F32, (hipStream_t)stream));
-}
-
-kvq_status kvq_attn_split(const kvq_layer_desc* d, const void* cache, uint32_t hq,
-                          uint32_t seq_len, void* ws, size_t ws_bytes, void* stream) {
-  AttnArgs a;
-  kvq_status st = attn_args(d, hq, seq_len, 0.0f, ws, ws_bytes, &a);
-  if (st != KVQ_OK) return st;
-  if (!cache) return KVQ_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_attn_split(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
-                                      (hipStream_t)stream));
-}
-
-kvq_status kvq_attn_merge(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, void* out,
-                          kvq_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
-  AttnArgs a;
-  kvq_status st = attn_args(d, hq, seq_len, 0.0f, ws, ws_bytes, &a);
-  if (st != KVQ_OK) return st;
-  if (!out || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  return hip_status(
-      launch_attn_merge(a, (int)d->head_dim, out, out_dtype == KVQ_F32, (hipStream_t)stream));
-}
-
 kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const void* q,
                            kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, float scale,
                            void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
                            void* stream) {
-  // Validate everything before the first launch so a rejected call enqueues nothing.
   AttnArgs a;
   kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
   if (st != KVQ_OK) return st;
@@ -291,12 +261,12 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const voi
     return KVQ_ERR_INVALID_ARGUMENT;
   if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
   if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  const int dim = (int)d->head_dim;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_attn_prepare(a, dim, q, q_dtype == KVQ_F32, s);
-  if (e == hipSuccess) e = launch_attn_split(a, dim, geom_of(d), (const uint8_t*)cache, s);
-  if (e == hipSuccess) e = launch_attn_merge(a, dim, out, out_dtype == KVQ_F32, s);
-  return hip_status(e);
+  a.q = q;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.out = out;
+  a.out_f32 = out_dtype == KVQ_F32;
+  return hip_status(
+      launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
 }
 
 }  // extern "C"

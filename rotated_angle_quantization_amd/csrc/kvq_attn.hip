@@ -119,23 +119,19 @@ struct Geo {
   static constexpr int BYTES = OFF_VP + 4 * kTile;
 };
 
-// ---------------------------------------------------------------------------- prepare
-
+// Rotated query of one head: lane p < D/2 returns elements 2p, 2p+1 of
+// q~ = H diag(sign) q / sqrt(d), times the softmax scale * log2(e) / 255.
 template <int D>
-__global__ __launch_bounds__(64) void attn_prepare_kernel(AttnArgs a, const void* __restrict__ q,
-                                                          int f32_q) {
+__device__ __forceinline__ float2 rotate_query(const AttnArgs& a, size_t qoff, int lane) {
   constexpr int P = D / 2;
-  const int bh = blockIdx.x;
-  const int lane = threadIdx.x;
-  if (lane >= P) return;
   const int e0 = 2 * lane;
   float x0, x1;
-  if (f32_q) {
-    const float2 v = reinterpret_cast<const float2*>(q)[((size_t)bh * D + e0) >> 1];
+  if (a.q_f32) {
+    const float2 v = reinterpret_cast<const float2*>(a.q)[(qoff + e0) >> 1];
     x0 = v.x;
     x1 = v.y;
   } else {
-    const __half2 v = reinterpret_cast<const __half2*>(q)[((size_t)bh * D + e0) >> 1];
+    const __half2 v = reinterpret_cast<const __half2*>(a.q)[(qoff + e0) >> 1];
     x0 = __half2float(__low2half(v));
     x1 = __half2float(__high2half(v));
   }
@@ -143,7 +139,39 @@ __global__ __launch_bounds__(64) void attn_prepare_kernel(AttnArgs a, const void
   if (sign_neg(a.sign, e0 + 1)) x1 = -x1;
   fwht_pairs_f32<P>(x0, x1, lane);
   const float sc = a.inv_sqrt_d * a.q_scale;
-  reinterpret_cast<float2*>(a.qrot)[((size_t)bh * D + e0) >> 1] = make_float2(x0 * sc, x1 * sc);
+  return make_float2(x0 * sc, x1 * sc);
+}
+
+// Output of one head from its rotated-domain sum: lane p < D/2 holds elements 2p, 2p+1
+// of acc / l; o = sign * H (acc / l) / sqrt(d).
+template <int D>
+__device__ __forceinline__ void store_output(const AttnArgs& a, size_t ooff, int lane, float a0,
+                                             float a1) {
+  constexpr int P = D / 2;
+  fwht_pairs_f32<P>(a0, a1, lane);
+  const int e0 = 2 * lane;
+  a0 *= a.inv_sqrt_d;
+  a1 *= a.inv_sqrt_d;
+  if (sign_neg(a.sign, e0)) a0 = -a0;
+  if (sign_neg(a.sign, e0 + 1)) a1 = -a1;
+  if (a.out_f32)
+    reinterpret_cast<float2*>(a.out)[(ooff + e0) >> 1] = make_float2(a0, a1);
+  else
+    reinterpret_cast<__half2*>(a.out)[(ooff + e0) >> 1] = __floats2half2_rn(a0, a1);
+}
+
+// ---------------------------------------------------------------------------- prepare
+
+// Rotated queries into the workspace, for the kernels without a key table (their
+// scores read q~ through scalar loads, which must not see data written by the same
+// launch). One wave per (batch, query head).
+template <int D>
+__global__ __launch_bounds__(64) void attn_prepare_kernel(AttnArgs a) {
+  constexpr int P = D / 2;
+  const int lane = threadIdx.x;
+  if (lane >= P) return;
+  const size_t off = (size_t)blockIdx.x * D;
+  reinterpret_cast<float2*>(a.qrot)[off / 2 + lane] = rotate_query<D>(a, off, lane);
 }
 
 // ---------------------------------------------------------------------------- split
@@ -271,11 +299,12 @@ __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
 // four heads per kv head, which leaves the kernel under 168 VGPRs; otherwise 8.
 constexpr int split_waves(bool key_table, int group) { return key_table && group <= 4 ? 12 : 8; }
 
-// KT: scores read a per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) +
-// q~_h,2i+1 sin(2 pi c / n) from LDS, one FMA per (pair, head); otherwise scores
-// use the cos/sin table and the rotated query from scalar registers.
+// One workgroup per (split, batch * kv head). KT: scores read a per-workgroup table
+// T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n) from LDS, one FMA per
+// (pair, head); otherwise scores use the cos/sin table and the rotated query from
+// scalar registers.
 template <int D, int G, int BK, int BV, bool KT>
-__global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
+__global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot) {
   using C = SplitCfg<D, G, BK, BV>;
   using GE = typename C::GE;
@@ -283,17 +312,23 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
   constexpr int UNION_BYTES = (KT && C::TAB_BYTES > MERGE_BYTES) ? C::TAB_BYTES : MERGE_BYTES;
   // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
-  // instruction's immediate offset; the key table (or the merge buffers) above them
-  constexpr int LUTK_OFF = 0, LUTV_OFF = NKT * 8, UNION_OFF = LUTV_OFF + (1 << BV) * 8;
+  // instruction's immediate offset; then the rotated query (later the normalised
+  // output), a flag, and the key table (or the merge buffers)
+  constexpr int LUTK_OFF = 0, LUTV_OFF = NKT * 8, Q_OFF = LUTV_OFF + (1 << BV) * 8;
+  constexpr int FLAG_OFF = Q_OFF + G * D * 4, UNION_OFF = FLAG_OFF + 16;
   __shared__ __align__(16) char smem[UNION_OFF + UNION_BYTES];
   float2* lut_k = reinterpret_cast<float2*>(smem + LUTK_OFF);
   float2* lut_v = reinterpret_cast<float2*>(smem + LUTV_OFF);
+  float* s_q = reinterpret_cast<float*>(smem + Q_OFF);  // [G][D]
+  int* s_flag = reinterpret_cast<int*>(smem + FLAG_OFF);
   char* s_union = smem + UNION_OFF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
+  // rotated query in the workspace, written by the prepare kernel (only launched when
+  // there is no key table: then the scores read it through scalar loads)
   const float* qg = qrot + (size_t)bk * G * D;
 
   // The first tile's key loads go out before the tables are built, so their latency
@@ -304,6 +339,11 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
   TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
   if (tile < tile_end) load_tile_keys(cur, base + (size_t)tile * GE::BYTES, lane);
+
+  // Rotated query for the key table: wave g < G rotates head kv_head * G + g (query
+  // heads of one kv head are consecutive, so its row is bk * G + g).
+  if (KT && wave < G && lane < P)
+    reinterpret_cast<float2*>(s_q)[wave * P + lane] = rotate_query<D>(a, ((size_t)bk * G + wave) * D, lane);
 
   // cos/sin of the bin centres 2 pi c / n; rows past n are only ever read for slots
   // past the sequence end and are zeroed
@@ -326,8 +366,8 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
     float qa[G], qb[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      qa[g] = qg[g * D + 2 * i];
-      qb[g] = qg[g * D + 2 * i + 1];
+      qa[g] = s_q[g * D + 2 * i];
+      qb[g] = s_q[g * D + 2 * i + 1];
     }
     for (int c = c0; c < NKT; c += TPP) {
       const float2 cs = lut_k[c];
@@ -350,11 +390,8 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
 
   const int vshift = (row * kStepTokens * BV) & 31;  // 0, or 16 for odd widths
 
-  // Online softmax state per head: m = running reference (base-2 log units), l = per-lane
-  // partial sums of p (reduced once at the end). The reference is only raised when a
-  // score exceeds it by more than kLazy, so p <= 2^kLazy and most tiles skip the
-  // wave-wide max and the rescale.
-  constexpr float kLazy = 8.0f;
+  // Online softmax state per head: m = running maximum (base-2 log units, uniform
+  // across the wave), l = per-lane partial sums of p (reduced once at the end).
   float m[G], l[G];
   float2 acc[G][PPL];
 #pragma unroll
@@ -553,6 +590,7 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
     }
   }
   __syncthreads();
+  const bool single = a.nsplit == 1;
   for (int idx = tid; idx < G * D; idx += NW * 64) {
     const int g = idx / D, e = idx % D;
     float mm = s_ml[g * 2];
@@ -565,151 +603,148 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_split_kernel(
       ll += s_ml[(w * G + g) * 2 + 1] * f;
       aa += s_acc[(w * G + g) * D + e] * f;
     }
-    const size_t rowi = ((size_t)bk * G + g) * a.nsplit + split;
-    a.part_acc[rowi * D + e] = aa;
-    if (e == 0) {
-      a.part_ml[2 * rowi] = mm;
-      a.part_ml[2 * rowi + 1] = ll;
+    if (single) {
+      s_q[idx] = aa / ll;
+    } else {
+      // device-coherent stores (they bypass the non-coherent caches, so no cache
+      // write-back is needed before another workgroup reads them)
+      const size_t rowi = ((size_t)bk * G + g) * a.nsplit + split;
+      __hip_atomic_store(a.part_acc + rowi * D + e, aa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (e == 0) {
+        __hip_atomic_store(a.part_ml + 2 * rowi, mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.part_ml + 2 * rowi + 1, ll, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
-}
-
-// ---------------------------------------------------------------------------- merge
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, void* __restrict__ out,
-                                                         int f32_out) {
-  constexpr int P = D / 2;
-  __shared__ float s_red[4];
-  __shared__ float2 s_acc[4][P];
-  __shared__ float s_l[4];
-  const int bh = blockIdx.x;  // b * hq + h
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* ml = a.part_ml + (size_t)bh * a.nsplit * 2;
-  const float* acc = a.part_acc + (size_t)bh * a.nsplit * D;
-  // global max over the splits
-  float mloc = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
-  mloc = wave_max(mloc);
-  if (lane == 0) s_red[wave] = mloc;
-  __syncthreads();
-  const float mm = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  // wave w sums splits w, w + 4, ...; lane p owns pair p (two output elements)
-  float a0 = 0.f, a1 = 0.f, ll = 0.f;
-  if (lane < P) {
-    for (int s = wave; s < a.nsplit; s += 4) {
-      const float f = fast_exp2(ml[2 * s] - mm);
-      const float2 v = reinterpret_cast<const float2*>(acc + (size_t)s * D)[lane];
-      a0 = fmaf(f, v.x, a0);
-      a1 = fmaf(f, v.y, a1);
-      ll = fmaf(f, ml[2 * s + 1], ll);
+  if (single) {
+    __syncthreads();
+    if (wave < G && lane < P) {
+      const float2 v = reinterpret_cast<const float2*>(s_q)[wave * P + lane];
+      store_output<D>(a, ((size_t)bk * G + wave) * D, lane, v.x, v.y);
     }
-    s_acc[wave][lane] = make_float2(a0, a1);
+    return;
   }
-  if (lane == 0) s_l[wave] = ll;
+
+  // ---- cross-split merge by the last workgroup of this (batch, kv head) to finish:
+  // once its partial results are complete in memory it takes a ticket; the holder of
+  // the last ticket combines the splits (log-sum-exp), applies the inverse transform
+  // and resets the counter. The partials are written and read with device-coherent
+  // accesses, so completion of the stores (waitcnt) is all the ordering needed, and no
+  // agent-wide cache write-back or invalidate is issued.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (wave != 0 || lane >= P) return;
-  float2 t = s_acc[0][lane];
+  if (tid == 0) {
+    // system scope: the counter update is performed at the memory side, so workgroups
+    // on different XCDs (each with its own L2) count on one copy
+    const unsigned t = __hip_atomic_fetch_add(a.tickets + bk, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
+    *s_flag = t == (unsigned)(a.nsplit - 1);
+  }
+  __syncthreads();
+  if (!*s_flag) return;
+  // thread (g, e) folds element e of head g over the splits with a running
+  // log-sum-exp, eight splits' loads in flight at a time
+  auto ld = [](const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
+    const int g = idx / D, e = idx % D;
+    const size_t row0 = ((size_t)bk * G + g) * a.nsplit;
+    const float* ml = a.part_ml + 2 * row0;
+    const float* pa = a.part_acc + row0 * D + e;
+    float mm = -INFINITY, ll = 0.f, aa = 0.f;
+    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+      float mv[8], lv[8], av[8];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    t.x += s_acc[w][lane].x;
-    t.y += s_acc[w][lane].y;
+      for (int u = 0; u < 8; ++u) {
+        const int sp = min(s0 + u, a.nsplit - 1);
+        mv[u] = ld(ml + 2 * sp);
+        lv[u] = ld(ml + 2 * sp + 1);
+        av[u] = ld(pa + (size_t)sp * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < a.nsplit) {  // every split covers a valid token, so m is finite
+          const float mnew = fmaxf(mm, mv[u]);
+          const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv[u] - mnew);
+          ll = ll * c0 + lv[u] * c1;
+          aa = aa * c0 + av[u] * c1;
+          mm = mnew;
+        }
+      }
+    }
+    s_q[idx] = aa / ll;
   }
-  const float inv_l = 1.0f / ((s_l[0] + s_l[1]) + (s_l[2] + s_l[3]));
-  a0 = t.x * inv_l;
-  a1 = t.y * inv_l;
-  fwht_pairs_f32<P>(a0, a1, lane);
-  const int e0 = 2 * lane;
-  a0 *= a.inv_sqrt_d;
-  a1 *= a.inv_sqrt_d;
-  if (sign_neg(a.sign, e0)) a0 = -a0;
-  if (sign_neg(a.sign, e0 + 1)) a1 = -a1;
-  const size_t off = (size_t)bh * D + e0;
-  if (f32_out)
-    reinterpret_cast<float2*>(out)[off >> 1] = make_float2(a0, a1);
-  else
-    reinterpret_cast<__half2*>(out)[off >> 1] = __floats2half2_rn(a0, a1);
+  __syncthreads();
+  if (wave < G && lane < P) {
+    const float2 v = reinterpret_cast<const float2*>(s_q)[wave * P + lane];
+    store_output<D>(a, ((size_t)bk * G + wave) * D, lane, v.x, v.y);
+  }
+  if (tid == 0) __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 template <int D, int G, int BK, int BV>
-hipError_t split_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   if constexpr (SplitCfg<D, G, BK, BV>::TAB_BYTES <= kKeyTableMaxBytes) {
     if (a.key_table) {
-      hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, true>), grid, dim3(split_waves(true, G) * 64), 0, s, a,
-                         cache, a.qrot);
+      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, true>), grid,
+                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
       return hipGetLastError();
     }
   }
   if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
-  hipLaunchKernelGGL((attn_split_kernel<D, G, BK, BV, false>), grid, dim3(split_waves(false, G) * 64), 0, s, a, cache,
-                     a.qrot);
+  hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, false>), grid,
+                     dim3(split_waves(false, G) * 64), 0, s, a, cache, a.qrot);
   return hipGetLastError();
 }
 
 template <int D, int G, int BK>
-hipError_t split_bv(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_bv(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   switch (a.bv) {
-    case 6: return split_launch<D, G, BK, 6>(a, cache, grid, s);
-    case 7: return split_launch<D, G, BK, 7>(a, cache, grid, s);
-    case 8: return split_launch<D, G, BK, 8>(a, cache, grid, s);
+    case 6: return decode_launch<D, G, BK, 6>(a, cache, grid, s);
+    case 7: return decode_launch<D, G, BK, 7>(a, cache, grid, s);
+    case 8: return decode_launch<D, G, BK, 8>(a, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D, int G>
-hipError_t split_bk(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_bk(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   switch (a.bk) {
-    case 6: return split_bv<D, G, 6>(a, cache, grid, s);
-    case 7: return split_bv<D, G, 7>(a, cache, grid, s);
-    case 8: return split_bv<D, G, 8>(a, cache, grid, s);
+    case 6: return decode_bv<D, G, 6>(a, cache, grid, s);
+    case 7: return decode_bv<D, G, 7>(a, cache, grid, s);
+    case 8: return decode_bv<D, G, 8>(a, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t split_g(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_g(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
   switch (a.group) {
-    case 1: return split_bk<D, 1>(a, cache, grid, s);
-    case 2: return split_bk<D, 2>(a, cache, grid, s);
-    case 4: return split_bk<D, 4>(a, cache, grid, s);
-    case 8: return split_bk<D, 8>(a, cache, grid, s);
+    case 1: return decode_bk<D, 1>(a, cache, grid, s);
+    case 2: return decode_bk<D, 2>(a, cache, grid, s);
+    case 4: return decode_bk<D, 4>(a, cache, grid, s);
+    case 8: return decode_bk<D, 8>(a, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_prepare(const AttnArgs& a, int d, const void* q, bool f32_q,
-                               hipStream_t stream) {
-  const dim3 grid((unsigned)(a.batch * a.hq)), block(64);
-  if (d == 64)
-    hipLaunchKernelGGL(attn_prepare_kernel<64>, grid, block, 0, stream, a, q, (int)f32_q);
-  else if (d == 128)
-    hipLaunchKernelGGL(attn_prepare_kernel<128>, grid, block, 0, stream, a, q, (int)f32_q);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_split(const AttnArgs& a, int d, TileGeom geom, const uint8_t* cache,
-                             hipStream_t stream) {
-  (void)geom;
+hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache,
+                              hipStream_t stream) {
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  if (!a.key_table) {
+    const dim3 pgrid((unsigned)(a.batch * a.hq));
+    if (d == 64)
+      hipLaunchKernelGGL(attn_prepare_kernel<64>, pgrid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_prepare_kernel<128>, pgrid, dim3(64), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv));
-  if (d == 64) return split_g<64>(a, cache, grid, stream);
-  if (d == 128) return split_g<128>(a, cache, grid, stream);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_attn_merge(const AttnArgs& a, int d, void* out, bool f32_out,
-                             hipStream_t stream) {
-  const dim3 grid((unsigned)(a.batch * a.hq)), block(256);
-  if (d == 64)
-    hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, 0, stream, a, out, (int)f32_out);
-  else if (d == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, 0, stream, a, out, (int)f32_out);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return d == 64 ? decode_g<64>(a, cache, grid, stream) : decode_g<128>(a, cache, grid, stream);
 }
 
 }  // namespace kvq

@@ -76,24 +76,23 @@ struct AttnArgs {
   int seq_len, tiles_per_seq, ntiles, nsplit, tiles_per_split;
   int n_k, n_v, bk, bv;
   int key_table;       // 1: scores read a per-workgroup query table in LDS
+  int q_f32, out_f32;  // element types of q and out (else fp16)
   float q_scale;       // softmax scale * log2(e) / 255, folded into the rotated query
   float inv_sqrt_d;    // fp32 1/sqrt(d)
   SignMask sign;
-  float* qrot;         // [B, Hq, d]
+  const void* q;       // [B, Hq, d]
+  void* out;           // [B, Hq, d]
+  unsigned* tickets;   // [B * Hkv] split counters; zero between calls
+  float* qrot;         // [B, Hq, d] rotated queries (kernels without the key table)
   float* part_ml;      // [B, Hq, nsplit, 2]
   float* part_acc;     // [B, Hq, nsplit, d]
 };
 
 // Bytes of the per-workgroup key-score table (pairs x 2^bk codes x heads x fp32) and
-// the largest table the split kernel keeps in LDS.
+// the largest table the decode kernel keeps in LDS.
 constexpr int kKeyTableMaxBytes = 128 * 1024;
 inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (1L << bk) * group * 4; }
 
-hipError_t launch_attn_prepare(const AttnArgs& a, int d, const void* q, bool f32_q,
-                               hipStream_t stream);
-hipError_t launch_attn_split(const AttnArgs& a, int d, TileGeom geom, const uint8_t* cache,
-                             hipStream_t stream);
-hipError_t launch_attn_merge(const AttnArgs& a, int d, void* out, bool f32_out,
-                             hipStream_t stream);
+hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache, hipStream_t stream);
 
 }  // namespace kvq

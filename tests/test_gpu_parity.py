@@ -280,25 +280,37 @@ def test_deterministic_across_runs_and_seeds(dev):
     assert torch.equal(o1, o2)
 
 
-def test_attention_phases_match_single_call(dev):
+def test_attention_workspace_reuse_and_explicit_scale(dev):
+    """One zero-filled workspace serves a sequence of calls of different shapes and
+    split counts: results equal those with fresh workspaces, and the split counters at
+    its start are back at zero afterwards."""
     cfg = get("mistral7b")
-    k, v = layer_kv(cfg, 9, dev, seq=640, batch=1)
-    q = query(cfg, 9, dev, batch=1)
-    desc = kvq.make_desc(128, cfg.hkv, 1, 640, 128, 64, 9, 0)
+    k, v = layer_kv(cfg, 9, dev, seq=2048, batch=2)
+    q = query(cfg, 9, dev, batch=2)
+    desc = kvq.make_desc(128, cfg.hkv, 2, 2048, 128, 64, 9, 0)
     cache = kvq.alloc_cache(desc, dev)
     kvq.encode(desc, cache, k, v, 0)
-    ws = kvq.alloc_workspace(desc, cfg.hq, 600, dev)
-    whole = kvq.attn_decode(desc, cache, q, 600, softmax_scale=0.05, workspace=ws)
-    out = torch.empty_like(whole)
-    kvq.attn_prepare(desc, q, 600, ws, softmax_scale=0.05)
-    kvq.attn_split(desc, cache, cfg.hq, 600, ws)
-    kvq.attn_merge(desc, cfg.hq, 600, out, ws)
+    lens = [2048, 600, 64, 1500, 2048]
+    assert len({kvq.attn_num_splits(desc, cfg.hq, n) for n in lens}) >= 3
+    fresh = [kvq.attn_decode(desc, cache, q, n, workspace=kvq.alloc_workspace(desc, cfg.hq, n, dev))
+             for n in lens]
+    ws = kvq.alloc_workspace(desc, cfg.hq, 2048, dev)
+    for _ in range(2):
+        for n, ref in zip(lens, fresh):
+            got = kvq.attn_decode(desc, cache, q, n, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), n
+    assert int(ws[: 4 * 2 * cfg.hkv].count_nonzero()) == 0
+    desc1 = kvq.make_desc(128, cfg.hkv, 1, 640, 128, 64, 9, 0)
+    cache1 = kvq.alloc_cache(desc1, dev)
+    kvq.encode(desc1, cache1, k[:1, :640].contiguous(), v[:1, :640].contiguous(), 0)
+    q1 = q[:1].contiguous()
+    out = kvq.attn_decode(desc1, cache1, q1, 600, softmax_scale=0.05, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(whole, out)
     # an explicit softmax scale is honoured
     sg = oc.layer_signs(0, 9, 128)
-    got = unpack(cache.cpu().numpy(), 128, 128, 64, 1, cfg.hkv, 640, 0, 600)
+    got = unpack(cache1.cpu().numpy(), 128, 128, 64, 1, cfg.hkv, 640, 0, 600)
     kh, vh = oracle_dequant(got, sg, 128, 64)
-    ref = oc.attention(np64(q), kh, vh, scale=0.05)
+    ref = oc.attention(np64(q1), kh, vh, scale=0.05)
     compare_attention(np64(out), ref, "scale 0.05")
     assert math.isclose(kvq.default_scale(128), 128 ** -0.5)
