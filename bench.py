@@ -57,11 +57,13 @@ def copy_calibration(mib):
 
 
 def attn_kernel_name(d, group, n_k, n_v):
-    """Name of the attention-kernel instantiation the library launches for this shape
-    (the key-score table is used when P * 2^bk * G * 4 bytes fit in 128 KiB of LDS)."""
+    """Name of the attention-kernel instantiation the library launches for this shape:
+    key-table mode 1 when the P * 2^bk * G * 4-byte score table fits in 128 KiB of LDS,
+    2 (half table) when half of it fits and n_k is a power of two, else 0."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
-    kt = (d // 2) * (1 << bk) * group * 4 <= 128 * 1024
-    return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {'true' if kt else 'false'}>"
+    full = (d // 2) * (1 << bk) * group * 4
+    mode = 1 if full <= 128 * 1024 else (2 if n_k == 1 << bk and full // 2 <= 128 * 1024 else 0)
+    return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {mode}>"
 
 
 def attn_traffic(cfg):

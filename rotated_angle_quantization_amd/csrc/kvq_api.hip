@@ -73,9 +73,15 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
 }
 
 // Whether decode attention uses the LDS key-score table for this shape.
-bool use_key_table(const kvq_layer_desc* d, uint32_t hq) {
+// Key-table mode of the decode kernel: 1 = full score table in LDS, 2 = half table
+// (n a power of two; rows c >= n/2 are the negated rows c - n/2), 0 = no table.
+int key_table_mode(const kvq_layer_desc* d, uint32_t hq) {
   const int g = (int)(hq / d->num_kv_heads);
-  return key_table_bytes((int)d->head_dim, g, code_bits(d->n_bins_k)) <= kKeyTableMaxBytes;
+  const int bk = code_bits(d->n_bins_k);
+  const long bytes = key_table_bytes((int)d->head_dim, g, bk);
+  if (bytes <= kKeyTableMaxBytes) return 1;
+  if (d->n_bins_k == (1u << bk) && bytes / 2 <= kKeyTableMaxBytes) return 2;
+  return 0;
 }
 
 // Sequence split for decode attention. Each wave of a workgroup streams whole tiles; aim
@@ -133,8 +139,8 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   kvq_status st = attn_check(d, hq, seq_len);
   if (st != KVQ_OK) return st;
   int nsplit, tps;
-  const bool kt = use_key_table(d, hq);
-  split_plan(d->batch * d->num_kv_heads, seq_len, kt, &nsplit, &tps);
+  const int ktm = key_table_mode(d, hq);
+  split_plan(d->batch * d->num_kv_heads, seq_len, ktm != 0, &nsplit, &tps);
   const AttnLayout l = attn_layout(d, hq, nsplit);
   if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < l.total)
     return KVQ_ERR_WORKSPACE;
@@ -151,7 +157,7 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->n_v = (int)d->n_bins_v;
   a->bk = code_bits(d->n_bins_k);
   a->bv = code_bits(d->n_bins_v);
-  a->key_table = kt ? 1 : 0;
+  a->key_table = ktm;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
   a->q_scale = (float)(sc * 1.4426950408889634 / 255.0);
   a->inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
@@ -239,7 +245,7 @@ uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_
   if (!desc_ok(d) || hq == 0 || hq % d->num_kv_heads || seq_len == 0 || seq_len > d->capacity)
     return 0;
   int nsplit, tps;
-  split_plan(d->batch * d->num_kv_heads, seq_len, use_key_table(d, hq), &nsplit, &tps);
+  split_plan(d->batch * d->num_kv_heads, seq_len, key_table_mode(d, hq) != 0, &nsplit, &tps);
   return (uint32_t)nsplit;
 }
 

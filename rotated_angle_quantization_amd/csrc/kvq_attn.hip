@@ -299,18 +299,23 @@ __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
 // four heads per kv head, which leaves the kernel under 168 VGPRs; otherwise 8.
 constexpr int split_waves(bool key_table, int group) { return key_table && group <= 4 ? 12 : 8; }
 
-// One workgroup per (split, batch * kv head). KT: scores read a per-workgroup table
-// T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n) from LDS, one FMA per
-// (pair, head); otherwise scores use the cos/sin table and the rotated query from
-// scalar registers.
-template <int D, int G, int BK, int BV, bool KT>
-__global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
+// One workgroup per (split, batch * kv head). KTM (key-table mode) 1: scores read a
+// per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n)
+// from LDS, one FMA per (pair, head). KTM 2 (n a power of two whose full table would
+// not fit): only rows c < n/2 are stored and T[i][c + n/2] = -T[i][c] (the angle plus
+// pi), the top code bit flipping the sign of the radius. KTM 0: scores use the cos/sin
+// table and the rotated query from scalar registers.
+template <int D, int G, int BK, int BV, int KTM>
+__global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot) {
   using C = SplitCfg<D, G, BK, BV>;
   using GE = typename C::GE;
+  constexpr bool KT = KTM != 0, HALF = KTM == 2;
   constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KT, G);
+  constexpr int NTAB = HALF ? NKT / 2 : NKT;  // table rows per pair
+  constexpr int TAB_BYTES = P * NTAB * G * 4;
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
-  constexpr int UNION_BYTES = (KT && C::TAB_BYTES > MERGE_BYTES) ? C::TAB_BYTES : MERGE_BYTES;
+  constexpr int UNION_BYTES = (KT && TAB_BYTES > MERGE_BYTES) ? TAB_BYTES : MERGE_BYTES;
   // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
   // instruction's immediate offset; then the rotated query (later the normalised
   // output), a flag, and the key table (or the merge buffers)
@@ -369,12 +374,12 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
       qa[g] = s_q[g * D + 2 * i];
       qb[g] = s_q[g * D + 2 * i + 1];
     }
-    for (int c = c0; c < NKT; c += TPP) {
+    for (int c = c0; c < NTAB; c += TPP) {
       const float2 cs = lut_k[c];
       float tv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) tv[g] = fmaf(qa[g], cs.x, qb[g] * cs.y);
-      float* dst = ktab + (i * NKT + c) * G;
+      float* dst = ktab + (i * NTAB + c) * G;
 #pragma unroll
       for (int g = 0; g < G; g += (G >= 4 ? 4 : G)) {
         if (G >= 4)
@@ -421,6 +426,7 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
       // (the scheduling fences keep the compiler from re-serialising them).
       constexpr int KB = 4, NKB = P / KB;
       float tb[2][KB][G];
+      uint32_t sg[2][KB];  // half table: sign bit of the radius (top code bit at bit 31)
 #pragma unroll
       for (int blk = 0; blk <= NKB; ++blk) {
         if (blk < NKB) {
@@ -428,7 +434,8 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
           for (int ii = 0; ii < KB; ++ii) {
             const int i = blk * KB + ii;
             const uint32_t c = field<BK>(cur.ka, i);
-            load_row<G>(tb[blk & 1][ii], ktab + (i * NKT + c) * G);
+            sg[blk & 1][ii] = HALF ? (c >> (BK - 1)) << 31 : 0u;
+            load_row<G>(tb[blk & 1][ii], ktab + (i * NTAB + (c & (NTAB - 1))) * G);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -436,7 +443,8 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
 #pragma unroll
           for (int ii = 0; ii < KB; ++ii) {
             const int i = (blk - 1) * KB + ii;
-            const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+            float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+            if (HALF) rho = __uint_as_float(__float_as_uint(rho) ^ sg[(blk - 1) & 1][ii]);
 #pragma unroll
             for (int g = 0; g < G; ++g) sc[g] = fmaf(rho, tb[(blk - 1) & 1][ii][g], sc[g]);
           }
@@ -685,15 +693,22 @@ __global__ __launch_bounds__(split_waves(KT, G) * 64) void attn_decode_kernel(
 
 template <int D, int G, int BK, int BV>
 hipError_t decode_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
-  if constexpr (SplitCfg<D, G, BK, BV>::TAB_BYTES <= kKeyTableMaxBytes) {
-    if (a.key_table) {
-      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, true>), grid,
+  constexpr long full = SplitCfg<D, G, BK, BV>::TAB_BYTES;
+  if constexpr (full <= kKeyTableMaxBytes) {
+    if (a.key_table == 1) {
+      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 1>), grid,
+                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
+      return hipGetLastError();
+    }
+  } else if constexpr (full / 2 <= kKeyTableMaxBytes) {
+    if (a.key_table == 2) {
+      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 2>), grid,
                          dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
       return hipGetLastError();
     }
   }
   if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
-  hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, false>), grid,
+  hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 0>), grid,
                      dim3(split_waves(false, G) * 64), 0, s, a, cache, a.qrot);
   return hipGetLastError();
 }

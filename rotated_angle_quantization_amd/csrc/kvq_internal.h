@@ -75,7 +75,7 @@ struct AttnArgs {
   int batch, hkv, hq, group;
   int seq_len, tiles_per_seq, ntiles, nsplit, tiles_per_split;
   int n_k, n_v, bk, bv;
-  int key_table;       // 1: scores read a per-workgroup query table in LDS
+  int key_table;       // score table in LDS: 0 none, 1 full, 2 half (sign-symmetric)
   int q_f32, out_f32;  // element types of q and out (else fp16)
   float q_scale;       // softmax scale * log2(e) / 255, folded into the rotated query
   float inv_sqrt_d;    // fp32 1/sqrt(d)
