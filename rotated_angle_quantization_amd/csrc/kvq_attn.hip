@@ -38,8 +38,11 @@
 namespace kvq {
 namespace {
 
+// Sign bit of element e < 128, selecting the word without indexing the kernel-argument
+// array by a lane-dependent value (which would turn into a per-lane memory load).
 __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
-  return (m.w[e >> 6] >> (e & 63)) & 1ull;
+  const uint64_t w = e < 64 ? m.w[0] : m.w[1];
+  return (w >> (e & 63)) & 1ull;
 }
 
 template <int P>
@@ -120,26 +123,33 @@ struct Geo {
 };
 
 // Rotated query of one head: lane p < D/2 returns elements 2p, 2p+1 of
-// q~ = H diag(sign) q / sqrt(d), times the softmax scale * log2(e) / 255.
+// q~ = H diag(sign) q / sqrt(d), times the softmax scale * log2(e) / 255. Split into the
+// load and the arithmetic so callers can issue other loads in between.
+// Raw bits of elements 2p, 2p+1: two dwords for fp32 input, one (read twice) for fp16,
+// with no branch, so the loads can stay in flight while other loads are issued.
+__device__ __forceinline__ uint2 load_query_pair(const AttnArgs& a, size_t qoff, int lane) {
+  const uint32_t* base = static_cast<const uint32_t*>(a.q);
+  const size_t w0 = a.q_f32 ? qoff + 2 * lane : (qoff >> 1) + lane;
+  const size_t w1 = a.q_f32 ? w0 + 1 : w0;
+  return make_uint2(base[w0], base[w1]);
+}
+
 template <int D>
-__device__ __forceinline__ float2 rotate_query(const AttnArgs& a, size_t qoff, int lane) {
+__device__ __forceinline__ float2 rotate_query_pair(const AttnArgs& a, uint2 raw, int lane) {
   constexpr int P = D / 2;
   const int e0 = 2 * lane;
-  float x0, x1;
-  if (a.q_f32) {
-    const float2 v = reinterpret_cast<const float2*>(a.q)[(qoff + e0) >> 1];
-    x0 = v.x;
-    x1 = v.y;
-  } else {
-    const __half2 v = reinterpret_cast<const __half2*>(a.q)[(qoff + e0) >> 1];
-    x0 = __half2float(__low2half(v));
-    x1 = __half2float(__high2half(v));
-  }
+  float x0 = a.q_f32 ? __uint_as_float(raw.x) : __half2float(__ushort_as_half((uint16_t)(raw.x & 0xFFFFu)));
+  float x1 = a.q_f32 ? __uint_as_float(raw.y) : __half2float(__ushort_as_half((uint16_t)(raw.x >> 16)));
   if (sign_neg(a.sign, e0)) x0 = -x0;
   if (sign_neg(a.sign, e0 + 1)) x1 = -x1;
   fwht_pairs_f32<P>(x0, x1, lane);
   const float sc = a.inv_sqrt_d * a.q_scale;
   return make_float2(x0 * sc, x1 * sc);
+}
+
+template <int D>
+__device__ __forceinline__ float2 rotate_query(const AttnArgs& a, size_t qoff, int lane) {
+  return rotate_query_pair<D>(a, load_query_pair(a, qoff, lane), lane);
 }
 
 // Output of one head from its rotated-domain sum: lane p < D/2 holds elements 2p, 2p+1
@@ -336,19 +346,25 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   // there is no key table: then the scores read it through scalar loads)
   const float* qg = qrot + (size_t)bk * G * D;
 
-  // The first tile's key loads go out before the tables are built, so their latency
-  // overlaps the set-up.
+  // Set-up order: the query loads go out first (wave g < G loads head kv_head * G + g;
+  // query heads of one kv head are consecutive, so its row is bk * G + g), then the
+  // first tile's key loads. Loads complete in order, so the query is waited for without
+  // waiting for the tile, whose latency overlaps the table build.
+  // Both loads are unconditional (indices clamped into range), so no branch separates
+  // them from the rotation below and only the query loads are waited for there.
+  uint2 qraw = make_uint2(0u, 0u);
+  if (KT) qraw = load_query_pair(a, ((size_t)bk * G + min(wave, G - 1)) * D, min(lane, P - 1));
+  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
   TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
-  if (tile < tile_end) load_tile_keys(cur, base + (size_t)tile * GE::BYTES, lane);
-
-  // Rotated query for the key table: wave g < G rotates head kv_head * G + g (query
-  // heads of one kv head are consecutive, so its row is bk * G + g).
-  if (KT && wave < G && lane < P)
-    reinterpret_cast<float2*>(s_q)[wave * P + lane] = rotate_query<D>(a, ((size_t)bk * G + wave) * D, lane);
+  load_tile_keys(cur, base + (size_t)min(tile, tile_end - 1) * GE::BYTES, lane);
+  if (KT) {
+    const float2 qv = rotate_query_pair<D>(a, qraw, lane);
+    if (wave < G && lane < P) reinterpret_cast<float2*>(s_q)[wave * P + lane] = qv;
+  }
 
   // cos/sin of the bin centres 2 pi c / n; rows past n are only ever read for slots
   // past the sequence end and are zeroed
