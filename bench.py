@@ -58,11 +58,12 @@ def copy_calibration(mib):
 
 def attn_kernel_name(d, group, n_k, n_v):
     """Name of the attention-kernel instantiation the library launches for this shape:
-    key-table mode 1 when the P * 2^bk * G * 4-byte score table fits in 128 KiB of LDS,
-    2 (half table) when half of it fits and n_k is a power of two, else 0."""
+    key-table mode 2 (half table) when n_k is a power of two and half of the
+    P * 2^bk * G * 4-byte score table fits in 128 KiB of LDS, else 1 when the full
+    table fits, else 0."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
     full = (d // 2) * (1 << bk) * group * 4
-    mode = 1 if full <= 128 * 1024 else (2 if n_k == 1 << bk and full // 2 <= 128 * 1024 else 0)
+    mode = 2 if n_k == 1 << bk and full // 2 <= 128 * 1024 else (1 if full <= 128 * 1024 else 0)
     return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {mode}>"
 
 

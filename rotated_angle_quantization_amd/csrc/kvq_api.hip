@@ -79,8 +79,10 @@ int key_table_mode(const kvq_layer_desc* d, uint32_t hq) {
   const int g = (int)(hq / d->num_kv_heads);
   const int bk = code_bits(d->n_bins_k);
   const long bytes = key_table_bytes((int)d->head_dim, g, bk);
-  if (bytes <= kKeyTableMaxBytes) return 1;
+  // the half table whenever n is a power of two: half the LDS, fewer bank conflicts,
+  // for one extra sign operation per pair
   if (d->n_bins_k == (1u << bk) && bytes / 2 <= kKeyTableMaxBytes) return 2;
+  if (bytes <= kKeyTableMaxBytes) return 1;
   return 0;
 }
 

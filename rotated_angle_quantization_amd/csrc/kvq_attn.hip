@@ -311,10 +311,11 @@ constexpr int split_waves(bool key_table, int group) { return key_table && group
 
 // One workgroup per (split, batch * kv head). KTM (key-table mode) 1: scores read a
 // per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n)
-// from LDS, one FMA per (pair, head). KTM 2 (n a power of two whose full table would
-// not fit): only rows c < n/2 are stored and T[i][c + n/2] = -T[i][c] (the angle plus
-// pi), the top code bit flipping the sign of the radius. KTM 0: scores use the cos/sin
-// table and the rotated query from scalar registers.
+// from LDS, one FMA per (pair, head). KTM 2 (n a power of two): only rows c < n/2 are
+// stored and T[i][c + n/2] = -T[i][c] (the angle plus pi), the top code bit flipping the
+// sign of the radius; half the LDS and fewer bank conflicts for one extra operation per
+// pair, and it admits n = 256 at four heads. KTM 0: scores use the cos/sin table and the
+// rotated query from scalar registers.
 template <int D, int G, int BK, int BV, int KTM>
 __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot) {
@@ -716,7 +717,8 @@ hipError_t decode_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hip
                          dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
       return hipGetLastError();
     }
-  } else if constexpr (full / 2 <= kKeyTableMaxBytes) {
+  }
+  if constexpr (full / 2 <= kKeyTableMaxBytes) {
     if (a.key_table == 2) {
       hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 2>), grid,
                          dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
