@@ -82,26 +82,30 @@ __device__ __forceinline__ float atan01(float z) {
 
 // Angle of a nonzero pair in fp32, by octant reduction: |error| <= 3.5e-7 (polynomial)
 // + 1.2e-7 (z = min/max through the reciprocal) + 6e-8 (rounding the pair to fp32)
-// + 2.4e-7 (the two reflections about pi/2 and pi) < 8e-7 rad.
+// + 2.4e-7 (the two reflections about pi/2 and pi) < 8e-7 rad. The reflections and the
+// sign use the fp32 values' sign bits (exact: rounding keeps the sign).
 __device__ __forceinline__ float angle_f32(float a, float b) {
   const float ax = fabsf(a), ay = fabsf(b);
   const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
   const float p = atan01(mn * __builtin_amdgcn_rcpf(mx));
   float t = ay > ax ? 1.5707963267948966f - p : p;
   t = a < 0.f ? 3.141592653589793f - t : t;
-  return b < 0.f ? -t : t;
+  return __builtin_copysignf(t, b);
 }
 
-// Angle code of a nonzero pair: nearest of n centres 2 pi c / n, i.e.
-// floor(theta n / (2 pi) + 1/2) mod n. The fp32 estimate theta32 (error < 8e-7 rad)
-// gives the centre cf and the distance to the nearest bin edge through the residual
-// theta32 - cf * (2 pi / n) (rounding of the bin width adds < 4e-7 rad). When that
-// distance is below kAngleMargin the pair is compared in binary64 with the edge's
-// direction (bedge[k] = (cos, sin) of (k + 1/2) 2 pi / n): on or past the edge means
-// the upper bin, as the floor above gives at an exact half.
+// Angle code: nearest of n centres 2 pi c / n, i.e. floor(theta n / (2 pi) + 1/2) mod n;
+// 0 for a zero pair. The fp32 estimate theta32 (error < 8e-7 rad) gives the centre cf
+// and the distance to the nearest bin edge through the residual theta32 - cf * (2 pi / n)
+// (rounding of the bin width adds < 4e-7 rad). When that distance is below kAngleMargin
+// the pair is compared in binary64 with the edge's direction (bedge[k] = (cos, sin) of
+// (k + 1/2) 2 pi / n): on or past the edge means the upper bin, as the floor above gives
+// at an exact half. The estimate runs for zero pairs too (it yields NaN, which fails the
+// margin test and converts to 0) and the zero test only selects the result, so no
+// branch surrounds the common path.
 constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
-__device__ __forceinline__ int angle_code(double a, double b, int n, float bins_per_rad_f,
-                                          float bin_rad_f, const double2* bedge) {
+__device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
+                                          float bins_per_rad_f, float bin_rad_f,
+                                          const double2* bedge) {
   const float th = angle_f32((float)a, (float)b);
   const float cf = rintf(th * bins_per_rad_f);
   const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
@@ -112,8 +116,10 @@ __device__ __forceinline__ int angle_code(double a, double b, int n, float bins_
     const double2 e = bedge[kk];
     c = fma(e.x, b, -e.y * a) >= 0.0 ? k + 1 : k;
   }
-  c = c < 0 ? c + n : c;
-  return c >= n ? c - n : c;
+  // c is in [-n/2 - 1, n/2 + 1]: wrap into [0, n) as min(c + n, c) in unsigned terms
+  const unsigned cu = (unsigned)(c + n);
+  const unsigned wrapped = min(cu, cu - (unsigned)n);
+  return zero ? 0 : (int)wrapped;
 }
 
 constexpr int kEncWaves = 4;  // waves (tiles) per workgroup, sharing the edge tables
@@ -250,8 +256,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         const double s_255 = s * (1.0 / 255.0);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_k, kbpr, kbin,
-                                                          s_kedge);
+          cc[k] = (uint8_t)angle_code(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_k, kbpr, kbin,
+                                      s_kedge);
           int rho = 0;
           if (s > 0.0) {
             const float t = __builtin_amdgcn_sqrtf((float)r2[k]) * sc255 + 0.5f;
@@ -285,8 +291,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         const float inv_smin2 = __builtin_amdgcn_rcpf((float)smin2);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = r2[k] == 0.0 ? 0 : (uint8_t)angle_code(y[2 * k], y[2 * k + 1], a.n_v, vbpr, vbin,
-                                                          s_vedge);
+          cc[k] = (uint8_t)angle_code(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_v, vbpr, vbin,
+                                      s_vedge);
           int rho = 0;
           if (spread && r2[k] >= smin2) {
             // lr = log2(r^2 / s_min^2) <= 2 l2; t = 7.5 lr / l2 + 1/2. With absolute
