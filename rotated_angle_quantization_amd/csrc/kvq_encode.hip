@@ -122,6 +122,63 @@ __device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
   return zero ? 0 : (int)wrapped;
 }
 
+// NC codes of width B (one per byte, four per dword in cw) as an LSB-first bit string
+// of NC * B / 32 words, word w stored at dst[w * stride].
+template <int B, int NC>
+__device__ __forceinline__ void store_packed_w(const uint32_t (&cw)[NC / 4], uint32_t* dst,
+                                               int stride) {
+  if constexpr (B == 8) {
+#pragma unroll
+    for (int w = 0; w < NC / 4; ++w) dst[w * stride] = cw[w];
+  } else {
+    uint32_t out[NC * B / 32];
+#pragma unroll
+    for (int w = 0; w < NC * B / 32; ++w) out[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const uint32_t c = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const int bit = B * i, w = bit >> 5, sh = bit & 31;
+      out[w] |= c << sh;
+      if (sh + B > 32) out[w + 1] |= c >> (32 - sh);
+    }
+#pragma unroll
+    for (int w = 0; w < NC * B / 32; ++w) dst[w * stride] = out[w];
+  }
+}
+
+// Same for a runtime width: unrolled kernels for 6, 7 and 8 bits, a loop otherwise.
+template <int NC>
+__device__ __forceinline__ void store_packed(const uint32_t (&cw)[NC / 4], int bits, uint32_t* dst,
+                                             int stride) {
+  switch (bits) {
+    case 6: store_packed_w<6, NC>(cw, dst, stride); return;
+    case 7: store_packed_w<7, NC>(cw, dst, stride); return;
+    case 8: store_packed_w<8, NC>(cw, dst, stride); return;
+    default: break;
+  }
+  uint64_t acc = 0;
+  int nb = 0, w = 0;
+  for (int i = 0; i < NC; ++i) {
+    acc |= (uint64_t)((cw[i >> 2] >> (8 * (i & 3))) & 0xFFu) << nb;
+    nb += bits;
+    if (nb >= 32) {
+      dst[w * stride] = (uint32_t)acc;
+      acc >>= 32;
+      nb -= 32;
+      ++w;
+    }
+  }
+}
+
+// Eight 4-bit values held one per byte in lo, hi (values < 16) as one word of nibbles.
+__device__ __forceinline__ uint32_t nibbles8(uint32_t lo, uint32_t hi) {
+  lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+  lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+  hi = (hi | (hi >> 4)) & 0x00FF00FFu;
+  hi = (hi | (hi >> 8)) & 0x0000FFFFu;
+  return lo | (hi << 16);
+}
+
 constexpr int kEncWaves = 4;  // waves (tiles) per workgroup, sharing the edge tables
 
 template <int D, bool F32IN>
@@ -134,6 +191,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   constexpr int E = D / 4;    // elements per lane
   constexpr int PL = E / 2;   // pairs per lane
   constexpr int TPS = 16;     // tokens per step (4 lanes each)
+  // code staging: keys [token][pair], values [pair][token] (the order each plane is
+  // packed in), one byte per code, rows padded to kRow bytes
   __shared__ uint8_t s_code[kEncWaves][4][kTile][kRow];  // key angle, key radius, value angle, value radius
   __shared__ uint16_t s_ks_all[kEncWaves][kTile];
   __shared__ uint32_t s_vp_all[kEncWaves][kTile];
@@ -314,13 +373,16 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
       }
       if (act) {
         // local pair k is pair 16 (k / 4) + 4 q + k % 4 of the vector
-        uint8_t* dc = kv == 0 ? s_kc[j] : s_vc[j];
-        uint8_t* dr = kv == 0 ? s_kr[j] : s_vr[j];
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
           const int i = 16 * (k >> 2) + 4 * q + (k & 3);
-          dc[i] = cc[k];
-          dr[i] = rr[k];
+          if (kv == 0) {
+            s_kc[j][i] = cc[k];
+            s_kr[j][i] = rr[k];
+          } else {
+            s_vc[i][j] = cc[k];
+            s_vr[i][j] = rr[k];
+          }
         }
       }
     }
@@ -334,72 +396,81 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   {
     const int t = lane;
     if (t >= j_lo && t < j_hi) {
+      uint32_t cw[P / 4], rw[P / 4];  // the token's codes, four per dword
+      const uint32_t* crow = reinterpret_cast<const uint32_t*>(s_kc[t]);
+      const uint32_t* rrow = reinterpret_cast<const uint32_t*>(s_kr[t]);
+#pragma unroll
+      for (int w = 0; w < P / 4; ++w) {
+        cw[w] = crow[w];
+        rw[w] = rrow[w];
+      }
       uint32_t* ka = reinterpret_cast<uint32_t*>(tp + g.ka);
-      uint64_t acc = 0;
-      int nb = 0, w = 0;
-      for (int i = 0; i < P; ++i) {
-        acc |= (uint64_t)s_kc[t][i] << nb;
-        nb += a.bk;
-        if (nb >= 32) {
-          ka[w * kTile + t] = (uint32_t)acc;
-          acc >>= 32;
-          nb -= 32;
-          ++w;
-        }
-      }
+      store_packed<P>(cw, a.bk, ka + t, kTile);
       uint32_t* kr = reinterpret_cast<uint32_t*>(tp + g.kr);
-      for (int w4 = 0; w4 < P / 4; ++w4) {
-        const uint32_t word = (uint32_t)s_kr[t][4 * w4] | ((uint32_t)s_kr[t][4 * w4 + 1] << 8) |
-                              ((uint32_t)s_kr[t][4 * w4 + 2] << 16) |
-                              ((uint32_t)s_kr[t][4 * w4 + 3] << 24);
-        kr[w4 * kTile + t] = word;
-      }
+#pragma unroll
+      for (int w = 0; w < P / 4; ++w) kr[w * kTile + t] = rw[w];
       reinterpret_cast<uint16_t*>(tp + g.ks)[t] = s_ks[t];
       reinterpret_cast<uint32_t*>(tp + g.vp)[t] = s_vp[t];
     }
   }
 
-  // Value planes: one lane per pair. A word shared with slots outside the range is
+  // Value planes: one lane per pair. A whole tile is packed straight from the pair's
+  // staged row; for a partial tile, a word shared with slots outside the range is
   // merged with the bits already stored (this wave owns the whole tile here).
   if (lane < P) {
     const int i = lane;
     uint32_t* va = reinterpret_cast<uint32_t*>(tp + g.va);
     uint32_t* vrw = reinterpret_cast<uint32_t*>(tp + g.vr);
-    uint64_t acc = 0, macc = 0;
-    int nb = 0, w = 0;
-    const uint64_t cmask = (1ull << a.bv) - 1;
-    for (int t = 0; t < kTile; ++t) {
-      const bool in = t >= j_lo && t < j_hi;
-      acc |= (uint64_t)(in ? s_vc[t][i] : 0) << nb;
-      macc |= (in ? cmask : 0ull) << nb;
-      nb += a.bv;
-      if (nb >= 32) {
-        uint32_t* dst = va + w * P + i;
-        const uint32_t mk = (uint32_t)macc;
-        if (mk == 0xffffffffu)
-          *dst = (uint32_t)acc;
-        else if (mk)
-          *dst = (*dst & ~mk) | ((uint32_t)acc & mk);
-        acc >>= 32;
-        macc >>= 32;
-        nb -= 32;
-        ++w;
+    if (j_lo == 0 && j_hi == kTile) {
+      uint32_t cw[kTile / 4], rw[kTile / 4];
+      const uint32_t* crow = reinterpret_cast<const uint32_t*>(s_vc[i]);
+      const uint32_t* rrow = reinterpret_cast<const uint32_t*>(s_vr[i]);
+#pragma unroll
+      for (int w = 0; w < kTile / 4; ++w) {
+        cw[w] = crow[w];
+        rw[w] = rrow[w];
       }
-    }
-    for (int w8 = 0; w8 < 8; ++w8) {
-      uint32_t word = 0, mk = 0;
-      for (int q = 0; q < 8; ++q) {
-        const int t = w8 * 8 + q;
-        if (t >= j_lo && t < j_hi) {
-          word |= (uint32_t)s_vr[t][i] << (4 * q);
-          mk |= 0xFu << (4 * q);
+      store_packed<kTile>(cw, a.bv, va + i, P);
+      // radius nibbles: 8 tokens per word (bytes hold values < 16)
+#pragma unroll
+      for (int w8 = 0; w8 < 8; ++w8) vrw[w8 * P + i] = nibbles8(rw[2 * w8], rw[2 * w8 + 1]);
+    } else {
+      uint64_t acc = 0, macc = 0;
+      int nb = 0, w = 0;
+      const uint64_t cmask = (1ull << a.bv) - 1;
+      for (int t = 0; t < kTile; ++t) {
+        const bool in = t >= j_lo && t < j_hi;
+        acc |= (uint64_t)(in ? s_vc[i][t] : 0) << nb;
+        macc |= (in ? cmask : 0ull) << nb;
+        nb += a.bv;
+        if (nb >= 32) {
+          uint32_t* dst = va + w * P + i;
+          const uint32_t mk = (uint32_t)macc;
+          if (mk == 0xffffffffu)
+            *dst = (uint32_t)acc;
+          else if (mk)
+            *dst = (*dst & ~mk) | ((uint32_t)acc & mk);
+          acc >>= 32;
+          macc >>= 32;
+          nb -= 32;
+          ++w;
         }
       }
-      uint32_t* dst = vrw + w8 * P + i;
-      if (mk == 0xffffffffu)
-        *dst = word;
-      else if (mk)
-        *dst = (*dst & ~mk) | word;
+      for (int w8 = 0; w8 < 8; ++w8) {
+        uint32_t word = 0, mk = 0;
+        for (int q = 0; q < 8; ++q) {
+          const int t = w8 * 8 + q;
+          if (t >= j_lo && t < j_hi) {
+            word |= (uint32_t)s_vr[i][t] << (4 * q);
+            mk |= 0xFu << (4 * q);
+          }
+        }
+        uint32_t* dst = vrw + w8 * P + i;
+        if (mk == 0xffffffffu)
+          *dst = word;
+        else if (mk)
+          *dst = (*dst & ~mk) | word;
+      }
     }
   }
 }
