@@ -83,7 +83,9 @@ const char* kvq_status_string(kvq_status status);
  *
  * Byte layout (this library's own; the abstract fixes no format). P = d/2 pairs,
  * bk = ceil(log2 n_bins_k), bv = ceil(log2 n_bins_v). The cache is
- * [batch][kv_head][tile][tile_bytes], tile = 64 token slots. A tile holds, in order:
+ * [batch][kv_head][tile][tile_bytes], tile = 64 token slots; every entry point takes
+ * the cache pointer 16-byte aligned (tiles are read as 16-byte vectors; tile_bytes is
+ * a multiple of 16). A tile holds, in order:
  *   KA key angle codes   token-major 32-bit words: word w of slot t at 4*(w*64+t);
  *                        slot t's bit string (P*bk bits) has pair i's code at bits
  *                        [i*bk, (i+1)*bk)

@@ -219,7 +219,7 @@ kvq_status kvq_encode(const kvq_layer_desc* d, void* cache, const void* k, const
   if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
   if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
   if (ntok == 0) return KVQ_OK;
-  if (!cache || !k || !v) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!cache || !k || !v || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
   if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
   if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0)
@@ -236,7 +236,7 @@ kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, v
   if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
   if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
   if (ntok == 0) return KVQ_OK;
-  if (!cache || !k_out || !v_out) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!cache || !k_out || !v_out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)k_out % 16) || ((uintptr_t)v_out % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   const CodecArgs a = codec_args(d, t0, ntok);
   return hip_status(launch_decode(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
@@ -264,7 +264,7 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const voi
   AttnArgs a;
   kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
   if (st != KVQ_OK) return st;
-  if (!cache || !q || !out) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
     return KVQ_ERR_INVALID_ARGUMENT;
   if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;

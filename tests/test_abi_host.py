@@ -77,6 +77,7 @@ def test_encode_validation():
     assert _enc(desc, t0=100, ntok=29) == CAPACITY
     assert _enc(desc, k=None) == INVALID
     assert _enc(desc, cache=None) == INVALID
+    assert _enc(desc, cache=FAKE + 8) == INVALID  # cache must be 16-byte aligned
     assert _enc(desc, dtype=7) == INVALID
     assert _enc(desc, k=FAKE + 2) == INVALID  # fp16 pairs need 4-byte alignment
     assert _enc(desc, dtype=1, k=FAKE + 4) == INVALID  # fp32 pairs need 8 bytes
@@ -98,6 +99,7 @@ def test_decode_validation():
     assert dec(dt=2) == INVALID
     assert dec(v=FAKE + 2) == INVALID
     assert dec(k=FAKE + 8) == INVALID  # outputs must be 16-byte aligned
+    assert dec(cache=FAKE + 8) == INVALID  # so must the cache
 
 
 def _attn(desc, hq=32, seq=100, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, qdt=0, odt=0,
@@ -122,6 +124,7 @@ def test_attention_validation():
     assert _attn(desc, out=FAKE + 2) == INVALID
     assert _attn(desc, qdt=3) == INVALID
     assert _attn(desc, cache=None) == INVALID
+    assert _attn(desc, cache=FAKE + 4) == INVALID  # cache must be 16-byte aligned
     small = kvq.make_desc(128, 8, 2, 256, 32, 64)  # 5-bit key angle codes
     assert _attn(small) == UNSUPPORTED
     d64 = kvq.make_desc(64, 4, 1, 256, 256, 33)  # 8-bit / 6-bit: supported shape
