@@ -243,13 +243,36 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;  // n / (2 pi)
   const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
 
+  // Element offset of this lane's part of the row of step jb; lanes past the range
+  // read the last valid row and discard it.
+  auto row_offset = [&](int jb) {
+    const int jr = min(jb + tq, j_hi - 1);
+    return (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
+  };
+  // fp16 input: the K and V words of the next step are loaded while this one is coded
+  uint32_t next_raw[2][PL];
+  auto load_raw = [&](int jb) {
+    const int64_t off = row_offset(jb);
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint32_t* p =
+          reinterpret_cast<const uint32_t*>(static_cast<const __half*>(kv == 0 ? kin : vin) + off);
+#pragma unroll
+      for (int k = 0; k < PL; ++k) next_raw[kv][k] = p[16 * (k >> 2) + (k & 3)];
+    }
+  };
+  if (!F32IN && j_lo < j_hi) load_raw(j_lo);
+
   for (int jb = j_lo; jb < j_hi; jb += TPS) {
     const int j = jb + tq;
     const bool act = j < j_hi;
-    // lanes past the range read the last valid row and discard it
-    const int jr = act ? j : j_hi - 1;
-    const int64_t row_off =
-        (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
+    const int64_t row_off = row_offset(jb);
+    uint32_t raw[2][PL];
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+      for (int k = 0; k < PL; ++k) raw[kv][k] = next_raw[kv][k];
+    if (!F32IN && jb + TPS < j_hi) load_raw(jb + TPS);
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const void* src = kv == 0 ? kin : vin;
@@ -265,11 +288,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
           y[e] = (double)f;
         }
       } else {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const __half*>(src) + row_off);
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          uint32_t w = p[16 * (k >> 2) + (k & 3)];
-          w = (act ? w : 0u) ^ hmask[k];
+          const uint32_t w = (act ? raw[kv][k] : 0u) ^ hmask[k];
           y[2 * k] = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
           y[2 * k + 1] = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
         }
