@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -148,6 +148,23 @@ kvq_status kvq_encode(const kvq_layer_desc* desc, void* cache, const void* k, co
                       int64_t stride_h, uint32_t t0, uint32_t ntok, void* hip_stream);
 
 /*
+ * Append one token per sequence, each at its own slot: the decode-loop step for a batch
+ * whose sequences have different lengths. Sequence b's new K and V rows are encoded
+ * into slot positions[b] of its cache, with exactly the codes and bytes kvq_encode
+ * would write for that token (neighbouring slots keep their bytes).
+ * k, v: device tensors holding one token per sequence; element i of kv head h of
+ *   sequence b at k[b * stride_b + h * stride_h + i] (elements), d contiguous,
+ *   in_dtype f16 or f32, pointers aligned to two elements, strides even.
+ * positions: device array of B slots (uint32, 4-byte aligned), read by the kernel on
+ *   the given stream; an entry >= capacity writes nothing for that sequence.
+ * Errors: INVALID_ARGUMENT (also a null or misaligned positions), UNSUPPORTED (d not
+ * 64/128), HIP.
+ */
+kvq_status kvq_append(const kvq_layer_desc* desc, void* cache, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t stride_b, int64_t stride_h,
+                      const uint32_t* positions, void* hip_stream);
+
+/*
  * Dequantise tokens [t0, t0 + ntok) back to vectors: x_hat = sign * H_d y_hat / sqrt(d)
  * with y_hat[2i] = r_hat cos(2 pi c / n), y_hat[2i+1] = r_hat sin(2 pi c / n);
  * key r_hat = code * s / 255; value r_hat = s_min * exp(code * L / 15) (s_max when
@@ -169,7 +186,8 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  * and one inverse transform per output head brings o back. Work is split over the
  * sequence (flash-decoding style); the last workgroup of each (batch, kv head) to
  * finish merges the partial (max, sum, vector) triples with a log-sum-exp combine, so
- * the whole operation is one kernel launch. fp32 arithmetic.
+ * the whole operation is one kernel launch (two when the key codebook is too large for
+ * an LDS score table: a small query-rotation kernel runs first). fp32 arithmetic.
  *
  * q:   contiguous device tensor [B, Hq, d], q_dtype f16 or f32.
  * out: contiguous device tensor [B, Hq, d], out_dtype f16 or f32.
@@ -190,6 +208,30 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* desc, const void* cache, const 
                            kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t seq_len,
                            float softmax_scale, void* out, kvq_dtype out_dtype,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * kvq_attn_decode with a length per sequence, for batches whose sequences have grown
+ * to different lengths (a decode loop over ragged requests). Entry b attends to its
+ * first seq_lens[b] cached tokens.
+ * seq_lens: device array of B lengths (uint32, 4-byte aligned, one per sequence), read
+ *   by the kernel on the given stream, so it may be produced by earlier work on that
+ *   stream. Entries above max_seq_len are treated as max_seq_len; an entry of 0 gives
+ *   an all-zero output for that sequence.
+ * max_seq_len: host bound, 1 <= max_seq_len <= capacity; the split plan and the
+ *   workspace size are those of kvq_attn_decode at seq_len = max_seq_len (use
+ *   kvq_attn_workspace_bytes(desc, Hq, max_seq_len)). Workgroups of splits past an
+ *   entry's length exit at once.
+ * Everything else (q, out, scale, workspace contract, supported shapes) is as for
+ * kvq_attn_decode; with every entry equal to max_seq_len the result is bitwise that
+ * of kvq_attn_decode(..., seq_len = max_seq_len, ...).
+ * Errors: INVALID_ARGUMENT (also a null or misaligned seq_lens), UNSUPPORTED, CAPACITY,
+ * WORKSPACE, HIP.
+ */
+kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* desc, const void* cache, const void* q,
+                                  kvq_dtype q_dtype, uint32_t num_q_heads,
+                                  const uint32_t* seq_lens, uint32_t max_seq_len,
+                                  float softmax_scale, void* out, kvq_dtype out_dtype,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libkvq.so not found at {LIB_PATH}; build it with "
-        "`python -m rotated_angle_quantization_amd.build` (hipcc, gfx950)")
+        "`python rotated_angle_quantization_amd/build.py` (hipcc, gfx950)")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -60,11 +60,14 @@ _SIGS = {
     "kvq_layer_signs": (ctypes.c_int, [_u64, _u32, _u32, ctypes.POINTER(ctypes.c_int8)]),
     "kvq_encode": (ctypes.c_int, [_P, _v, _v, _v, ctypes.c_int, _i64, _i64, _i64, _u32, _u32,
                                   _v]),
+    "kvq_append": (ctypes.c_int, [_P, _v, _v, _v, ctypes.c_int, _i64, _i64, _v, _v]),
     "kvq_decode": (ctypes.c_int, [_P, _v, _v, _v, ctypes.c_int, _u32, _u32, _v]),
     "kvq_attn_workspace_bytes": (_sz, [_P, _u32, _u32]),
     "kvq_attn_num_splits": (_u32, [_P, _u32, _u32]),
     "kvq_attn_decode": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
                                        ctypes.c_int, _v, _sz, _v]),
+    "kvq_attn_decode_varlen": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _v, _u32, _f32,
+                                              _v, ctypes.c_int, _v, _sz, _v]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -135,6 +138,25 @@ def encode(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tenso
                           _stream(cache.device)), "kvq_encode")
 
 
+def append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+           positions: torch.Tensor):
+    """Encode one token per sequence at slot positions[b] of sequence b.
+    k, v: [B, Hkv, d] (or [B, 1, Hkv, d]) with d contiguous, fp16 or fp32; positions:
+    int32 device tensor [B]."""
+    if k.dim() == 4 and k.shape[1] == 1:
+        k, v = k[:, 0], v[:, 0]
+    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must have the same dtype")
+    if positions.dtype not in (torch.int32, torch.uint32) or not positions.is_contiguous() \
+            or positions.numel() != k.shape[0] or positions.device != k.device:
+        raise ValueError("positions must be a contiguous int32 device tensor [B] on k's device")
+    _check(lib.kvq_append(ctypes.byref(desc), cache.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          _dtype_code(k), k.stride(0), k.stride(1), positions.data_ptr(),
+                          _stream(cache.device)), "kvq_append")
+
+
 def decode(desc: LayerDesc, cache: torch.Tensor, t0: int, ntok: int,
            out_dtype=torch.float16, out: tuple | None = None):
     """Dequantise tokens [t0, t0 + ntok) -> (k_hat, v_hat), each [B, ntok, Hkv, d]."""
@@ -182,6 +204,30 @@ def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: 
                                _dtype_code(q), hq, seq_len, float(softmax_scale),
                                out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
                                workspace.numel(), _stream(q.device)), "kvq_attn_decode")
+    return out
+
+
+def attn_decode_varlen(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor,
+                       seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
+                       out_dtype=None, workspace=None, out=None):
+    """attn_decode with a length per sequence: entry b attends to its first seq_lens[b]
+    cached tokens. seq_lens: int32 (or uint32 bits) device tensor [B], every entry
+    <= max_seq_len (larger entries count as max_seq_len; 0 gives a zero output)."""
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    if seq_lens.dtype not in (torch.int32, torch.uint32) or not seq_lens.is_contiguous() \
+            or seq_lens.numel() != q.shape[0] or seq_lens.device != q.device:
+        raise ValueError("seq_lens must be a contiguous int32 device tensor [B] on q's device")
+    hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    _check(lib.kvq_attn_decode_varlen(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
+                                      _dtype_code(q), hq, seq_lens.data_ptr(), max_seq_len,
+                                      float(softmax_scale), out.data_ptr(), _dtype_code(out),
+                                      workspace.data_ptr(), workspace.numel(),
+                                      _stream(q.device)), "kvq_attn_decode_varlen")
     return out
 
 

@@ -1,6 +1,7 @@
 """Build libkvq.so for gfx950 with hipcc (in-tree, next to this file).
 
-    python -m rotated_angle_quantization_amd.build [-j N]
+    python rotated_angle_quantization_amd/build.py [-j N]   (as a script: the package
+    itself loads the library, which may be missing or older than the sources)
 
 Each HIP source compiles to an object under _build/ (in parallel), then one shared
 library is linked. Packed-FP32 instruction selection is disabled for device code.

@@ -69,6 +69,8 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
   a.k_bins_per_rad = (double)d->n_bins_k / kTwoPi;
   a.v_bins_per_rad = (double)d->n_bins_v / kTwoPi;
   a.sign = sign_mask(d->seed, d->layer, d->head_dim);
+  a.positions = nullptr;
+  a.capacity = (int)d->capacity;
   return a;
 }
 
@@ -169,10 +171,32 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->qrot = (float*)(base + l.qrot);
   a->part_ml = (float*)(base + l.ml);
   a->part_acc = (float*)(base + l.acc);
+  a->seq_lens = nullptr;
   return KVQ_OK;
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const void* q,
+                    kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, const uint32_t* seq_lens,
+                    float scale, void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                    void* stream) {
+  AttnArgs a;
+  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  a.q = q;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.out = out;
+  a.out_f32 = out_dtype == KVQ_F32;
+  a.seq_lens = seq_lens;
+  return hip_status(
+      launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
+}
 
 }  // namespace
 
@@ -229,6 +253,23 @@ kvq_status kvq_encode(const kvq_layer_desc* d, void* cache, const void* k, const
                                   in_dtype == KVQ_F32, sb, st, sh, (hipStream_t)stream));
 }
 
+kvq_status kvq_append(const kvq_layer_desc* d, void* cache, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t sb, int64_t sh, const uint32_t* positions,
+                      void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (!cache || !k || !v || !positions || ((uintptr_t)cache % 16) || ((uintptr_t)positions % 4))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (sh & 1) || sb < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  CodecArgs a = codec_args(d, 0, 1);  // one tile per (batch, kv head), chosen on the device
+  a.positions = positions;
+  return hip_status(launch_encode(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
+                                  in_dtype == KVQ_F32, sb, 0, sh, (hipStream_t)stream));
+}
+
 kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, void* v_out,
                       kvq_dtype out_dtype, uint32_t t0, uint32_t ntok, void* stream) {
   if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
@@ -261,20 +302,22 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const voi
                            kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, float scale,
                            void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
                            void* stream) {
-  AttnArgs a;
-  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
-  if (st != KVQ_OK) return st;
-  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
-    return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  a.q = q;
-  a.q_f32 = q_dtype == KVQ_F32;
-  a.out = out;
-  a.out_f32 = out_dtype == KVQ_F32;
-  return hip_status(
-      launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
+  return attn_run(d, cache, q, q_dtype, hq, seq_len, nullptr, scale, out, out_dtype, ws,
+                  ws_bytes, stream);
+}
+
+kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* d, const void* cache, const void* q,
+                                  kvq_dtype q_dtype, uint32_t hq, const uint32_t* seq_lens,
+                                  uint32_t max_seq_len, float scale, void* out,
+                                  kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!seq_lens || ((uintptr_t)seq_lens % 4)) {
+    // shape errors take precedence, as in kvq_attn_decode
+    const kvq_status st = attn_check(d, hq, max_seq_len);
+    return st != KVQ_OK ? st : KVQ_ERR_INVALID_ARGUMENT;
+  }
+  return attn_run(d, cache, q, q_dtype, hq, max_seq_len, seq_lens, scale, out, out_dtype, ws,
+                  ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -11,25 +11,27 @@
 // and the output is o = R^T (sum_j p_j z^_j) with z^_j the rotated-domain values:
 // one inverse transform per output head instead of one per cached token.
 //
-// Three launches on one stream:
-//   prepare  q~ = R q, pre-multiplied by softmax_scale * log2(e) / 255, into the
-//            workspace.
-//   split    grid (splits, batch * kv heads); each wave streams whole 64-token tiles
-//            (12 waves per workgroup with the key table, else 8). Keys: one lane per
-//            token; the score of pair i is one FMA per head against a per-workgroup
-//            LDS table T[i][code][head] = q~_2i cos + q~_2i+1 sin (or, when the table
-//            would not fit, cos/sin from a small LDS table times q~ from SGPRs).
-//            Online softmax per wave in base 2. Values: lanes are 4 rows x 16
-//            columns; each step takes one token per row, its weights broadcast along
-//            the row with DPP, its 16 radius levels computed once per row and gathered
-//            with a lane permute, cos/sin from LDS. Waves merge through LDS; each split
-//            writes (max, sum, acc[d]) per head.
-//   merge    per (batch, query head): log-sum-exp combine of the splits, divide,
-//            inverse transform, sign, store.
+// One launch (two without a key table): grid (splits, batch * kv heads), each wave
+// streaming whole 64-token tiles (12 waves per workgroup with the key table and up to
+// four heads, else 8).
+//   set-up   the workgroup rotates its G query heads (q~ = R q times
+//            softmax_scale * log2(e) / 255) and builds cos/sin tables and the score
+//            table T[i][code][head] = q~_2i cos + q~_2i+1 sin in LDS. Without a key
+//            table (codebook too large for LDS) a small prepare kernel writes q~ to
+//            the workspace first and scores read it through scalar loads.
+//   keys     one lane per token; the score of pair i is one FMA per head against T.
+//            Online softmax per wave in base 2.
+//   values   lanes are 4 rows x 16 columns; each step takes one token per row, its
+//            weights broadcast along the row with DPP, its 16 radius levels computed
+//            once per row and gathered with a lane permute, cos/sin from LDS.
+//   merge    waves merge through LDS. With one split the workgroup normalises,
+//            inverse-transforms and stores; otherwise each split writes
+//            (max, sum, acc[d]) per head and the last workgroup of the (batch, kv head)
+//            to finish combines them (log-sum-exp), inverse-transforms and stores.
 //
-// The split kernel is bound by VALU issue, not by HBM: every (token, pair) of a tile
-// costs G FMAs for the score and 2G for the value sum, and a wave64 FP32 FMA occupies
-// a SIMD for four cycles on this chip.
+// The kernel is bound by VALU issue and LDS instruction throughput, not by HBM: every
+// (token, pair) of a tile costs G FMAs for the score and 2G for the value sum, and a
+// wave64 FP32 FMA occupies a SIMD for four cycles on this chip.
 #include <hip/hip_fp16.h>
 #include <math.h>
 
@@ -343,6 +345,24 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
+  // This entry's length (per-entry lengths are clamped to the planned maximum), its
+  // tiles and the splits that cover them; a.nsplit stays the stride of the partials.
+  const int seq_len = a.seq_lens ? (int)min(a.seq_lens[bk / a.hkv], (unsigned)a.seq_len)
+                                 : a.seq_len;
+  const int ntiles = (seq_len + kTile - 1) / kTile;
+  const int nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (split >= nsplit) {
+    if (split == 0) {  // an empty sequence attends to nothing: zero output
+      for (int idx = tid; idx < G * D; idx += NW * 64) {
+        const size_t o = (size_t)bk * G * D + idx;
+        if (a.out_f32)
+          static_cast<float*>(a.out)[o] = 0.f;
+        else
+          static_cast<__half*>(a.out)[o] = __float2half(0.f);
+      }
+    }
+    return;
+  }
   // rotated query in the workspace, written by the prepare kernel (only launched when
   // there is no key table: then the scores read it through scalar loads)
   const float* qg = qrot + (size_t)bk * G * D;
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   if (KT) qraw = load_query_pair(a, ((size_t)bk * G + min(wave, G - 1)) * D, min(lane, P - 1));
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads
   const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
+  const int tile_end = min(tile_begin + a.tiles_per_split, ntiles);
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
   TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
@@ -430,7 +450,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     // keeps the register count low enough for that occupancy.
     const uint8_t* tp = base + (size_t)tile * GE::BYTES;
     if (tile != tile_begin + wave) load_tile_keys(cur, tp, lane);
-    const int nvalid = min(a.seq_len - tile * kTile, kTile);
+    const int nvalid = min(seq_len - tile * kTile, kTile);
     const bool valid = lane < nvalid;
 
     // ---- keys: lane = token slot
@@ -615,7 +635,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     }
   }
   __syncthreads();
-  const bool single = a.nsplit == 1;
+  const bool single = nsplit == 1;
   for (int idx = tid; idx < G * D; idx += NW * 64) {
     const int g = idx / D, e = idx % D;
     float mm = s_ml[g * 2];
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     // on different XCDs (each with its own L2) count on one copy
     const unsigned t = __hip_atomic_fetch_add(a.tickets + bk, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_SYSTEM);
-    *s_flag = t == (unsigned)(a.nsplit - 1);
+    *s_flag = t == (unsigned)(nsplit - 1);
   }
   __syncthreads();
   if (!*s_flag) return;
@@ -678,18 +698,18 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     const float* ml = a.part_ml + 2 * row0;
     const float* pa = a.part_acc + row0 * D + e;
     float mm = -INFINITY, ll = 0.f, aa = 0.f;
-    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
       float mv[8], lv[8], av[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int sp = min(s0 + u, a.nsplit - 1);
+        const int sp = min(s0 + u, nsplit - 1);
         mv[u] = ld(ml + 2 * sp);
         lv[u] = ld(ml + 2 * sp + 1);
         av[u] = ld(pa + (size_t)sp * D);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (s0 + u < a.nsplit) {  // every split covers a valid token, so m is finite
+        if (s0 + u < nsplit) {  // every split covers a valid token, so m is finite
           const float mnew = fmaxf(mm, mv[u]);
           const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv[u] - mnew);
           ll = ll * c0 + lv[u] * c1;

@@ -217,14 +217,24 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   // one tile per wave; waves past the last tile do no work (but take the barrier)
   const int task = blockIdx.x * kEncWaves + wave;
   const int ntasks = a.batch * a.hkv * a.tiles_touched;
-  const bool live = task < ntasks;
+  bool live = task < ntasks;
   const int tile_rel = task % a.tiles_touched;
   const int bh = live ? task / a.tiles_touched : 0;
   const int b = bh / a.hkv, h = bh % a.hkv;
-  const int tile = a.tile_lo + tile_rel;
+  // token range: [t0, t0 + ntok) for every sequence, or one token per sequence at its
+  // own slot (positions past the capacity write nothing)
+  int t0 = a.t0, ntok = a.ntok, tile_lo = a.tile_lo;
+  if (a.positions) {
+    const unsigned pos = a.positions[b];
+    live = live && pos < (unsigned)a.capacity;
+    t0 = live ? (int)pos : 0;
+    ntok = 1;
+    tile_lo = t0 / kTile;
+  }
+  const int tile = tile_lo + tile_rel;
   const int tok_base = tile * kTile;
-  const int j_lo = max(a.t0 - tok_base, 0);
-  const int j_hi = live ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
+  const int j_lo = max(t0 - tok_base, 0);
+  const int j_hi = live ? min(t0 + ntok - tok_base, kTile) : j_lo;
 
   // Lane q of a token's quad owns the 8-element chunks m*4 + q (elements
   // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   // read the last valid row and discard it.
   auto row_offset = [&](int jb) {
     const int jr = min(jb + tq, j_hi - 1);
-    return (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
+    return (int64_t)b * sb + (int64_t)(tok_base + jr - t0) * st + (int64_t)h * sh + 8 * q;
   };
   // fp16 input: the K and V words of the next step are loaded while this one is coded
   uint32_t next_raw[2][PL];

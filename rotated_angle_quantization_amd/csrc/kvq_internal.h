@@ -61,6 +61,8 @@ struct CodecArgs {
   double k_bins_per_rad;    // n_k / (2 pi) in fp64
   double v_bins_per_rad;    // n_v / (2 pi) in fp64
   SignMask sign;
+  const unsigned* positions;  // encode: [B] one token per sequence at these slots, or null
+  int capacity;               // tokens per sequence
 };
 
 hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cache,
@@ -86,6 +88,7 @@ struct AttnArgs {
   float* qrot;         // [B, Hq, d] rotated queries (kernels without the key table)
   float* part_ml;      // [B, Hq, nsplit, 2]
   float* part_acc;     // [B, Hq, nsplit, d]
+  const unsigned* seq_lens;  // [B] per-entry lengths (device), or null: seq_len for all
 };
 
 // Bytes of the per-workgroup key-score table (pairs x 2^bk codes x heads x fp32) and

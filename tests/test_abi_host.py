@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 2
+    assert kvq.abi_version() == 3
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -149,3 +149,44 @@ def test_layer_signs_validation():
     assert lib.kvq_layer_signs(0, 0, 8, None) == INVALID
     assert lib.kvq_layer_signs(0, 0, 8, buf) == OK
     assert set(np.array(buf)) <= {-1, 1}
+
+
+def _varlen(desc, hq=32, lens=FAKE, maxlen=100, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE,
+            cache=FAKE):
+    return lib.kvq_attn_decode_varlen(ctypes.byref(desc), cache, q, 0, hq, lens, maxlen, 0.0,
+                                      out, 0, ws, ws_bytes, None)
+
+
+def test_attention_varlen_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    assert _varlen(desc, lens=None) == INVALID
+    assert _varlen(desc, lens=FAKE + 2) == INVALID  # uint32 lengths: 4-byte aligned
+    assert _varlen(desc, maxlen=0) == INVALID
+    assert _varlen(desc, maxlen=257) == CAPACITY
+    assert _varlen(desc, lens=None, maxlen=257) == CAPACITY  # shape errors first
+    assert _varlen(desc, hq=24) == UNSUPPORTED
+    assert _varlen(desc, ws=None) == WORKSPACE
+    assert _varlen(desc, cache=FAKE + 4) == INVALID
+    assert _varlen(desc, q=None) == INVALID
+    # the workspace needed is that of the fixed-length call at max_seq_len
+    need = kvq.attn_workspace_bytes(desc, 32, 200)
+    assert _varlen(desc, maxlen=200, ws_bytes=need - 1) == WORKSPACE
+
+
+def _app(desc, cache=FAKE, k=FAKE, v=FAKE, dtype=0, sb=0, sh=0, pos=FAKE):
+    return lib.kvq_append(ctypes.byref(desc), cache, k, v, dtype, sb, sh, pos, None)
+
+
+def test_append_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    assert _app(desc, pos=None) == INVALID
+    assert _app(desc, pos=FAKE + 2) == INVALID
+    assert _app(desc, cache=None) == INVALID
+    assert _app(desc, cache=FAKE + 8) == INVALID
+    assert _app(desc, k=FAKE + 2) == INVALID
+    assert _app(desc, dtype=1, v=FAKE + 4) == INVALID
+    assert _app(desc, dtype=5) == INVALID
+    assert _app(desc, sb=3) == INVALID
+    assert _app(desc, sh=-2) == INVALID
+    assert _app(kvq.make_desc(256, 8, 1, 128, 128, 64)) == UNSUPPORTED
+    assert lib.kvq_append(None, FAKE, FAKE, FAKE, 0, 0, 0, FAKE, None) == INVALID
