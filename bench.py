@@ -5,7 +5,9 @@ One step = the whole path over one batch of synthetic input, all layers:
   attend   one decode query per sequence over the full compressed cache
            (kvq_attn_decode: one kernel launch), every layer
   dequant  packed cache -> fp16 K/V (kvq_decode), every layer
-Inputs and caches are resident in HBM before timing starts. `value` is decode-attention
+After the timed steps, a ragged-batch decode loop is timed on the same caches (append one
+token per sequence at its own slot, attend with per-sequence lengths) and reported under
+`decode_loop`. Inputs and caches are resident in HBM before timing starts. `value` is decode-attention
 throughput in GB/s of compressed cache read per second over the attention phase of a
 step (all layers, every launch and gap included). Phase times come from HIP events on
 the stream the library launches on. Each attention launch (the dominant kernel) is
@@ -152,6 +154,63 @@ def cpu_baseline(cfg, budget_s):
     }
 
 
+def decode_loop(kvq, cfg, descs, caches, ws, dev, iters=8):
+    """Decode steps of a ragged batch on the resident caches: per layer, append one new
+    token per sequence at its own slot (kvq_append), then attend with a length per
+    sequence (kvq_attn_decode_varlen). Timed with HIP events on the library's stream."""
+    import torch
+
+    L, B, T, Hkv, Hq, d = cfg.layers, cfg.batch, cfg.seq, cfg.hkv, cfg.hq, cfg.d
+    lens0 = [T - iters - (T // 3) * b // max(B - 1, 1) for b in range(B)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    new_k = torch.randn((B, Hkv, d), generator=gen, device=dev).half()
+    new_v = torch.randn((B, Hkv, d), generator=gen, device=dev).half()
+    qd = torch.randn((B, Hq, d), generator=gen, device=dev).half()
+    pos = [torch.tensor(lens0, dtype=torch.int32, device=dev) + i for i in range(iters + 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def run(record):
+        for i in range(iters):
+            for layer in range(L):
+                ev = (Ev(), Ev(), Ev()) if record is not None else None
+                if ev:
+                    ev[0].record()
+                kvq.append(descs[layer], caches[layer], new_k, new_v, pos[i])
+                if ev:
+                    ev[1].record()
+                kvq.attn_decode_varlen(descs[layer], caches[layer], qd, pos[i + 1], T,
+                                       workspace=ws, out=out)
+                if ev:
+                    ev[2].record()
+                    record.append((layer, i, ev))
+
+    run(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0, t1 = Ev(), Ev()
+    t0.record()
+    run(recs)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    app_us = sum(ev[0].elapsed_time(ev[1]) for _, _, ev in recs) * 1e3 / len(recs)
+    att_us = sum(ev[1].elapsed_time(ev[2]) for _, _, ev in recs) * 1e3 / len(recs)
+    att_bytes = sum(record_bytes(d, *cfg.bins(layer), Hkv * (sum(lens0) + B * (i + 1)))
+                    for layer, i, _ in recs) / len(recs)
+    return {
+        "what": "per layer: kvq_append of one token per sequence at its own slot, then "
+                "kvq_attn_decode_varlen over each sequence's length",
+        "batch_lengths_start": lens0,
+        "iterations": iters,
+        "ms_per_token_all_layers": round(total_ms / iters, 4),
+        "append_us_per_layer": round(app_us, 2),
+        "attend_us_per_layer": round(att_us, 2),
+        "attend_GBps": round(att_bytes / (att_us * 1e-6) / 1e9, 2),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -227,6 +286,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
+    loop = decode_loop(kvq, cfg, descs, caches, ws, dev)
+
     enc_ms = sum(e[0].elapsed_time(e[1]) for e, _ in recs) / args.steps
     att_ms = sum(e[1].elapsed_time(e[2]) for e, _ in recs) / args.steps
     deq_ms = sum(e[2].elapsed_time(e[3]) for e, _ in recs) / args.steps
@@ -265,6 +326,7 @@ def main():
         "dequant_ms": round(deq_ms, 4),
         "dequant_out_GBps": round(2 * L * B * T * Hkv * d * 2 / (deq_ms * 1e-3) / 1e9, 2),
         "wall_s_timed": round(wall, 3),
+        "decode_loop": loop,
         "roofline": {
             "kernel": "attn_decode_kernel (kvq_attn_decode)",
             "bound": "hbm",
