@@ -264,10 +264,10 @@ kvq_status kvq_append(const kvq_layer_desc* d, void* cache, const void* k, const
   const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
   if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
   if ((sb & 1) || (sh & 1) || sb < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
-  CodecArgs a = codec_args(d, 0, 1);  // one tile per (batch, kv head), chosen on the device
+  CodecArgs a = codec_args(d, 0, 1);
   a.positions = positions;
-  return hip_status(launch_encode(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
-                                  in_dtype == KVQ_F32, sb, 0, sh, (hipStream_t)stream));
+  return hip_status(launch_append(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
+                                  in_dtype == KVQ_F32, sb, sh, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, void* v_out,

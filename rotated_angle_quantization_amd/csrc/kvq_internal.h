@@ -61,10 +61,13 @@ struct CodecArgs {
   double k_bins_per_rad;    // n_k / (2 pi) in fp64
   double v_bins_per_rad;    // n_v / (2 pi) in fp64
   SignMask sign;
-  const unsigned* positions;  // encode: [B] one token per sequence at these slots, or null
+  const unsigned* positions;  // append: [B] slot of each sequence's new token
   int capacity;               // tokens per sequence
 };
 
+hipError_t launch_append(const CodecArgs& a, int d, TileGeom geom, uint8_t* cache,
+                         const void* k, const void* v, bool f32_in, int64_t sb, int64_t sh,
+                         hipStream_t stream);
 hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cache,
                          const void* k, const void* v, bool f32_in, int64_t sb, int64_t st,
                          int64_t sh, hipStream_t stream);
