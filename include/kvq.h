@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -232,6 +232,34 @@ kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* desc, const void* cache,
                                   const uint32_t* seq_lens, uint32_t max_seq_len,
                                   float softmax_scale, void* out, kvq_dtype out_dtype,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Multi-query attention over the compressed cache: num_queries query tokens per
+ * sequence (a chunk of prefill, or the draft tokens of a speculative step under
+ * verification), whose own K/V are the last num_queries of the seq_len cached tokens.
+ * Query token j (0-based) attends causally to tokens [0, seq_len - num_queries + j + 1):
+ *   o[b, j, h] = sum_t softmax_t(scale <q[b, j, h], k_hat[b, t, h/G]>) v_hat[b, t, h/G].
+ * The num_queries * G query rows of a kv head share every key and value, so the scores
+ * and the value sum are dense products and run on the matrix cores with fp16 operands
+ * (rotated queries, reconstructed rotated keys, probabilities, reconstructed rotated
+ * values) and fp32 accumulation; softmax and the merge are fp32. Same rotated-domain
+ * formulation and single inverse transform per output row as kvq_attn_decode.
+ * q:   contiguous device tensor [B, num_queries, Hq, d], q_dtype f16 or f32.
+ * out: contiguous device tensor [B, num_queries, Hq, d], out_dtype f16 or f32.
+ * workspace: at least kvq_attn_multi_workspace_bytes(desc, Hq, num_queries, seq_len)
+ *   bytes, 256-byte aligned, zero-filled once after allocation; every completed call
+ *   leaves its split counters at zero. Calls sharing a workspace must not overlap.
+ * Supported: d in {64, 128}; G in {1, 2, 4, 8}; num_queries * G <= 32; angle codes of 6
+ *   to 8 bits for K and V; 1 <= num_queries <= seq_len <= capacity.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
+ */
+size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* desc, uint32_t num_q_heads,
+                                      uint32_t num_queries, uint32_t seq_len);
+
+kvq_status kvq_attn_multi(const kvq_layer_desc* desc, const void* cache, const void* q,
+                          kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t num_queries,
+                          uint32_t seq_len, float softmax_scale, void* out, kvq_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole

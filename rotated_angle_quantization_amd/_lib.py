@@ -68,6 +68,9 @@ _SIGS = {
                                        ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_decode_varlen": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _v, _u32, _f32,
                                               _v, ctypes.c_int, _v, _sz, _v]),
+    "kvq_attn_multi_workspace_bytes": (_sz, [_P, _u32, _u32, _u32]),
+    "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
+                                      ctypes.c_int, _v, _sz, _v]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -228,6 +231,33 @@ def attn_decode_varlen(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor,
                                       float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                       workspace.data_ptr(), workspace.numel(),
                                       _stream(q.device)), "kvq_attn_decode_varlen")
+    return out
+
+
+def attn_multi_workspace_bytes(desc: LayerDesc, num_q_heads: int, num_queries: int,
+                               seq_len: int) -> int:
+    return lib.kvq_attn_multi_workspace_bytes(ctypes.byref(desc), num_q_heads, num_queries,
+                                              seq_len)
+
+
+def attn_multi(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
+               softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None):
+    """Multi-query attention: q contiguous [B, NQ, Hq, d]; query token j attends to the
+    first seq_len - NQ + j + 1 cached tokens. Returns [B, NQ, Hq, d]."""
+    if not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be contiguous [B, NQ, Hq, d]")
+    nq, hq = q.shape[1], q.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        n = attn_multi_workspace_bytes(desc, hq, nq, seq_len)
+        if n == 0:
+            raise KvqError(1, "kvq_attn_multi_workspace_bytes")
+        workspace = torch.zeros(n, dtype=torch.uint8, device=q.device)
+    _check(lib.kvq_attn_multi(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
+                              _dtype_code(q), hq, nq, seq_len, float(softmax_scale),
+                              out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
+                              workspace.numel(), _stream(q.device)), "kvq_attn_multi")
     return out
 
 

@@ -172,6 +172,7 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->part_ml = (float*)(base + l.ml);
   a->part_acc = (float*)(base + l.acc);
   a->seq_lens = nullptr;
+  a->nq = 1;
   return KVQ_OK;
 }
 
@@ -196,6 +197,53 @@ kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const void* q,
   a.seq_lens = seq_lens;
   return hip_status(
       launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
+}
+
+// Multi-query attention: rows = nq * G query rows per kv head, padded to 16 or 32.
+constexpr uint32_t kMultiMaxRows = 32;
+int multi_rows(uint32_t rows) { return rows <= 16 ? 16 : 32; }
+
+kvq_status multi_check(const kvq_layer_desc* d, uint32_t hq, uint32_t nq, uint32_t seq_len) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (hq == 0 || hq % d->num_kv_heads || nq == 0 || seq_len == 0 || nq > seq_len)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (seq_len > d->capacity) return KVQ_ERR_CAPACITY;
+  const uint32_t g = hq / d->num_kv_heads;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
+  if ((uint64_t)nq * g > kMultiMaxRows) return KVQ_ERR_UNSUPPORTED;
+  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
+  if (bk < 6 || bk > 8 || bv < 6 || bv > 8) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+// Sequence split for multi-query attention: one four-wave workgroup per compute unit
+// fits its LDS, so aim for 256 workgroups, with at least four tiles (one per wave) per
+// split and no empty split.
+void multi_split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tiles_per_split) {
+  const int ntiles = (int)((seq_len + kTile - 1) / kTile);
+  int s = (int)((256 + units - 1) / units);
+  int max_s = (ntiles + 3) / 4;
+  if (max_s < 1) max_s = 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  const int tps = (ntiles + s - 1) / s;
+  *tiles_per_split = tps;
+  *nsplit = (ntiles + tps - 1) / tps;
+}
+
+struct MultiLayout {
+  size_t tickets, ml, acc, total;
+};
+MultiLayout multi_layout(const kvq_layer_desc* d, uint32_t rows, int nsplit) {
+  MultiLayout l;
+  const size_t units = (size_t)d->batch * d->num_kv_heads;
+  const size_t m = (size_t)multi_rows(rows);
+  l.tickets = 0;
+  l.ml = align256(units * sizeof(unsigned));
+  l.acc = align256(l.ml + units * nsplit * m * 2 * sizeof(float));
+  l.total = align256(l.acc + units * nsplit * m * d->head_dim * sizeof(float));
+  return l;
 }
 
 }  // namespace
@@ -318,6 +366,62 @@ kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* d, const void* cache, co
   }
   return attn_run(d, cache, q, q_dtype, hq, max_seq_len, seq_lens, scale, out, out_dtype, ws,
                   ws_bytes, stream);
+}
+
+size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t nq,
+                                      uint32_t seq_len) {
+  if (multi_check(d, hq, nq, seq_len) != KVQ_OK) return 0;
+  int nsplit, tps;
+  multi_split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  return multi_layout(d, nq * (hq / d->num_kv_heads), nsplit).total;
+}
+
+kvq_status kvq_attn_multi(const kvq_layer_desc* d, const void* cache, const void* q,
+                          kvq_dtype q_dtype, uint32_t hq, uint32_t nq, uint32_t seq_len,
+                          float scale, void* out, kvq_dtype out_dtype, void* ws,
+                          size_t ws_bytes, void* stream) {
+  kvq_status st = multi_check(d, hq, nq, seq_len);
+  if (st != KVQ_OK) return st;
+  int nsplit, tps;
+  multi_split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  const uint32_t g = hq / d->num_kv_heads;
+  const MultiLayout l = multi_layout(d, nq * g, nsplit);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < l.total) return KVQ_ERR_WORKSPACE;
+  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  AttnArgs a = {};
+  a.batch = (int)d->batch;
+  a.hkv = (int)d->num_kv_heads;
+  a.hq = (int)hq;
+  a.group = (int)g;
+  a.nq = (int)nq;
+  a.seq_len = (int)seq_len;
+  a.tiles_per_seq = tiles_per_seq(d);
+  a.ntiles = (int)((seq_len + kTile - 1) / kTile);
+  a.nsplit = nsplit;
+  a.tiles_per_split = tps;
+  a.n_k = (int)d->n_bins_k;
+  a.n_v = (int)d->n_bins_v;
+  a.bk = code_bits(d->n_bins_k);
+  a.bv = code_bits(d->n_bins_v);
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
+  a.q_scale = (float)(sc * 1.4426950408889634);  // the key radius carries s / 255 here
+  a.inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
+  a.sign = sign_mask(d->seed, d->layer, d->head_dim);
+  a.q = q;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.out = out;
+  a.out_f32 = out_dtype == KVQ_F32;
+  char* base = (char*)ws;
+  a.tickets = (unsigned*)(base + l.tickets);
+  a.part_ml = (float*)(base + l.ml);
+  a.part_acc = (float*)(base + l.acc);
+  a.seq_lens = nullptr;
+  return hip_status(launch_attn_multi(a, (int)d->head_dim, (int)(nq * g), (const uint8_t*)cache,
+                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,391 @@
+// Multi-query attention straight from the packed angle codes: NQ query tokens per
+// sequence (a chunk of prefill, or the draft tokens of a speculative step under
+// verification), each attending causally to the cache.
+//
+// Method: the codec of "TurboAngle: Near-Lossless KV Cache Compression via Uniform
+// Angle Quantization" (arXiv 2603.27467), Abstract, consumed without writing a
+// dequantised cache, as in single-query decode attention: scores and the value sum stay
+// in the rotated domain, and each output row gets one inverse transform.
+//
+// With M = NQ * G query rows per kv head (G query heads per kv head) the per-tile work
+// is a dense [M x d] x [d x 64] product for the scores and [M x 64] x [64 x d] for the
+// values, so it runs on the matrix cores (v_mfma_f32_16x16x16f16: fp16 operands, fp32
+// accumulation) instead of one FMA per (row, token, pair). A wave streams whole 64-token
+// tiles: it rebuilds the tile's rotated keys r^ (cos, sin) as fp16 in LDS (one lane per
+// token), multiplies, runs the online softmax on the score fragments, stores the
+// probabilities as fp16, rebuilds the rotated values in the same LDS space (one lane
+// per pair) and accumulates P V^. Rows of query token j see tokens [0, L - NQ + j + 1).
+// Waves merge through LDS; splits of the sequence merge through the workspace, the last
+// workgroup of each (batch, kv head) combining them (log-sum-exp) and storing.
+#include "kvq_attn_common.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMqWaves = 4;
+
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __floats2half2_rn(lo, hi));
+}
+// Four fp16 values from two dwords (low halves first).
+__device__ __forceinline__ h4 h4_from(const uint32_t* p) {
+  const uint2 u = make_uint2(p[0], p[1]);
+  return __builtin_bit_cast(h4, u);
+}
+
+// Maximum and sum over the 16 lanes of each DPP row (lanes 16k .. 16k + 15).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  return fmaxf(x, dpp<kDppMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x + dpp<kDppMirror>(x);
+}
+
+// MFMA operand layouts (16x16x16, wave64): lane l holds A[row l % 16][k 4(l/16) .. +3],
+// B[k 4(l/16) .. +3][column l % 16] and D[rows 4(l/16) .. +3][column l % 16].
+template <int D, int BK, int BV, int RB>
+__global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
+                                                                   const uint8_t* __restrict__ cache) {
+  using GE = Geo<D, BK, BV>;
+  constexpr int P = D / 2, M = 16 * RB, NS = D / 16;
+  constexpr int KROW = P + 1;  // dwords per token row of the key tile (odd: fewer conflicts)
+  constexpr int VROW = 33;     // dwords per feature row of the value tile (64 tokens + pad)
+  constexpr int PROW = 33;     // dwords per row of the probability tile
+  constexpr int TILEW = 64 * KROW > D * VROW ? 64 * KROW : D * VROW;
+  constexpr int MERGEW = M * D + 2 * M;  // a wave's (acc, max, sum) for the merge
+  constexpr int WAVEW = TILEW > MERGEW ? TILEW : MERGEW;
+  constexpr int NKT = 1 << BK, NVT = 1 << BV;
+  static_assert(M * D <= WAVEW, "rotated queries are staged in the first wave's space");
+  __shared__ float2 lut_k[NKT], lut_v[NVT];
+  __shared__ __align__(16) uint32_t s_wave[kMqWaves][WAVEW];
+  __shared__ uint32_t s_p[kMqWaves][M * PROW];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
+  const int b = bk / a.hkv, kvh = bk % a.hkv;
+  const int G = a.group, NQ = a.nq, MR = NQ * G;  // real rows (row = query * G + head)
+  const int seq_len = a.seq_len;
+  const int tile_begin = split * a.tiles_per_split;
+  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
+
+  for (int c = tid; c < NKT; c += kMqWaves * 64) {
+    float sn = 0.f, co = 0.f;
+    if (c < a.n_k) sincospif(2.0f * (float)c / (float)a.n_k, &sn, &co);
+    lut_k[c] = make_float2(co, sn);
+  }
+  for (int c = tid; c < NVT; c += kMqWaves * 64) {
+    float sn = 0.f, co = 0.f;
+    if (c < a.n_v) sincospif(2.0f * (float)c / (float)a.n_v, &sn, &co);
+    lut_v[c] = make_float2(co, sn);
+  }
+  // rotated queries (times softmax scale * log2 e) as fp32 [M][D]; padding rows zero
+  float* s_q = reinterpret_cast<float*>(s_wave[0]);
+  for (int row = wave; row < M; row += kMqWaves) {
+    float2 v = make_float2(0.f, 0.f);
+    if (row < MR) {
+      const size_t qoff = (((size_t)b * NQ + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
+      v = rotate_query<D>(a, qoff, min(lane, P - 1));
+    }
+    if (lane < P) reinterpret_cast<float2*>(s_q)[row * P + lane] = v;
+  }
+  __syncthreads();
+  h4 qa[RB][NS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float4 f = *reinterpret_cast<const float4*>(s_q + (16 * rb + l16) * D + 16 * s + 4 * g4);
+      qa[rb][s] = h4{(_Float16)f.x, (_Float16)f.y, (_Float16)f.z, (_Float16)f.w};
+    }
+  // tokens visible to each accumulator row of this lane (0 for padding rows)
+  int lim[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * rb + 4 * g4 + r;
+      lim[rb][r] = row < MR ? seq_len - NQ + row / G + 1 : 0;
+    }
+  __syncthreads();  // the query staging space becomes the first wave's tile space
+
+  f4 o[RB][NS];
+  float m_run[RB][4], l_run[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) o[rb][s] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_run[rb][r] = -INFINITY;
+      l_run[rb][r] = 0.f;
+    }
+  }
+  uint32_t* kb = s_wave[wave];
+  uint32_t* pb = s_p[wave];
+  const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
+  const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
+
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kMqWaves) {
+    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(base + (size_t)tile * GE::BYTES);
+    uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8];
+#pragma unroll
+    for (int w = 0; w < GE::WKA; ++w) ka[w] = w32[w * kTile + lane];
+#pragma unroll
+    for (int w = 0; w < GE::WKR; ++w) kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
+    const uint16_t ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
+    const uint32_t vp = w32[GE::OFF_VP / 4 + lane];
+#pragma unroll
+    for (int w = 0; w < 2 * BV; ++w) va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
+    const bool tvalid = tile * kTile + lane < seq_len;
+
+    // ---- key tile K^[token][feature] (fp16, rotated domain, radius s / 255 * code)
+    {
+      const float ksc = tvalid ? __half2float(__ushort_as_half(ks)) * (1.0f / 255.0f) : 0.f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const float2 cs = lut_k[field<BK>(ka, i)];
+        const float r = (float)((kr[i >> 2] >> (8 * (i & 3))) & 0xFFu) * ksc;
+        kb[lane * KROW + i] = pack_h2(r * cs.x, r * cs.y);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- scores S = q~ K^T: fragment [rb][blk] holds rows 16 rb + 4 g4 + r, token
+    // 16 blk + l16
+    f4 sc[RB][4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      h4 kv[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kv[s] = h4_from(kb + (16 * blk + l16) * KROW + 8 * s + 2 * g4);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[rb][s], kv[s], acc, 0, 0, 0);
+        sc[rb][blk] = acc;
+      }
+    }
+
+    // ---- online softmax per row (base 2); probabilities to LDS as fp16 [row][token]
+    _Float16* ph = reinterpret_cast<_Float16*>(pb);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[4], mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const int t = tile * kTile + 16 * blk + l16;
+          v[blk] = t < lim[rb][r] ? sc[rb][blk][r] : -INFINITY;
+          mx = fmaxf(mx, v[blk]);
+        }
+        mx = row16_max(mx);
+        const float mnew = fmaxf(m_run[rb][r], mx);
+        const bool none = mnew == -INFINITY;  // no visible token yet
+        const float alpha = none ? 1.f : fast_exp2(m_run[rb][r] - mnew);
+        float ps = 0.f;
+        const int row = 16 * rb + 4 * g4 + r;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const float p = none ? 0.f : fast_exp2(v[blk] - mnew);
+          ps += p;
+          ph[row * (2 * PROW) + 16 * blk + l16] = (_Float16)p;
+        }
+        l_run[rb][r] = l_run[rb][r] * alpha + ps;
+        m_run[rb][r] = mnew;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) o[rb][s][r] *= alpha;
+      }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- value tile V^[feature][token] in the key tile's space (its reads are done):
+    // lane = pair; the token's radius parameters come from lane t by readlane
+    {
+      float r0 = 0.f, beta = 0.f;
+      {
+        const float smin = __half2float(__ushort_as_half((uint16_t)(vp & 0xFFFFu)));
+        const float smax = __half2float(__ushort_as_half((uint16_t)(vp >> 16)));
+        r0 = smax;
+        if (smax > smin) {
+          r0 = smin;
+          beta = (__log2f(smax) - __log2f(smin)) * (1.0f / 15.0f);
+        }
+        if (!tvalid) {
+          r0 = 0.f;
+          beta = 0.f;
+        }
+      }
+      const bool store = lane < P;
+      float x0 = 0.f, y0 = 0.f;
+#pragma unroll
+      for (int t = 0; t < kTile; ++t) {
+        const float r0t = readlane_f(r0, t), bt = readlane_f(beta, t);
+        const uint32_t nib = (vr[t >> 3] >> (4 * (t & 7))) & 0xFu;
+        const float rr = r0t * fast_exp2((float)nib * bt);
+        const float2 cs = lut_v[field<BV>(va, t)];
+        const float x = rr * cs.x, y = rr * cs.y;
+        if (t & 1) {
+          if (store) {
+            kb[(2 * vi) * VROW + (t >> 1)] = pack_h2(x0, x);
+            kb[(2 * vi + 1) * VROW + (t >> 1)] = pack_h2(y0, y);
+          }
+        } else {
+          x0 = x;
+          y0 = y;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- O += P V^
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      h4 pa[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) pa[rb] = h4_from(pb + (16 * rb + l16) * PROW + 8 * k4 + 2 * g4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const h4 vb = h4_from(kb + (16 * s + l16) * VROW + 8 * k4 + 2 * g4);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][s] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[rb], vb, o[rb][s], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the waves: each writes (acc [M][D], max [M], sum [M]) to its space
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_run[rb][r] = row16_sum(l_run[rb][r]);
+  __syncthreads();
+  float* mine = reinterpret_cast<float*>(s_wave[wave]);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mine[(16 * rb + 4 * g4 + r) * D + 16 * s + l16] = o[rb][s][r];
+  if (l16 == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mine[M * D + 16 * rb + 4 * g4 + r] = m_run[rb][r];
+        mine[M * D + M + 16 * rb + 4 * g4 + r] = l_run[rb][r];
+      }
+  }
+  __syncthreads();
+  const bool single = a.nsplit == 1;
+  float* s_out = reinterpret_cast<float*>(s_p);  // normalised rows when single: [M][D]
+  static_assert(M * D <= kMqWaves * M * PROW, "output staging fits the probability space");
+  for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
+    const int row = idx / D, e = idx % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w)
+      mm = fmaxf(mm, reinterpret_cast<const float*>(s_wave[w])[M * D + row]);
+    float ll = 0.f, aa = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kMqWaves; ++w) {
+        const float* f = reinterpret_cast<const float*>(s_wave[w]);
+        const float c = fast_exp2(f[M * D + row] - mm);  // 0 for a wave that saw nothing
+        ll += f[M * D + M + row] * c;
+        aa += f[row * D + e] * c;
+      }
+    }
+    if (single) {
+      s_out[idx] = aa / ll;
+    } else {
+      const size_t rowi = ((size_t)bk * a.nsplit + split) * M + row;
+      __hip_atomic_store(a.part_acc + rowi * D + e, aa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (e == 0) {
+        __hip_atomic_store(a.part_ml + 2 * rowi, mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.part_ml + 2 * rowi + 1, ll, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (!single) {
+    // the last workgroup of this (batch, kv head) to finish combines the splits; the
+    // partials are written and read with device-coherent accesses, so completion of the
+    // stores is all the ordering needed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned t = __hip_atomic_fetch_add(a.tickets + bk, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_SYSTEM);
+      s_flag = t == (unsigned)(a.nsplit - 1);
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
+      const int row = idx / D, e = idx % D;
+      float mm = -INFINITY, ll = 0.f, aa = 0.f;
+      for (int sp = 0; sp < a.nsplit; ++sp) {
+        const size_t rowi = ((size_t)bk * a.nsplit + sp) * M + row;
+        const float mv = __hip_atomic_load(a.part_ml + 2 * rowi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (mv == -INFINITY) continue;  // this split saw no token of the row
+        const float lv = __hip_atomic_load(a.part_ml + 2 * rowi + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float av = __hip_atomic_load(a.part_acc + rowi * D + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float mnew = fmaxf(mm, mv);
+        const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv - mnew);
+        ll = ll * c0 + lv * c1;
+        aa = aa * c0 + av * c1;
+        mm = mnew;
+      }
+      s_out[idx] = aa / ll;
+    }
+    if (tid == 0)
+      __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+  // inverse transform and sign per output row (one wave per row, lane = pair)
+  for (int row = wave; row < MR; row += kMqWaves) {
+    if (lane < P) {
+      const float2 v = reinterpret_cast<const float2*>(s_out)[row * P + lane];
+      const size_t ooff = (((size_t)b * NQ + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
+      store_output<D>(a, ooff, lane, v.x, v.y);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* cache,
+                             hipStream_t stream) {
+  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv)), block(kMqWaves * 64);
+  const int rb = rows <= 16 ? 1 : 2;
+#define KVQ_MQ(D_, BK_, BV_, RB_)                                                             \
+  if (d == D_ && a.bk == BK_ && a.bv == BV_ && rb == RB_) {                                   \
+    hipLaunchKernelGGL((attn_multi_kernel<D_, BK_, BV_, RB_>), grid, block, 0, stream, a, cache); \
+    return hipGetLastError();                                                                 \
+  }
+#define KVQ_MQ_BV(D_, BK_, RB_) KVQ_MQ(D_, BK_, 6, RB_) KVQ_MQ(D_, BK_, 7, RB_) KVQ_MQ(D_, BK_, 8, RB_)
+#define KVQ_MQ_BK(D_, RB_) KVQ_MQ_BV(D_, 6, RB_) KVQ_MQ_BV(D_, 7, RB_) KVQ_MQ_BV(D_, 8, RB_)
+  KVQ_MQ_BK(64, 1)
+  KVQ_MQ_BK(64, 2)
+  KVQ_MQ_BK(128, 1)
+  KVQ_MQ_BK(128, 2)
+#undef KVQ_MQ_BK
+#undef KVQ_MQ_BV
+#undef KVQ_MQ
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -92,6 +92,7 @@ struct AttnArgs {
   float* part_ml;      // [B, Hq, nsplit, 2]
   float* part_acc;     // [B, Hq, nsplit, d]
   const unsigned* seq_lens;  // [B] per-entry lengths (device), or null: seq_len for all
+  int nq;                    // query tokens per sequence (multi-query attention; else 1)
 };
 
 // Bytes of the per-workgroup key-score table (pairs x 2^bk codes x heads x fp32) and
@@ -100,5 +101,8 @@ constexpr int kKeyTableMaxBytes = 128 * 1024;
 inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (1L << bk) * group * 4; }
 
 hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache, hipStream_t stream);
+// rows = nq * group query rows per kv head (at most 32)
+hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* cache,
+                             hipStream_t stream);
 
 }  // namespace kvq

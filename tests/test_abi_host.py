@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 3
+    assert kvq.abi_version() == 4
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -190,3 +190,26 @@ def test_append_validation():
     assert _app(desc, sh=-2) == INVALID
     assert _app(kvq.make_desc(256, 8, 1, 128, 128, 64)) == UNSUPPORTED
     assert lib.kvq_append(None, FAKE, FAKE, FAKE, 0, 0, 0, FAKE, None) == INVALID
+
+
+def _multi(desc, hq=32, nq=4, seq=100, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, cache=FAKE):
+    return lib.kvq_attn_multi(ctypes.byref(desc), cache, q, 0, hq, nq, seq, 0.0, out, 0, ws,
+                              ws_bytes, None)
+
+
+def test_attention_multi_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    assert _multi(desc, nq=0) == INVALID
+    assert _multi(desc, nq=101, seq=100) == INVALID  # more queries than cached tokens
+    assert _multi(desc, seq=257) == CAPACITY
+    assert _multi(desc, hq=36) == INVALID
+    assert _multi(desc, hq=24) == UNSUPPORTED  # G = 3
+    assert _multi(desc, nq=9) == UNSUPPORTED  # 9 * 4 rows > 32
+    assert _multi(desc, ws=None) == WORKSPACE
+    need = kvq.attn_multi_workspace_bytes(desc, 32, 4, 100)
+    assert need > 0
+    assert _multi(desc, ws_bytes=need - 1) == WORKSPACE
+    assert _multi(desc, cache=FAKE + 4) == INVALID
+    assert _multi(desc, q=FAKE + 2) == INVALID
+    assert _multi(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
+    assert kvq.attn_multi_workspace_bytes(desc, 32, 9, 100) == 0
