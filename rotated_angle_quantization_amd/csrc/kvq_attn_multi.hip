@@ -137,19 +137,36 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
   const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
 
-  for (int tile = tile_begin + wave; tile < tile_end; tile += kMqWaves) {
+  // The planes of this wave's next tile are loaded while the current one is processed
+  // (one wave per SIMD here, so nothing else would hide the load latency).
+  struct Planes {
+    uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8], ks, vp;
+  };
+  auto load_planes = [&](Planes& t, int tile) {
     const uint32_t* w32 = reinterpret_cast<const uint32_t*>(base + (size_t)tile * GE::BYTES);
-    uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8];
 #pragma unroll
-    for (int w = 0; w < GE::WKA; ++w) ka[w] = w32[w * kTile + lane];
+    for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
 #pragma unroll
-    for (int w = 0; w < GE::WKR; ++w) kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
-    const uint16_t ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
-    const uint32_t vp = w32[GE::OFF_VP / 4 + lane];
+    for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
+    t.ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
+    t.vp = w32[GE::OFF_VP / 4 + lane];
 #pragma unroll
-    for (int w = 0; w < 2 * BV; ++w) va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
+    for (int w = 0; w < 2 * BV; ++w) t.va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
+    for (int w = 0; w < 8; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
+  };
+  Planes nxt;
+  if (tile_begin + wave < tile_end) load_planes(nxt, tile_begin + wave);
+
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kMqWaves) {
+    const Planes cur = nxt;
+    if (tile + kMqWaves < tile_end) load_planes(nxt, tile + kMqWaves);
+    const uint32_t(&ka)[GE::WKA] = cur.ka;
+    const uint32_t(&kr)[GE::WKR] = cur.kr;
+    const uint32_t(&va)[2 * BV] = cur.va;
+    const uint32_t(&vr)[8] = cur.vr;
+    const uint16_t ks = (uint16_t)cur.ks;
+    const uint32_t vp = cur.vp;
     const bool tvalid = tile * kTile + lane < seq_len;
 
     // ---- key tile K^[token][feature] (fp16, rotated domain, radius s / 255 * code)
