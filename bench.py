@@ -7,7 +7,9 @@ One step = the whole path over one batch of synthetic input, all layers:
   dequant  packed cache -> fp16 K/V (kvq_decode), every layer
 After the timed steps, a ragged-batch decode loop is timed on the same caches (append one
 token per sequence at its own slot, attend with per-sequence lengths) and reported under
-`decode_loop`. Inputs and caches are resident in HBM before timing starts. `value` is decode-attention
+`decode_loop`; multi-query attention (kvq_attn_multi, several query tokens per sequence
+on the matrix cores) is timed on them last and reported under `multi_query`. Inputs and
+caches are resident in HBM before timing starts. `value` is decode-attention
 throughput in GB/s of compressed cache read per second over the attention phase of a
 step (all layers, every launch and gap included). Phase times come from HIP events on
 the stream the library launches on. Each attention launch (the dominant kernel) is
@@ -211,6 +213,49 @@ def decode_loop(kvq, cfg, descs, caches, ws, dev, iters=8):
     }
 
 
+def multi_query(kvq, cfg, descs, caches, dev, nqs=(4, 8), reps=5):
+    """Multi-query attention (kvq_attn_multi) on the resident caches: NQ query tokens per
+    sequence attending causally over the full context, every layer; HIP events."""
+    import torch
+
+    L, B, T, Hkv, Hq, d = cfg.layers, cfg.batch, cfg.seq, cfg.hkv, cfg.hq, cfg.d
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    res = {}
+    for nq in nqs:
+        if nq * (Hq // Hkv) > 32:
+            continue
+        q = torch.randn((B, nq, Hq, d), generator=gen, device=dev).half()
+        out = torch.empty_like(q)
+        ws = torch.zeros(max(kvq.attn_multi_workspace_bytes(dd, Hq, nq, T) for dd in descs),
+                         dtype=torch.uint8, device=dev)
+
+        def sweep():
+            for layer in range(L):
+                kvq.attn_multi(descs[layer], caches[layer], q, T, workspace=ws, out=out)
+
+        sweep()
+        torch.cuda.synchronize()
+        e0, e1 = Ev(), Ev()
+        e0.record()
+        for _ in range(reps):
+            sweep()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * L)
+        nbytes = sum(record_bytes(d, *cfg.bins(x), B * Hkv * T) for x in range(L)) / L
+        flops = 2 * 2 * B * Hq * nq * T * d  # scores and value sum, per layer
+        res[f"nq{nq}"] = {
+            "rows_per_kv_head": nq * (Hq // Hkv),
+            "us_per_layer": round(us, 2),
+            "cache_GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "mfma_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+            "mfma_frac_of_fp16_dense_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
+        }
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,6 +332,7 @@ def main():
     wall = time.perf_counter() - t_start
 
     loop = decode_loop(kvq, cfg, descs, caches, ws, dev)
+    mq = multi_query(kvq, cfg, descs, caches, dev)
 
     enc_ms = sum(e[0].elapsed_time(e[1]) for e, _ in recs) / args.steps
     att_ms = sum(e[1].elapsed_time(e[2]) for e, _ in recs) / args.steps
@@ -327,6 +373,7 @@ def main():
         "dequant_out_GBps": round(2 * L * B * T * Hkv * d * 2 / (deq_ms * 1e-3) / 1e9, 2),
         "wall_s_timed": round(wall, 3),
         "decode_loop": loop,
+        "multi_query": mq,
         "roofline": {
             "kernel": "attn_decode_kernel (kvq_attn_decode)",
             "bound": "hbm",
