@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -260,6 +260,57 @@ kvq_status kvq_attn_multi(const kvq_layer_desc* desc, const void* cache, const v
                           kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t num_queries,
                           uint32_t seq_len, float softmax_scale, void* out, kvq_dtype out_dtype,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Paged caches. A paged layer keeps its tiles in a pool of pages shared by all
+ * sequences, laid out [page][kv_head][tile_bytes] (one page = one 64-slot tile of every
+ * kv head), and a page table maps tile t of sequence b to page
+ * page_table[b * pages_per_seq + t]. Sequences then grow page by page without a
+ * contiguous reservation, and a page can be dropped from attention by mapping it to no
+ * page. The codes and bytes of a tile are exactly those of the contiguous layout. (The
+ * pages describe the codec and its attention, not how cache memory is handed out: this
+ * layout is the usual serving one, a pool of pages plus a table per sequence.)
+ * page_table: device int32 array [batch][pages_per_seq], 4-byte aligned, read by the
+ *   kernels on the given stream. An entry outside [0, num_pages) maps its tile to no
+ *   page: encode and append write nothing there, dequantisation returns zero vectors
+ *   for its slots, attention treats its slots as absent (a sequence with no present
+ *   slot gives a zero output).
+ * pages_per_seq >= ceil(capacity / 64); num_pages >= 1 (pages in the pool).
+ * Each *_paged call is its contiguous counterpart with the cache argument replaced by
+ * (pool, paging); arguments and errors are as documented there, plus INVALID_ARGUMENT
+ * for a null or misaligned paging description.
+ */
+typedef struct {
+  const int32_t* page_table;
+  uint32_t pages_per_seq;
+  uint32_t num_pages;
+} kvq_paging;
+
+/* Bytes of a pool of num_pages pages for this layer (0 if the descriptor is invalid). */
+size_t kvq_paged_pool_bytes(const kvq_layer_desc* desc, uint32_t num_pages);
+
+kvq_status kvq_encode_paged(const kvq_layer_desc* desc, void* pool, const kvq_paging* paging,
+                            const void* k, const void* v, kvq_dtype in_dtype, int64_t stride_b,
+                            int64_t stride_t, int64_t stride_h, uint32_t t0, uint32_t ntok,
+                            void* hip_stream);
+
+kvq_status kvq_append_paged(const kvq_layer_desc* desc, void* pool, const kvq_paging* paging,
+                            const void* k, const void* v, kvq_dtype in_dtype, int64_t stride_b,
+                            int64_t stride_h, const uint32_t* positions, void* hip_stream);
+
+kvq_status kvq_decode_paged(const kvq_layer_desc* desc, const void* pool,
+                            const kvq_paging* paging, void* k_out, void* v_out,
+                            kvq_dtype out_dtype, uint32_t t0, uint32_t ntok, void* hip_stream);
+
+/* Decode attention over a paged cache; seq_lens may be null (every sequence attends to
+ * max_seq_len tokens) or a device array of per-sequence lengths as for
+ * kvq_attn_decode_varlen. Workspace as kvq_attn_decode at seq_len = max_seq_len. */
+kvq_status kvq_attn_decode_paged(const kvq_layer_desc* desc, const void* pool,
+                                 const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
+                                 uint32_t num_q_heads, const uint32_t* seq_lens,
+                                 uint32_t max_seq_len, float softmax_scale, void* out,
+                                 kvq_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole

@@ -40,6 +40,13 @@ class LayerDesc(ctypes.Structure):
                 f"layer={self.layer}, seed={self.seed})")
 
 
+class Paging(ctypes.Structure):
+    """kvq_paging: page table (device int32 [batch][pages_per_seq]) of a paged cache."""
+
+    _fields_ = [("page_table", ctypes.c_void_p), ("pages_per_seq", ctypes.c_uint32),
+                ("num_pages", ctypes.c_uint32)]
+
+
 class KvqError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -68,6 +75,15 @@ _SIGS = {
                                        ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_decode_varlen": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _v, _u32, _f32,
                                               _v, ctypes.c_int, _v, _sz, _v]),
+    "kvq_paged_pool_bytes": (_sz, [_P, _u32]),
+    "kvq_encode_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, _v, ctypes.c_int, _i64,
+                                        _i64, _i64, _u32, _u32, _v]),
+    "kvq_append_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, _v, ctypes.c_int, _i64,
+                                        _i64, _v, _v]),
+    "kvq_decode_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, _v, ctypes.c_int, _u32,
+                                        _u32, _v]),
+    "kvq_attn_decode_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, ctypes.c_int, _u32,
+                                             _v, _u32, _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi_workspace_bytes": (_sz, [_P, _u32, _u32, _u32]),
     "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
                                       ctypes.c_int, _v, _sz, _v]),
@@ -258,6 +274,70 @@ def attn_multi(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: i
                               _dtype_code(q), hq, nq, seq_len, float(softmax_scale),
                               out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
                               workspace.numel(), _stream(q.device)), "kvq_attn_multi")
+    return out
+
+
+def paged_pool_bytes(desc: LayerDesc, num_pages: int) -> int:
+    return lib.kvq_paged_pool_bytes(ctypes.byref(desc), num_pages)
+
+
+def make_paging(page_table: torch.Tensor, num_pages: int) -> Paging:
+    """page_table: contiguous int32 device tensor [batch, pages_per_seq]. The tensor must
+    stay alive while calls that use the returned description are in flight."""
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 tensor [batch, pages_per_seq]")
+    return Paging(page_table.data_ptr(), page_table.shape[1], num_pages)
+
+
+def encode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.Tensor,
+                 v: torch.Tensor, t0: int = 0):
+    if k.dim() != 4 or k.stride(3) != 1 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k/v must be [B, ntok, Hkv, d] with d contiguous and equal strides")
+    _check(lib.kvq_encode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
+                                k.data_ptr(), v.data_ptr(), _dtype_code(k), k.stride(0),
+                                k.stride(1), k.stride(2), t0, k.shape[1], _stream(pool.device)),
+           "kvq_encode_paged")
+
+
+def append_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.Tensor,
+                 v: torch.Tensor, positions: torch.Tensor):
+    if k.dim() == 4 and k.shape[1] == 1:
+        k, v = k[:, 0], v[:, 0]
+    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
+    _check(lib.kvq_append_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
+                                k.data_ptr(), v.data_ptr(), _dtype_code(k), k.stride(0),
+                                k.stride(1), positions.data_ptr(), _stream(pool.device)),
+           "kvq_append_paged")
+
+
+def decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, t0: int, ntok: int,
+                 out_dtype=torch.float16):
+    shape = (desc.batch, ntok, desc.num_kv_heads, desc.head_dim)
+    k_out = torch.empty(shape, dtype=out_dtype, device=pool.device)
+    v_out = torch.empty(shape, dtype=out_dtype, device=pool.device)
+    _check(lib.kvq_decode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
+                                k_out.data_ptr(), v_out.data_ptr(), _dtype_code(k_out), t0, ntok,
+                                _stream(pool.device)), "kvq_decode_paged")
+    return k_out, v_out
+
+
+def attn_decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, q: torch.Tensor,
+                      max_seq_len: int, seq_lens: torch.Tensor | None = None,
+                      softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None):
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    lens = seq_lens.data_ptr() if seq_lens is not None else None
+    _check(lib.kvq_attn_decode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
+                                     q.data_ptr(), _dtype_code(q), hq, lens, max_seq_len,
+                                     float(softmax_scale), out.data_ptr(), _dtype_code(out),
+                                     workspace.data_ptr(), workspace.numel(), _stream(q.device)),
+           "kvq_attn_decode_paged")
     return out
 
 

@@ -71,6 +71,7 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
   a.sign = sign_mask(d->seed, d->layer, d->head_dim);
   a.positions = nullptr;
   a.capacity = (int)d->capacity;
+  a.pg = Paging{nullptr, 0, 0};
   return a;
 }
 
@@ -173,12 +174,13 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->part_acc = (float*)(base + l.acc);
   a->seq_lens = nullptr;
   a->nq = 1;
+  a->pg = Paging{nullptr, 0, 0};
   return KVQ_OK;
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const void* q,
+kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg, const void* q,
                     kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, const uint32_t* seq_lens,
                     float scale, void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
                     void* stream) {
@@ -195,6 +197,7 @@ kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const void* q,
   a.out = out;
   a.out_f32 = out_dtype == KVQ_F32;
   a.seq_lens = seq_lens;
+  a.pg = pg;
   return hip_status(
       launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
 }
@@ -246,6 +249,71 @@ MultiLayout multi_layout(const kvq_layer_desc* d, uint32_t rows, int nsplit) {
   return l;
 }
 
+const Paging kNoPaging = {nullptr, 0, 0};
+
+kvq_status paging_args(const kvq_layer_desc* d, const kvq_paging* p, Paging* out) {
+  if (!desc_ok(d) || !p || !p->page_table || ((uintptr_t)p->page_table % 4))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (p->num_pages == 0 || p->num_pages > 0x7fffffffu) return KVQ_ERR_INVALID_ARGUMENT;
+  if (p->pages_per_seq < (uint32_t)tiles_per_seq(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  out->table = p->page_table;
+  out->pages_per_seq = (int)p->pages_per_seq;
+  out->num_pages = (int)p->num_pages;
+  return KVQ_OK;
+}
+
+kvq_status encode_impl(const kvq_layer_desc* d, void* cache, const Paging& pg, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t sb, int64_t st, int64_t sh, uint32_t t0,
+                      uint32_t ntok, void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !k || !v || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  CodecArgs a = codec_args(d, t0, ntok);
+  a.pg = pg;
+  return hip_status(launch_encode(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
+                                  in_dtype == KVQ_F32, sb, st, sh, (hipStream_t)stream));
+}
+
+kvq_status append_impl(const kvq_layer_desc* d, void* cache, const Paging& pg, const void* k, const void* v,
+                      kvq_dtype in_dtype, int64_t sb, int64_t sh, const uint32_t* positions,
+                      void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (!cache || !k || !v || !positions || ((uintptr_t)cache % 16) || ((uintptr_t)positions % 4))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (sh & 1) || sb < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  CodecArgs a = codec_args(d, 0, 1);
+  a.positions = positions;
+  a.pg = pg;
+  return hip_status(launch_append(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
+                                  in_dtype == KVQ_F32, sb, sh, (hipStream_t)stream));
+}
+
+kvq_status decode_impl(const kvq_layer_desc* d, const void* cache, const Paging& pg, void* k_out, void* v_out,
+                      kvq_dtype out_dtype, uint32_t t0, uint32_t ntok, void* stream) {
+  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != KVQ_F16 && out_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !k_out || !v_out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)k_out % 16) || ((uintptr_t)v_out % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  CodecArgs a = codec_args(d, t0, ntok);
+  a.pg = pg;
+  return hip_status(launch_decode(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
+                                  k_out, v_out, out_dtype == KVQ_F32, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -286,50 +354,50 @@ kvq_status kvq_layer_signs(uint64_t seed, uint32_t layer, uint32_t d, int8_t* ou
 kvq_status kvq_encode(const kvq_layer_desc* d, void* cache, const void* k, const void* v,
                       kvq_dtype in_dtype, int64_t sb, int64_t st, int64_t sh, uint32_t t0,
                       uint32_t ntok, void* stream) {
-  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
-  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
-  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
-  if (ntok == 0) return KVQ_OK;
-  if (!cache || !k || !v || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
-  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
-  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0)
-    return KVQ_ERR_INVALID_ARGUMENT;
-  const CodecArgs a = codec_args(d, t0, ntok);
-  return hip_status(launch_encode(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
-                                  in_dtype == KVQ_F32, sb, st, sh, (hipStream_t)stream));
+  return encode_impl(d, cache, kNoPaging, k, v, in_dtype, sb, st, sh, t0, ntok, stream);
 }
 
 kvq_status kvq_append(const kvq_layer_desc* d, void* cache, const void* k, const void* v,
                       kvq_dtype in_dtype, int64_t sb, int64_t sh, const uint32_t* positions,
                       void* stream) {
-  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
-  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
-  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
-  if (!cache || !k || !v || !positions || ((uintptr_t)cache % 16) || ((uintptr_t)positions % 4))
-    return KVQ_ERR_INVALID_ARGUMENT;
-  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
-  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((sb & 1) || (sh & 1) || sb < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
-  CodecArgs a = codec_args(d, 0, 1);
-  a.positions = positions;
-  return hip_status(launch_append(a, (int)d->head_dim, geom_of(d), (uint8_t*)cache, k, v,
-                                  in_dtype == KVQ_F32, sb, sh, (hipStream_t)stream));
+  return append_impl(d, cache, kNoPaging, k, v, in_dtype, sb, sh, positions, stream);
 }
 
 kvq_status kvq_decode(const kvq_layer_desc* d, const void* cache, void* k_out, void* v_out,
                       kvq_dtype out_dtype, uint32_t t0, uint32_t ntok, void* stream) {
-  if (!desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
-  if (out_dtype != KVQ_F16 && out_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
-  if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
-  if (ntok == 0) return KVQ_OK;
-  if (!cache || !k_out || !v_out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)k_out % 16) || ((uintptr_t)v_out % 16)) return KVQ_ERR_INVALID_ARGUMENT;
-  const CodecArgs a = codec_args(d, t0, ntok);
-  return hip_status(launch_decode(a, (int)d->head_dim, geom_of(d), (const uint8_t*)cache,
-                                  k_out, v_out, out_dtype == KVQ_F32, (hipStream_t)stream));
+  return decode_impl(d, cache, kNoPaging, k_out, v_out, out_dtype, t0, ntok, stream);
+}
+
+size_t kvq_paged_pool_bytes(const kvq_layer_desc* d, uint32_t num_pages) {
+  if (!desc_ok(d)) return 0;
+  return (size_t)num_pages * d->num_kv_heads * kvq_tile_bytes(d->head_dim, d->n_bins_k, d->n_bins_v);
+}
+
+kvq_status kvq_encode_paged(const kvq_layer_desc* d, void* pool, const kvq_paging* paging,
+                            const void* k, const void* v, kvq_dtype in_dtype, int64_t sb,
+                            int64_t st, int64_t sh, uint32_t t0, uint32_t ntok, void* stream) {
+  Paging pg;
+  const kvq_status st0 = paging_args(d, paging, &pg);
+  if (st0 != KVQ_OK) return st0;
+  return encode_impl(d, pool, pg, k, v, in_dtype, sb, st, sh, t0, ntok, stream);
+}
+
+kvq_status kvq_append_paged(const kvq_layer_desc* d, void* pool, const kvq_paging* paging,
+                            const void* k, const void* v, kvq_dtype in_dtype, int64_t sb,
+                            int64_t sh, const uint32_t* positions, void* stream) {
+  Paging pg;
+  const kvq_status st0 = paging_args(d, paging, &pg);
+  if (st0 != KVQ_OK) return st0;
+  return append_impl(d, pool, pg, k, v, in_dtype, sb, sh, positions, stream);
+}
+
+kvq_status kvq_decode_paged(const kvq_layer_desc* d, const void* pool, const kvq_paging* paging,
+                            void* k_out, void* v_out, kvq_dtype out_dtype, uint32_t t0,
+                            uint32_t ntok, void* stream) {
+  Paging pg;
+  const kvq_status st0 = paging_args(d, paging, &pg);
+  if (st0 != KVQ_OK) return st0;
+  return decode_impl(d, pool, pg, k_out, v_out, out_dtype, t0, ntok, stream);
 }
 
 uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
@@ -350,8 +418,8 @@ kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const voi
                            kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, float scale,
                            void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
                            void* stream) {
-  return attn_run(d, cache, q, q_dtype, hq, seq_len, nullptr, scale, out, out_dtype, ws,
-                  ws_bytes, stream);
+  return attn_run(d, cache, kNoPaging, q, q_dtype, hq, seq_len, nullptr, scale, out, out_dtype,
+                  ws, ws_bytes, stream);
 }
 
 kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* d, const void* cache, const void* q,
@@ -364,8 +432,21 @@ kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* d, const void* cache, co
     const kvq_status st = attn_check(d, hq, max_seq_len);
     return st != KVQ_OK ? st : KVQ_ERR_INVALID_ARGUMENT;
   }
-  return attn_run(d, cache, q, q_dtype, hq, max_seq_len, seq_lens, scale, out, out_dtype, ws,
-                  ws_bytes, stream);
+  return attn_run(d, cache, kNoPaging, q, q_dtype, hq, max_seq_len, seq_lens, scale, out,
+                  out_dtype, ws, ws_bytes, stream);
+}
+
+kvq_status kvq_attn_decode_paged(const kvq_layer_desc* d, const void* pool,
+                                 const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
+                                 uint32_t hq, const uint32_t* seq_lens, uint32_t max_seq_len,
+                                 float scale, void* out, kvq_dtype out_dtype, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (seq_lens && ((uintptr_t)seq_lens % 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  Paging pg;
+  const kvq_status st0 = paging_args(d, paging, &pg);
+  if (st0 != KVQ_OK) return st0;
+  return attn_run(d, pool, pg, q, q_dtype, hq, max_seq_len, seq_lens, scale, out, out_dtype,
+                  ws, ws_bytes, stream);
 }
 
 size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t nq,

@@ -243,10 +243,29 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, ntiles);
+  // Tile addresses (wave-uniform): tile t sits at base + t * stride in a contiguous
+  // cache, at base + page * stride with page = table[t] in a paged pool. A tile the
+  // table maps to no page reads page 0 and counts as holding no token.
+  const int* ptab = nullptr;
   const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
+  size_t stride = GE::BYTES;
+  if (a.pg.table) {
+    const int b = bk / a.hkv;
+    ptab = a.pg.table + (size_t)b * a.pg.pages_per_seq;
+    base = cache + (size_t)(bk - b * a.hkv) * GE::BYTES;
+    stride = (size_t)a.hkv * GE::BYTES;
+  }
   TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
-  load_tile_keys(cur, base + (size_t)min(tile, tile_end - 1) * GE::BYTES, lane);
+  {
+    const int t0 = min(tile, tile_end - 1);
+    int idx = t0;
+    if (ptab) {
+      const int page = ptab[t0];
+      idx = page >= 0 && page < a.pg.num_pages ? page : 0;
+    }
+    load_tile_keys(cur, base + idx * stride, lane);
+  }
   if (KT) {
     const float2 qv = rotate_query_pair<D>(a, qraw, lane);
     if (wave < G && lane < P) reinterpret_cast<float2*>(s_q)[wave * P + lane] = qv;
@@ -313,9 +332,19 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     // No register double-buffering: several waves per SIMD cover each other's load
     // latency, and the value planes are only requested once the scores are done, which
     // keeps the register count low enough for that occupancy.
-    const uint8_t* tp = base + (size_t)tile * GE::BYTES;
+    bool present = true;
+    int idx = tile;
+    if (ptab) {
+      const int page = ptab[tile];
+      present = page >= 0 && page < a.pg.num_pages;
+      idx = present ? page : 0;
+    }
+    const uint8_t* tp = base + idx * stride;
     if (tile != tile_begin + wave) load_tile_keys(cur, tp, lane);
-    const int nvalid = min(seq_len - tile * kTile, kTile);
+    // opaque to the compiler, which otherwise specialises the whole tile body on an
+    // absent tile and runs out of registers
+    int nvalid = present ? min(seq_len - tile * kTile, kTile) : 0;
+    asm volatile("" : "+s"(nvalid));
     const bool valid = lane < nvalid;
 
     // ---- keys: lane = token slot
@@ -400,7 +429,8 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       const float s = valid ? sc[g] * kscale : -INFINITY;
       {
         const float mnew = fmaxf(m[g], wave_max(s));
-        const float alpha = fast_exp2(m[g] - mnew);
+        // no token seen yet (only tiles of absent pages): nothing to rescale
+        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[g] - mnew);
         l[g] *= alpha;
 #pragma unroll
         for (int j = 0; j < PPL; ++j) {
@@ -409,7 +439,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
         }
         m[g] = mnew;
       }
-      const float pv = fast_exp2(s - m[g]);
+      const float pv = m[g] == -INFINITY ? 0.f : fast_exp2(s - m[g]);
       l[g] += pv;
       pr[g] = pv * r0;
     }
@@ -509,12 +539,12 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     float ll = 0.f, aa = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(s_ml[(w * G + g) * 2] - mm);
+      const float f = mm == -INFINITY ? 0.f : fast_exp2(s_ml[(w * G + g) * 2] - mm);
       ll += s_ml[(w * G + g) * 2 + 1] * f;
       aa += s_acc[(w * G + g) * D + e] * f;
     }
     if (single) {
-      s_q[idx] = aa / ll;
+      s_q[idx] = ll > 0.f ? aa / ll : 0.f;  // no token at all: zero output
     } else {
       // device-coherent stores (they bypass the non-coherent caches, so no cache
       // write-back is needed before another workgroup reads them)
@@ -574,7 +604,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (s0 + u < nsplit) {  // every split covers a valid token, so m is finite
+        if (s0 + u < nsplit && mv[u] != -INFINITY) {  // skip splits that saw no token
           const float mnew = fmaxf(mm, mv[u]);
           const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv[u] - mnew);
           ll = ll * c0 + lv[u] * c1;
@@ -583,7 +613,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
         }
       }
     }
-    s_q[idx] = aa / ll;
+    s_q[idx] = ll > 0.f ? aa / ll : 0.f;
   }
   __syncthreads();
   if (wave < G && lane < P) {

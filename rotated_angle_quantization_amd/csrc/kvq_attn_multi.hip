@@ -134,16 +134,19 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
   }
   uint32_t* kb = s_wave[wave];
   uint32_t* pb = s_p[wave];
-  const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * GE::BYTES;
   const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
 
   // The planes of this wave's next tile are loaded while the current one is processed
   // (one wave per SIMD here, so nothing else would hide the load latency).
+  // A tile the page table maps to no page reads page 0 and counts as holding no token.
   struct Planes {
     uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8], ks, vp;
+    bool present;
   };
   auto load_planes = [&](Planes& t, int tile) {
-    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(base + (size_t)tile * GE::BYTES);
+    const long long off = tile_offset(a.pg, b, kvh, a.hkv, a.tiles_per_seq, tile, GE::BYTES);
+    t.present = off >= 0;
+    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(cache + (off >= 0 ? off : 0));
 #pragma unroll
     for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
 #pragma unroll
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
     const uint32_t(&vr)[8] = cur.vr;
     const uint16_t ks = (uint16_t)cur.ks;
     const uint32_t vp = cur.vp;
-    const bool tvalid = tile * kTile + lane < seq_len;
+    const bool tvalid = cur.present && tile * kTile + lane < seq_len;
 
     // ---- key tile K^[token][feature] (fp16, rotated domain, radius s / 255 * code)
     {
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
           const int t = tile * kTile + 16 * blk + l16;
-          v[blk] = t < lim[rb][r] ? sc[rb][blk][r] : -INFINITY;
+          v[blk] = cur.present && t < lim[rb][r] ? sc[rb][blk][r] : -INFINITY;
           mx = fmaxf(mx, v[blk]);
         }
         mx = row16_max(mx);
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
       }
     }
     if (single) {
-      s_out[idx] = aa / ll;
+      s_out[idx] = ll > 0.f ? aa / ll : 0.f;
     } else {
       const size_t rowi = ((size_t)bk * a.nsplit + split) * M + row;
       __hip_atomic_store(a.part_acc + rowi * D + e, aa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
         aa = aa * c0 + av * c1;
         mm = mnew;
       }
-      s_out[idx] = aa / ll;
+      s_out[idx] = ll > 0.f ? aa / ll : 0.f;
     }
     if (tid == 0)
       __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

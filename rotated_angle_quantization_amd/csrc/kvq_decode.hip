@@ -85,18 +85,27 @@ __global__ __launch_bounds__(256) void decode_kernel(CodecArgs a, TileGeom g,
   }
   // Tiles are taken in grid-stride order; pre holds the next tile's bytes.
   const size_t tile_bytes = (size_t)g.bytes;
-  auto tile_ptr = [&](int t) {
+  // A tile the page table maps to no page decodes as all-zero bytes (zero vectors).
+  (void)tile_bytes;
+  auto tile_ptr = [&](int t) -> const u32x4* {
     const int tile_rel = t % a.tiles_touched, bh = t / a.tiles_touched;
-    return reinterpret_cast<const u32x4*>(
-        cache + ((size_t)bh * a.tiles_per_seq + a.tile_lo + tile_rel) * tile_bytes);
+    const long long off = tile_offset(a.pg, bh / a.hkv, bh % a.hkv, a.hkv, a.tiles_per_seq,
+                                      a.tile_lo + tile_rel, g.bytes);
+    return off >= 0 ? reinterpret_cast<const u32x4*>(cache + off) : nullptr;
+  };
+  auto fetch = [&](u32x4 (&dstv)[NV4], int t) {
+    const u32x4* tp = tile_ptr(t);
+    if (tp) {
+#pragma unroll
+      for (int s = 0; s < NV4; ++s) dstv[s] = tp[src[s]];
+    } else {
+#pragma unroll
+      for (int s = 0; s < NV4; ++s) dstv[s] = u32x4{0u, 0u, 0u, 0u};
+    }
   };
   u32x4 pre[NV4];
   int task = blockIdx.x;
-  if (task < ntasks) {
-    const u32x4* tp = tile_ptr(task);
-#pragma unroll
-    for (int s = 0; s < NV4; ++s) pre[s] = tp[src[s]];
-  }
+  if (task < ntasks) fetch(pre, task);
 
   // Angle tables hold (cos + sin, cos - sin) of 2 pi c / n: the transform's first
   // stage (element stride 1) combines the two components of each pair.
@@ -157,11 +166,7 @@ __global__ __launch_bounds__(256) void decode_kernel(CodecArgs a, TileGeom g,
 #pragma unroll
     for (int s = 0; s < NV4; ++s) stage[dst[s]] = pre[s];
     __syncthreads();
-    if (task + (int)gridDim.x < ntasks) {
-      const u32x4* tp = tile_ptr(task + (int)gridDim.x);
-#pragma unroll
-      for (int s = 0; s < NV4; ++s) pre[s] = tp[src[s]];
-    }
+    if (task + (int)gridDim.x < ntasks) fetch(pre, task + (int)gridDim.x);
 
     const int tile_rel = task % a.tiles_touched, bh = task / a.tiles_touched;
     const int b = bh / a.hkv, h = bh % a.hkv;

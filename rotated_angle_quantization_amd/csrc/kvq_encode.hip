@@ -301,8 +301,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int tile = a.tile_lo + tile_rel;
   const int tok_base = tile * kTile;
+  // a tile the page table maps to no page is not written
+  const long long toff = live ? tile_offset(a.pg, b, h, a.hkv, a.tiles_per_seq, tile, g.bytes) : -1;
   const int j_lo = max(a.t0 - tok_base, 0);
-  const int j_hi = live ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
+  const int j_hi = toff >= 0 ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
 
   // Lane q of a token's quad owns the 8-element chunks m*4 + q (elements
   // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   }
   __syncthreads();
 
-  uint8_t* tp = cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * (size_t)g.bytes;
+  uint8_t* tp = cache + (toff >= 0 ? toff : 0);
 
   // Key planes and per-token parameters: one lane per token slot; slots outside the
   // range are not written (their words belong to them alone).
@@ -584,7 +586,9 @@ __global__ __launch_bounds__(64) void append_kernel(CodecArgs a, TileGeom g,
   const unsigned pos = a.positions[b];
   if (pos >= (unsigned)a.capacity) return;  // nothing to write for this sequence
   const int tile = (int)pos / kTile, t = (int)pos % kTile;
-  uint8_t* tp = cache + ((size_t)bh * a.tiles_per_seq + tile) * (size_t)g.bytes;
+  const long long toff = tile_offset(a.pg, b, h, a.hkv, a.tiles_per_seq, tile, g.bytes);
+  if (toff < 0) return;  // the page table maps this tile to no page
+  uint8_t* tp = cache + toff;
   const int i = lane & (P - 1);  // pair
   const bool store = lane < P;
   const int e0 = 2 * i;

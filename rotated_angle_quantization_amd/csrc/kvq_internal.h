@@ -51,6 +51,24 @@ struct SignMask {
   uint64_t w[4];
 };
 
+// Optional page table: tile t of sequence b of a paged cache lives in page
+// table[b * pages_per_seq + t] of a pool laid out [page][kv head][tile bytes]. Without a
+// table the cache is contiguous, [batch][kv head][tile][tile bytes].
+struct Paging {
+  const int* table;  // null: contiguous cache
+  int pages_per_seq, num_pages;
+};
+
+// Byte offset of tile `tile` of (sequence b, kv head h), or -1 when the page table maps
+// it to no page of the pool (an entry outside [0, num_pages)).
+__host__ __device__ __attribute__((always_inline)) inline long long tile_offset(
+    Paging pg, int b, int h, int hkv, int tiles_per_seq, int tile, int bytes) {
+  if (!pg.table) return ((long long)(b * hkv + h) * tiles_per_seq + tile) * bytes;
+  const int page = pg.table[(long long)b * pg.pages_per_seq + tile];
+  if (page < 0 || page >= pg.num_pages) return -1;
+  return ((long long)page * hkv + h) * bytes;
+}
+
 // Runtime parameters of one encode/decode launch.
 struct CodecArgs {
   int batch, hkv, tiles_per_seq;
@@ -63,6 +81,7 @@ struct CodecArgs {
   SignMask sign;
   const unsigned* positions;  // append: [B] slot of each sequence's new token
   int capacity;               // tokens per sequence
+  Paging pg;
 };
 
 hipError_t launch_append(const CodecArgs& a, int d, TileGeom geom, uint8_t* cache,
@@ -93,6 +112,7 @@ struct AttnArgs {
   float* part_acc;     // [B, Hq, nsplit, d]
   const unsigned* seq_lens;  // [B] per-entry lengths (device), or null: seq_len for all
   int nq;                    // query tokens per sequence (multi-query attention; else 1)
+  Paging pg;
 };
 
 // Bytes of the per-workgroup key-score table (pairs x 2^bk codes x heads x fp32) and

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 4
+    assert kvq.abi_version() == 5
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -213,3 +213,23 @@ def test_attention_multi_validation():
     assert _multi(desc, q=FAKE + 2) == INVALID
     assert _multi(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
     assert kvq.attn_multi_workspace_bytes(desc, 32, 9, 100) == 0
+
+
+def test_paged_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)  # 4 tiles per sequence
+    pg = kvq.Paging(FAKE, 4, 10)
+    enc = lambda paging, **kw: lib.kvq_encode_paged(ctypes.byref(desc), kw.get("pool", FAKE),
+                                                    paging, FAKE, FAKE, 0, 0, 0, 0, 0, 1, None)
+    assert enc(None) == INVALID
+    assert enc(ctypes.byref(kvq.Paging(None, 4, 10))) == INVALID
+    assert enc(ctypes.byref(kvq.Paging(FAKE + 2, 4, 10))) == INVALID  # int32 table alignment
+    assert enc(ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID  # fewer pages than tiles
+    assert enc(ctypes.byref(kvq.Paging(FAKE, 4, 0))) == INVALID  # empty pool
+    assert enc(ctypes.byref(pg), pool=FAKE + 8) == INVALID
+    assert lib.kvq_attn_decode_paged(ctypes.byref(desc), FAKE, ctypes.byref(pg), FAKE, 0, 32,
+                                     FAKE + 2, 100, 0.0, FAKE, 0, FAKE, 1 << 30, None) == INVALID
+    assert lib.kvq_attn_decode_paged(ctypes.byref(desc), FAKE, None, FAKE, 0, 32, None, 100,
+                                     0.0, FAKE, 0, FAKE, 1 << 30, None) == INVALID
+    assert lib.kvq_decode_paged(ctypes.byref(desc), FAKE, ctypes.byref(pg), FAKE, FAKE, 0, 0, 0,
+                                None) == OK  # nothing to do
+    assert kvq.paged_pool_bytes(desc, 10) == 10 * 8 * kvq.tile_bytes(128, 128, 64)
