@@ -201,15 +201,43 @@ def decode_loop(kvq, cfg, descs, caches, ws, dev, iters=8):
     att_us = sum(ev[1].elapsed_time(ev[2]) for _, _, ev in recs) * 1e3 / len(recs)
     att_bytes = sum(record_bytes(d, *cfg.bins(layer), Hkv * (sum(lens0) + B * (i + 1)))
                     for layer, i, _ in recs) / len(recs)
+
+    # the same steps with the append fused into the attention launch (rewriting the same
+    # tokens into the same slots)
+    def run_fused(record):
+        for i in range(iters):
+            for layer in range(L):
+                ev = (Ev(), Ev()) if record is not None else None
+                if ev:
+                    ev[0].record()
+                kvq.attn_decode_append(descs[layer], caches[layer], new_k, new_v, pos[i], qd, T,
+                                       workspace=ws, out=out)
+                if ev:
+                    ev[1].record()
+                    record.append(ev)
+
+    run_fused(None)
+    torch.cuda.synchronize()
+    frecs = []
+    f0, f1 = Ev(), Ev()
+    f0.record()
+    run_fused(frecs)
+    f1.record()
+    torch.cuda.synchronize()
+    fused_ms = f0.elapsed_time(f1)
+    fused_us = sum(e[0].elapsed_time(e[1]) for e in frecs) * 1e3 / len(frecs)
     return {
         "what": "per layer: kvq_append of one token per sequence at its own slot, then "
-                "kvq_attn_decode_varlen over each sequence's length",
+                "kvq_attn_decode_varlen over each sequence's length; fused: both in one "
+                "kvq_attn_decode_append launch",
         "batch_lengths_start": lens0,
         "iterations": iters,
         "ms_per_token_all_layers": round(total_ms / iters, 4),
         "append_us_per_layer": round(app_us, 2),
         "attend_us_per_layer": round(att_us, 2),
         "attend_GBps": round(att_bytes / (att_us * 1e-6) / 1e9, 2),
+        "fused_ms_per_token_all_layers": round(fused_ms / iters, 4),
+        "fused_us_per_layer": round(fused_us, 2),
     }
 
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -311,6 +311,31 @@ kvq_status kvq_attn_decode_paged(const kvq_layer_desc* desc, const void* pool,
                                  uint32_t max_seq_len, float softmax_scale, void* out,
                                  kvq_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                  void* hip_stream);
+
+/*
+ * One decode step in one launch: kvq_append, then decode attention over the appended
+ * sequences. For every sequence b, the token with K/V rows k, v [B, Hkv, d] (element
+ * strides stride_b, stride_h; d contiguous; fp16 or fp32 as in_dtype) is coded into
+ * slot positions[b] (device uint32 array [B]) exactly as kvq_append codes it, and query
+ * q [B, Hq, d] then attends to min(positions[b] + 1, max_seq_len) tokens. The codes are
+ * those of "TurboAngle: Near-Lossless KV Cache Compression via Uniform Angle
+ * Quantization" (arXiv 2603.27467), Abstract, so the cache bytes and the output equal
+ * those of kvq_append followed by kvq_attn_decode_varlen with seq_lens = positions + 1.
+ * A slot at or past the capacity is not written (its sequence attends to max_seq_len
+ * tokens); with paging, a slot whose page is absent is not written either. The token is
+ * coded inside the attention kernel by the wave that reads its tile, while the other
+ * waves stream their tiles.
+ * paging: null for a contiguous cache, else the pool's page table as for the *_paged
+ * calls (cache is then the pool). Workspace as kvq_attn_decode at seq_len = max_seq_len.
+ * Errors: as kvq_attn_decode (max_seq_len in [1, capacity]) and kvq_append.
+ */
+kvq_status kvq_attn_decode_append(const kvq_layer_desc* desc, void* cache,
+                                  const kvq_paging* paging, const void* k, const void* v,
+                                  kvq_dtype in_dtype, int64_t stride_b, int64_t stride_h,
+                                  const uint32_t* positions, const void* q, kvq_dtype q_dtype,
+                                  uint32_t num_q_heads, uint32_t max_seq_len,
+                                  float softmax_scale, void* out, kvq_dtype out_dtype,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole

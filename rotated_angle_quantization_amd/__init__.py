@@ -7,7 +7,8 @@ Abstract. Importing this package loads libkvq.so and fails if it has not been bu
 
 from ._lib import (  # noqa: F401
     EXPORTS, KVQ_F16, KVQ_F32, KvqError, LayerDesc, Paging, abi_version, alloc_cache, append,
-    append_paged, attn_decode_paged, decode_paged, encode_paged, make_paging, paged_pool_bytes,
+    append_paged, attn_decode_append, attn_decode_paged, decode_paged, encode_paged, make_paging,
+    paged_pool_bytes,
     alloc_workspace, attn_decode, attn_decode_varlen, attn_multi, attn_multi_workspace_bytes,
     attn_num_splits,
     attn_workspace_bytes, cache_bytes, decode, default_scale, encode, layer_signs, lib,

@@ -84,6 +84,9 @@ _SIGS = {
                                         _u32, _v]),
     "kvq_attn_decode_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, ctypes.c_int, _u32,
                                              _v, _u32, _f32, _v, ctypes.c_int, _v, _sz, _v]),
+    "kvq_attn_decode_append": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, _v,
+                                              ctypes.c_int, _i64, _i64, _v, _v, ctypes.c_int,
+                                              _u32, _u32, _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi_workspace_bytes": (_sz, [_P, _u32, _u32, _u32]),
     "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
                                       ctypes.c_int, _v, _sz, _v]),
@@ -338,6 +341,39 @@ def attn_decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, q: to
                                      float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                      workspace.data_ptr(), workspace.numel(), _stream(q.device)),
            "kvq_attn_decode_paged")
+    return out
+
+
+def attn_decode_append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       positions: torch.Tensor, q: torch.Tensor, max_seq_len: int,
+                       paging: Paging | None = None, softmax_scale: float = 0.0,
+                       out_dtype=None, workspace=None, out=None):
+    """One decode step in one launch: code the token k/v [B, Hkv, d] of sequence b at slot
+    positions[b] (int32 device tensor [B]), then attend with q [B, Hq, d] over
+    min(positions[b] + 1, max_seq_len) tokens. cache is the pool when paging is given."""
+    if k.dim() == 4 and k.shape[1] == 1:
+        k, v = k[:, 0], v[:, 0]
+    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must have the same dtype")
+    if positions.dtype not in (torch.int32, torch.uint32) or not positions.is_contiguous() \
+            or positions.numel() != k.shape[0] or positions.device != k.device:
+        raise ValueError("positions must be a contiguous int32 device tensor [B] on k's device")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    pg = ctypes.byref(paging) if paging is not None else None
+    _check(lib.kvq_attn_decode_append(ctypes.byref(desc), cache.data_ptr(), pg, k.data_ptr(),
+                                      v.data_ptr(), _dtype_code(k), k.stride(0), k.stride(1),
+                                      positions.data_ptr(), q.data_ptr(), _dtype_code(q), hq,
+                                      max_seq_len, float(softmax_scale), out.data_ptr(),
+                                      _dtype_code(out), workspace.data_ptr(), workspace.numel(),
+                                      _stream(q.device)), "kvq_attn_decode_append")
     return out
 
 

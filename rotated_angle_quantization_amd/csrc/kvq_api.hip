@@ -180,10 +180,12 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+const AppendArgs kNoAppend = {nullptr, nullptr, nullptr, 0, 0, 0, 0, 0.0, 0.0, 0.0};
+
 kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg, const void* q,
                     kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, const uint32_t* seq_lens,
                     float scale, void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    void* stream, const AppendArgs& app = kNoAppend) {
   AttnArgs a;
   kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
   if (st != KVQ_OK) return st;
@@ -199,7 +201,7 @@ kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg
   a.seq_lens = seq_lens;
   a.pg = pg;
   return hip_status(
-      launch_attn_decode(a, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
+      launch_attn_decode(a, app, (int)d->head_dim, (const uint8_t*)cache, (hipStream_t)stream));
 }
 
 // Multi-query attention: rows = nq * G query rows per kv head, padded to 16 or 32.
@@ -447,6 +449,42 @@ kvq_status kvq_attn_decode_paged(const kvq_layer_desc* d, const void* pool,
   if (st0 != KVQ_OK) return st0;
   return attn_run(d, pool, pg, q, q_dtype, hq, max_seq_len, seq_lens, scale, out, out_dtype,
                   ws, ws_bytes, stream);
+}
+
+kvq_status kvq_attn_decode_append(const kvq_layer_desc* d, void* cache,
+                                  const kvq_paging* paging, const void* k, const void* v,
+                                  kvq_dtype in_dtype, int64_t sb, int64_t sh,
+                                  const uint32_t* positions, const void* q, kvq_dtype q_dtype,
+                                  uint32_t hq, uint32_t max_seq_len, float scale, void* out,
+                                  kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  // shape errors first, as in kvq_attn_decode
+  const kvq_status st = attn_check(d, hq, max_seq_len);
+  if (st != KVQ_OK) return st;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!k || !v || !positions || ((uintptr_t)positions % 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (sh & 1) || sb < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  Paging pg = kNoPaging;
+  if (paging) {
+    const kvq_status sp = paging_args(d, paging, &pg);
+    if (sp != KVQ_OK) return sp;
+  }
+  const CodecArgs c = codec_args(d, 0, 1);
+  AppendArgs app;
+  app.positions = positions;
+  app.k = k;
+  app.v = v;
+  app.sb = sb;
+  app.sh = sh;
+  app.f32 = in_dtype == KVQ_F32;
+  app.capacity = (int)d->capacity;
+  app.inv_sqrt_d = c.inv_sqrt_d;
+  app.k_bins_per_rad = c.k_bins_per_rad;
+  app.v_bins_per_rad = c.v_bins_per_rad;
+  return attn_run(d, cache, pg, q, q_dtype, hq, max_seq_len, nullptr, scale, out, out_dtype,
+                  ws, ws_bytes, stream, app);
 }
 
 size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t nq,

@@ -33,6 +33,7 @@
 // (token, pair) of a tile costs G FMAs for the score and 2G for the value sum, and a
 // wave64 FP32 FMA occupies a SIMD for four cycles on this chip.
 #include "kvq_attn_common.h"
+#include "kvq_codec_dev.h"
 
 namespace kvq {
 namespace {
@@ -185,7 +186,8 @@ constexpr int split_waves(bool key_table, int group) { return key_table && group
 // rotated query from scalar registers.
 template <int D, int G, int BK, int BV, int KTM>
 __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_kernel(
-    AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot) {
+    AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot,
+    AppendArgs app) {
   using C = SplitCfg<D, G, BK, BV>;
   using GE = typename C::GE;
   constexpr bool KT = KTM != 0, HALF = KTM == 2;
@@ -210,10 +212,14 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
   const int row = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
-  // This entry's length (per-entry lengths are clamped to the planned maximum), its
-  // tiles and the splits that cover them; a.nsplit stays the stride of the partials.
-  const int seq_len = a.seq_lens ? (int)min(a.seq_lens[bk / a.hkv], (unsigned)a.seq_len)
-                                 : a.seq_len;
+  // This entry's length (per-entry lengths are clamped to the planned maximum; with a
+  // fused append, the appended slot + 1), its tiles and the splits that cover them;
+  // a.nsplit stays the stride of the partials.
+  const bool append = app.positions != nullptr;
+  const unsigned apos = append ? app.positions[bk / a.hkv] : 0u;
+  const int seq_len = append ? (apos >= (unsigned)a.seq_len ? a.seq_len : (int)apos + 1)
+                      : a.seq_lens ? (int)min(a.seq_lens[bk / a.hkv], (unsigned)a.seq_len)
+                                   : a.seq_len;
   const int ntiles = (seq_len + kTile - 1) / kTile;
   const int nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (split >= nsplit) {
@@ -255,9 +261,23 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     base = cache + (size_t)(bk - b * a.hkv) * GE::BYTES;
     stride = (size_t)a.hkv * GE::BYTES;
   }
+  // Fused append: the appended token is coded by the wave that reads its tile (for a
+  // slot past the attended range, wave 0 of split 0), after the set-up and before that
+  // wave's first tile load. Only this workgroup reads the tile in this launch.
+  bool owner = false;
+  int app_tile = 0;
+  if (append && apos < (unsigned)app.capacity) {
+    app_tile = (int)(apos / kTile);
+    if (app_tile < ntiles) {
+      const int s = app_tile / a.tiles_per_split;
+      owner = split == s && wave == (app_tile - s * a.tiles_per_split) % NW;
+    } else {
+      owner = split == 0 && wave == 0;
+    }
+  }
   TileRegs<D, G, BK, BV> cur;
   int tile = tile_begin + wave;
-  {
+  auto first_tile_keys = [&]() {
     const int t0 = min(tile, tile_end - 1);
     int idx = t0;
     if (ptab) {
@@ -265,7 +285,8 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       idx = page >= 0 && page < a.pg.num_pages ? page : 0;
     }
     load_tile_keys(cur, base + idx * stride, lane);
-  }
+  };
+  if (!owner) first_tile_keys();
   if (KT) {
     const float2 qv = rotate_query_pair<D>(a, qraw, lane);
     if (wave < G && lane < P) reinterpret_cast<float2*>(s_q)[wave * P + lane] = qv;
@@ -312,6 +333,46 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       }
     }
     __syncthreads();
+  }
+
+  if (owner) {
+    int idx = app_tile;
+    bool present = true;
+    if (ptab) {
+      const int page = ptab[app_tile];
+      present = page >= 0 && page < a.pg.num_pages;
+      idx = page;
+    }
+    if (present) {  // a tile mapped to no page takes no write
+      const int b = bk / a.hkv, h = bk - b * a.hkv;
+      const size_t esz = app.f32 ? 4 : 2;
+      const size_t roff = ((size_t)b * app.sb + (size_t)h * app.sh) * esz;
+      CodecArgs c;
+      c.n_k = a.n_k;
+      c.n_v = a.n_v;
+      c.bk = BK;
+      c.bv = BV;
+      c.inv_sqrt_d = app.inv_sqrt_d;
+      c.k_bins_per_rad = app.k_bins_per_rad;
+      c.v_bins_per_rad = app.v_bins_per_rad;
+      c.sign = a.sign;
+      TileGeom g;
+      g.ka = 0;
+      g.kr = GE::OFF_KR;
+      g.ks = GE::OFF_KS;
+      g.va = GE::OFF_VA;
+      g.vr = GE::OFF_VR;
+      g.vp = GE::OFF_VP;
+      g.wka = GE::WKA;
+      g.wkr = GE::WKR;
+      append_token<D>(c, g, const_cast<uint8_t*>(base) + idx * stride, (int)(apos % kTile),
+                      static_cast<const char*>(app.k) + roff,
+                      static_cast<const char*>(app.v) + roff, app.f32 != 0, lane);
+      // the token's stores complete before this wave reads the tile back (waves of a
+      // workgroup share the compute unit's L1, which the stores keep current)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    first_tile_keys();
   }
 
   const int vshift = (row * kStepTokens * BV) & 31;  // 0, or 16 for odd widths
@@ -624,63 +685,67 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
 }
 
 template <int D, int G, int BK, int BV>
-hipError_t decode_launch(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_launch(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
+                    hipStream_t s) {
   constexpr long full = SplitCfg<D, G, BK, BV>::TAB_BYTES;
   if constexpr (full <= kKeyTableMaxBytes) {
     if (a.key_table == 1) {
       hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 1>), grid,
-                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
+                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot, app);
       return hipGetLastError();
     }
   }
   if constexpr (full / 2 <= kKeyTableMaxBytes) {
     if (a.key_table == 2) {
       hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 2>), grid,
-                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot);
+                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot, app);
       return hipGetLastError();
     }
   }
   if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
   hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 0>), grid,
-                     dim3(split_waves(false, G) * 64), 0, s, a, cache, a.qrot);
+                     dim3(split_waves(false, G) * 64), 0, s, a, cache, a.qrot, app);
   return hipGetLastError();
 }
 
 template <int D, int G, int BK>
-hipError_t decode_bv(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_bv(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
+                    hipStream_t s) {
   switch (a.bv) {
-    case 6: return decode_launch<D, G, BK, 6>(a, cache, grid, s);
-    case 7: return decode_launch<D, G, BK, 7>(a, cache, grid, s);
-    case 8: return decode_launch<D, G, BK, 8>(a, cache, grid, s);
+    case 6: return decode_launch<D, G, BK, 6>(a, app, cache, grid, s);
+    case 7: return decode_launch<D, G, BK, 7>(a, app, cache, grid, s);
+    case 8: return decode_launch<D, G, BK, 8>(a, app, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D, int G>
-hipError_t decode_bk(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_bk(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
+                    hipStream_t s) {
   switch (a.bk) {
-    case 6: return decode_bv<D, G, 6>(a, cache, grid, s);
-    case 7: return decode_bv<D, G, 7>(a, cache, grid, s);
-    case 8: return decode_bv<D, G, 8>(a, cache, grid, s);
+    case 6: return decode_bv<D, G, 6>(a, app, cache, grid, s);
+    case 7: return decode_bv<D, G, 7>(a, app, cache, grid, s);
+    case 8: return decode_bv<D, G, 8>(a, app, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-hipError_t decode_g(const AttnArgs& a, const uint8_t* cache, dim3 grid, hipStream_t s) {
+hipError_t decode_g(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
+                    hipStream_t s) {
   switch (a.group) {
-    case 1: return decode_bk<D, 1>(a, cache, grid, s);
-    case 2: return decode_bk<D, 2>(a, cache, grid, s);
-    case 4: return decode_bk<D, 4>(a, cache, grid, s);
-    case 8: return decode_bk<D, 8>(a, cache, grid, s);
+    case 1: return decode_bk<D, 1>(a, app, cache, grid, s);
+    case 2: return decode_bk<D, 2>(a, app, cache, grid, s);
+    case 4: return decode_bk<D, 4>(a, app, cache, grid, s);
+    case 8: return decode_bk<D, 8>(a, app, cache, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache,
-                              hipStream_t stream) {
+hipError_t launch_attn_decode(const AttnArgs& a, const AppendArgs& app, int d,
+                              const uint8_t* cache, hipStream_t stream) {
   if (d != 64 && d != 128) return hipErrorInvalidValue;
   if (!a.key_table) {
     const dim3 pgrid((unsigned)(a.batch * a.hq));
@@ -692,7 +757,8 @@ hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache,
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv));
-  return d == 64 ? decode_g<64>(a, cache, grid, stream) : decode_g<128>(a, cache, grid, stream);
+  return d == 64 ? decode_g<64>(a, app, cache, grid, stream)
+                 : decode_g<128>(a, app, cache, grid, stream);
 }
 
 }  // namespace kvq

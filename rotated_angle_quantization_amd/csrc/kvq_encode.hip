@@ -24,31 +24,11 @@
 // matching the layout's word order so every store is a coalesced dword.
 #include <hip/hip_fp16.h>
 
+#include "kvq_codec_dev.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
-
-constexpr double kFp16Max = 65504.0;
-constexpr double kFp16MinNormal = 6.103515625e-05;  // 2^-14
-constexpr double kFp16Subnormal = 5.9604644775390625e-08;  // 2^-24
-
-// Nearest fp16 value of a non-negative x <= 65504, ties to even, computed exactly in
-// binary64: the fp16 spacing at x is 2^(e-10) (2^-24 below the normal range), so
-// rint(x / q) * q rounds to 11 significant bits with no double rounding.
-__device__ __forceinline__ double pow2(int e) {  // 2^e for -1022 <= e <= 1023
-  return __longlong_as_double((long long)(e + 1023) << 52);
-}
-__device__ __forceinline__ double fp16_round_pos(double x) {
-  if (x == 0.0) return 0.0;
-  // 2^(e-10) with x in [2^e, 2^(e+1)); frexp's exponent is e + 1
-  const int e = x < kFp16MinNormal ? -14 : __builtin_amdgcn_frexp_exp(x) - 1;
-  return rint(x * pow2(10 - e)) * pow2(e - 10);  // scaling by powers of two is exact
-}
-
-__device__ __forceinline__ uint16_t fp16_bits(double exact_fp16_value) {
-  return __half_as_ushort(__float2half_rn((float)exact_fp16_value));
-}
 
 __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
   return (m.w[e >> 6] >> (e & 63)) & 1ull;
@@ -65,143 +45,6 @@ __device__ __forceinline__ double quad_xor(double v) {
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 
 constexpr int kRow = 68;  // LDS row stride (bytes) of the per-token code staging
-
-// atan(z) on [0, 1]: odd polynomial z * sum_k c_k z^2k, least-squares fitted to atan
-// (measured maximum error 2.5e-7 rad on [0, 1]; 3.5e-7 rad evaluated in fp32).
-__device__ __forceinline__ float atan01(float z) {
-  const float s = z * z;
-  float p = 0.006806020624935627f;
-  p = fmaf(p, s, -0.03358602523803711f);
-  p = fmaf(p, s, 0.07960157096385956f);
-  p = fmaf(p, s, -0.13232044875621796f);
-  p = fmaf(p, s, 0.19807438552379608f);
-  p = fmaf(p, s, -0.3331731855869293f);
-  p = fmaf(p, s, 0.9999960660934448f);
-  return p * z;
-}
-
-// Angle of a nonzero pair in fp32, by octant reduction: |error| <= 3.5e-7 (polynomial)
-// + 1.2e-7 (z = min/max through the reciprocal) + 6e-8 (rounding the pair to fp32)
-// + 2.4e-7 (the two reflections about pi/2 and pi) < 8e-7 rad. The reflections and the
-// sign use the fp32 values' sign bits (exact: rounding keeps the sign).
-__device__ __forceinline__ float angle_f32(float a, float b) {
-  const float ax = fabsf(a), ay = fabsf(b);
-  const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
-  const float p = atan01(mn * __builtin_amdgcn_rcpf(mx));
-  float t = ay > ax ? 1.5707963267948966f - p : p;
-  t = a < 0.f ? 3.141592653589793f - t : t;
-  return __builtin_copysignf(t, b);
-}
-
-// Angle code: nearest of n centres 2 pi c / n, i.e. floor(theta n / (2 pi) + 1/2) mod n;
-// 0 for a zero pair. The fp32 estimate theta32 (error < 8e-7 rad) gives the centre cf
-// and the distance to the nearest bin edge through the residual theta32 - cf * (2 pi / n)
-// (rounding of the bin width adds < 4e-7 rad). When that distance is below kAngleMargin
-// the pair is compared in binary64 with the edge's direction (bedge[k] = (cos, sin) of
-// (k + 1/2) 2 pi / n): on or past the edge means the upper bin, as the floor above gives
-// at an exact half. The estimate runs for zero pairs too (it yields NaN, which fails the
-// margin test and converts to 0) and the zero test only selects the result, so no
-// branch surrounds the common path.
-constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
-template <class Edge>  // edge(k) = (cos, sin) of (k + 1/2) 2 pi / n in binary64
-__device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
-                                          float bins_per_rad_f, float bin_rad_f,
-                                          const Edge& edge) {
-  const float th = angle_f32((float)a, (float)b);
-  const float cf = rintf(th * bins_per_rad_f);
-  const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
-  int c = (int)cf;  // in [-n/2, n/2]
-  if (__builtin_expect(0.5f * bin_rad_f - fabsf(res) < kAngleMargin, 0)) {
-    const int k = res > 0.f ? c : c - 1;  // edge between centres k and k + 1
-    const int kk = k < 0 ? k + n : (k >= n ? k - n : k);
-    const double2 e = edge(kk);
-    c = fma(e.x, b, -e.y * a) >= 0.0 ? k + 1 : k;
-  }
-  // c is in [-n/2 - 1, n/2 + 1]: wrap into [0, n) as min(c + n, c) in unsigned terms
-  const unsigned cu = (unsigned)(c + n);
-  const unsigned wrapped = min(cu, cu - (unsigned)n);
-  return zero ? 0 : (int)wrapped;
-}
-
-// Bin edge k of an n-bin codebook, (cos, sin) of (k + 1/2) 2 pi / n in binary64; the
-// encode kernel tabulates these values, the append kernel computes them when needed.
-__device__ __forceinline__ double2 bin_edge(int k, int n) {
-  double sn, co;
-  sincospi((2.0 * k + 1.0) / n, &sn, &co);
-  return make_double2(co, sn);
-}
-
-// Key scale and radius level: s = fp16(max r); level = floor(255 r / s + 1/2). Estimate
-// in fp32: hardware sqrt (<= 2 ulp) of the rounded r^2, times 255/s: relative error
-// < 4e-7, i.e. < 1.1e-4 levels with the final rounding. Within 5e-4 of a half-integer
-// the level is decided by comparing r^2 with ((m - 1/2) s / 255)^2 in binary64.
-struct KeyScale {
-  double s, s_255;
-  float sc255;
-};
-__device__ __forceinline__ KeyScale key_scale(double max_r2) {
-  KeyScale k;
-  k.s = fp16_round_pos(fmin(sqrt(max_r2), kFp16Max));
-  k.sc255 = k.s > 0.0 ? 255.0f * __builtin_amdgcn_rcpf((float)k.s) : 0.f;
-  k.s_255 = k.s * (1.0 / 255.0);
-  return k;
-}
-__device__ __forceinline__ int key_level(double r2, const KeyScale& k) {
-  int rho = 0;
-  if (k.s > 0.0) {
-    const float t = __builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f;
-    const float m = rintf(t);
-    rho = (int)floorf(t);
-    if (__builtin_expect(fabsf(t - m) < 5e-4f, 0)) {
-      const double thr = ((double)m - 0.5) * k.s_255;
-      rho = r2 >= thr * thr ? (int)m : (int)m - 1;
-    }
-    rho = min(max(rho, 0), 255);
-  }
-  return rho;
-}
-
-// Value parameters and radius level: s_max = fp16(max r), s_min = fp16(max(min r,
-// 2^-14)); level = floor(15 ln(r / s_min) / L + 1/2), L = ln(s_max / s_min). Estimate:
-// 7.5 log2f(r^2 / s_min^2) / log2(s_max / s_min) from fp32; its error is bounded by
-// (7.5 / L2) (3 * 2^-24 / ln 2 + ulp(|log2|)) plus the rounding of the sum, which the
-// margin below covers with a factor of >= 4.
-struct ValueScale {
-  double smin, smax, smin2;
-  bool spread;
-  float scale, inv_smin2;
-};
-__device__ __forceinline__ ValueScale value_scale(double max_r2, double min_r2) {
-  ValueScale v;
-  v.smax = fp16_round_pos(fmin(sqrt(max_r2), kFp16Max));
-  v.smin = fp16_round_pos(fmin(fmax(sqrt(min_r2), kFp16MinNormal), kFp16Max));
-  v.spread = v.smax > v.smin;
-  v.smin2 = v.smin * v.smin;
-  // log2(s_max / s_min) from the fp32 ratio (s_max, s_min are fp16 values, exact in
-  // fp32): error < 4e-7 absolute
-  const float l2f =
-      v.spread ? __log2f((float)v.smax * __builtin_amdgcn_rcpf((float)v.smin)) : 1.f;
-  v.scale = 7.5f * __builtin_amdgcn_rcpf(l2f);
-  v.inv_smin2 = __builtin_amdgcn_rcpf((float)v.smin2);
-  return v;
-}
-__device__ __forceinline__ int value_level(double r2, const ValueScale& v) {
-  int rho = 0;
-  if (v.spread && r2 >= v.smin2) {
-    // lr = log2(r^2 / s_min^2) <= 2 l2; t = 7.5 lr / l2 + 1/2. With absolute errors
-    // <= 7e-7 (lr) and 4e-7 (l2), |dt| <= 7.5 (7e-7 + 2 * 4e-7) / l2 plus ~1e-6 of fp32
-    // rounding; the margin below is more than twice that.
-    const float lr = __log2f((float)r2 * v.inv_smin2);
-    const float t = lr * v.scale + 0.5f;
-    const float fl = floorf(t);
-    const float margin = v.scale * (4e-6f + 1e-6f * fabsf(lr)) + 2e-5f;
-    rho = (int)fl;
-    if (__builtin_expect(fminf(t - fl, fl + 1.0f - t) < margin, 0))
-      rho = (int)floor(15.0 * log(sqrt(r2) / v.smin) / log(v.smax / v.smin) + 0.5);
-    rho = min(max(rho, 0), 15);
-  }
-  return rho;
-}
 
 // NC codes of width B (one per byte, four per dword in cw) as an LSB-first bit string
 // of NC * B / 32 words, word w stored at dst[w * stride].
@@ -533,54 +376,15 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   }
 }
 
-// Exchange of a double with lane (lane ^ mask) of the wave.
-__device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
-  return __shfl_xor(v, mask, 64);
-}
-
-// Maximum / minimum over the lanes of groups of 2^k consecutive lanes (masks < group).
-template <int GROUP>
-__device__ __forceinline__ double group_max(double x) {
-#pragma unroll
-  for (int m = 1; m < GROUP; m <<= 1) x = fmax(x, shfl_xor_f64(x, m));
-  return x;
-}
-template <int GROUP>
-__device__ __forceinline__ double group_min(double x) {
-#pragma unroll
-  for (int m = 1; m < GROUP; m <<= 1) x = fmin(x, shfl_xor_f64(x, m));
-  return x;
-}
-
-// Transform stage across lanes: the pair held by this lane is combined with the pair of
-// lane ^ mask; the lane whose bit is clear keeps low + high, the other low - high (the
-// operations of the encode kernel's stages, so the results are the same doubles).
-__device__ __forceinline__ void lane_stage(double& y0, double& y1, int lane, int mask) {
-  const double p0 = shfl_xor_f64(y0, mask), p1 = shfl_xor_f64(y1, mask);
-  if (lane & mask) {
-    y0 = p0 - y0;
-    y1 = p1 - y1;
-  } else {
-    y0 = y0 + p0;
-    y1 = y1 + p1;
-  }
-}
-
 // Append: one token per sequence, each at its own slot (positions[b]). One wave per
-// (batch, kv head); lane i owns pair i (elements 2i, 2i + 1), so one token's coding is
-// spread over the wave: a decode step waits for this kernel's latency, not its
-// throughput. The transform stages run in the encode kernel's order (element strides
-// 1, 2, 4, 32, 64, then 8, 16) with the same operations, and the decisions call the same
-// functions, so the codes and bytes are those of the encode kernel. For d = 64 the upper
-// 32 lanes repeat the lower 32 and do not store.
+// (batch, kv head) runs the one-token append, so a decode step waits for this kernel's
+// latency, not its throughput.
 template <int D, bool F32IN>
 __global__ __launch_bounds__(64) void append_kernel(CodecArgs a, TileGeom g,
                                                     uint8_t* __restrict__ cache,
                                                     const void* __restrict__ kin,
                                                     const void* __restrict__ vin, int64_t sb,
                                                     int64_t sh) {
-  constexpr int P = D / 2;
-  __shared__ __align__(4) uint8_t s_kc[P], s_kr[P];
   const int lane = threadIdx.x;
   const int bh = blockIdx.x, b = bh / a.hkv, h = bh % a.hkv;
   const unsigned pos = a.positions[b];
@@ -588,109 +392,10 @@ __global__ __launch_bounds__(64) void append_kernel(CodecArgs a, TileGeom g,
   const int tile = (int)pos / kTile, t = (int)pos % kTile;
   const long long toff = tile_offset(a.pg, b, h, a.hkv, a.tiles_per_seq, tile, g.bytes);
   if (toff < 0) return;  // the page table maps this tile to no page
-  uint8_t* tp = cache + toff;
-  const int i = lane & (P - 1);  // pair
-  const bool store = lane < P;
-  const int e0 = 2 * i;
-  const uint64_t sw = e0 < 64 ? a.sign.w[0] : a.sign.w[1];  // d <= 128
-  const bool neg0 = (sw >> (e0 & 63)) & 1ull, neg1 = (sw >> ((e0 + 1) & 63)) & 1ull;
-  const int64_t off = (int64_t)b * sb + (int64_t)h * sh + e0;
-
-  // both rows are loaded before either is coded
-  float x[2][2];
-#pragma unroll
-  for (int kv = 0; kv < 2; ++kv) {
-    const void* src = kv == 0 ? kin : vin;
-    if (F32IN) {
-      const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(src) + off);
-      x[kv][0] = f.x;
-      x[kv][1] = f.y;
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const __half*>(src) + off);
-      x[kv][0] = __half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
-      x[kv][1] = __half2float(__ushort_as_half((uint16_t)(w >> 16)));
-    }
-  }
-  const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;
-  const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
-
-#pragma unroll
-  for (int kv = 0; kv < 2; ++kv) {
-    double y0 = (double)(neg0 ? -x[kv][0] : x[kv][0]);
-    double y1 = (double)(neg1 ? -x[kv][1] : x[kv][1]);
-    // element stride 1 in-lane, then strides 2, 4 (lane bits 0, 1), 32, 64 (lane bits
-    // 4, 5), 8, 16 (lane bits 2, 3)
-    {
-      const double u = y0, v = y1;
-      y0 = u + v;
-      y1 = u - v;
-    }
-    lane_stage(y0, y1, lane, 1);
-    lane_stage(y0, y1, lane, 2);
-    lane_stage(y0, y1, lane, 16);
-    if (D == 128) lane_stage(y0, y1, lane, 32);
-    lane_stage(y0, y1, lane, 4);
-    lane_stage(y0, y1, lane, 8);
-    y0 *= a.inv_sqrt_d;
-    y1 *= a.inv_sqrt_d;
-    const double r2 = fma(y1, y1, y0 * y0);
-    const double mx = group_max<P>(fmax(0.0, r2));
-
-    if (kv == 0) {
-      const KeyScale ksc = key_scale(mx);
-      const int nk = a.n_k;
-      const auto edge = [&](int e) { return bin_edge(e, nk); };
-      const int c = angle_code(y0, y1, r2 == 0.0, nk, kbpr, kbin, edge);
-      const int rho = key_level(r2, ksc);
-      if (store) {
-        s_kc[i] = (uint8_t)c;
-        s_kr[i] = (uint8_t)rho;
-      }
-      __syncthreads();
-      // key angle words: word w of the slot's bit string holds pairs with bits in
-      // [32w, 32w + 32)
-      if (lane < g.wka) {
-        const int w = lane, lo = 32 * w;
-        uint32_t acc = 0;
-        for (int p = lo / a.bk; p < P && p * a.bk < lo + 32; ++p) {
-          const int s = p * a.bk - lo;
-          const uint32_t cp = s_kc[p];
-          acc |= s >= 0 ? cp << s : cp >> -s;
-        }
-        reinterpret_cast<uint32_t*>(tp + g.ka)[w * kTile + t] = acc;
-      }
-      if (lane < g.wkr)
-        reinterpret_cast<uint32_t*>(tp + g.kr)[lane * kTile + t] =
-            reinterpret_cast<const uint32_t*>(s_kr)[lane];
-      if (lane == 0) reinterpret_cast<uint16_t*>(tp + g.ks)[t] = fp16_bits(ksc.s);
-    } else {
-      const double mn = group_min<P>(r2);
-      const ValueScale vsc = value_scale(mx, mn);
-      const int nv = a.n_v;
-      const auto edge = [&](int e) { return bin_edge(e, nv); };
-      const uint32_t c = (uint32_t)angle_code(y0, y1, r2 == 0.0, nv, vbpr, vbin, edge);
-      const uint32_t rho = (uint32_t)value_level(r2, vsc);
-      if (store) {
-        // this slot's bits in pair i's strings; the other slots' bits are kept
-        uint32_t* va = reinterpret_cast<uint32_t*>(tp + g.va);
-        const int bit = t * a.bv, w0 = bit >> 5, s0 = bit & 31;
-        const uint32_t mask = (1u << a.bv) - 1u;
-        uint32_t* d0 = va + w0 * P + i;
-        *d0 = (*d0 & ~(mask << s0)) | (c << s0);
-        if (s0 + a.bv > 32) {
-          uint32_t* d1 = va + (w0 + 1) * P + i;
-          const int hb = s0 + a.bv - 32;  // bits in the next word
-          *d1 = (*d1 & ~((1u << hb) - 1u)) | (c >> (32 - s0));
-        }
-        uint32_t* vr = reinterpret_cast<uint32_t*>(tp + g.vr) + (t >> 3) * P + i;
-        const int ns = 4 * (t & 7);
-        *vr = (*vr & ~(0xFu << ns)) | (rho << ns);
-      }
-      if (lane == 0)
-        reinterpret_cast<uint32_t*>(tp + g.vp)[t] =
-            (uint32_t)fp16_bits(vsc.smin) | ((uint32_t)fp16_bits(vsc.smax) << 16);
-    }
-  }
+  const int64_t off = (int64_t)b * sb + (int64_t)h * sh;
+  const size_t esz = F32IN ? 4 : 2;
+  append_token<D>(a, g, cache + toff, t, static_cast<const char*>(kin) + off * esz,
+                  static_cast<const char*>(vin) + off * esz, F32IN, lane);
 }
 
 }  // namespace

@@ -120,7 +120,23 @@ struct AttnArgs {
 constexpr int kKeyTableMaxBytes = 128 * 1024;
 inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (1L << bk) * group * 4; }
 
-hipError_t launch_attn_decode(const AttnArgs& a, int d, const uint8_t* cache, hipStream_t stream);
+// Fused append of decode attention: the new token of sequence b (K/V rows at
+// k / v + b * sb + h * sh elements, d contiguous) is coded into slot positions[b] before
+// that slot's tile is read; the sequence attends to min(positions[b] + 1, seq_len)
+// tokens. positions == null: no append. (A kernel argument of its own: enlarging
+// AttnArgs past a couple of hundred bytes costs the kernels without a key table their
+// scalar query loads.)
+struct AppendArgs {
+  const unsigned* positions;
+  const void* k;
+  const void* v;
+  int64_t sb, sh;
+  int f32, capacity;
+  double inv_sqrt_d, k_bins_per_rad, v_bins_per_rad;  // the layer's encode constants
+};
+
+hipError_t launch_attn_decode(const AttnArgs& a, const AppendArgs& app, int d,
+                              const uint8_t* cache, hipStream_t stream);
 // rows = nq * group query rows per kv head (at most 32)
 hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* cache,
                              hipStream_t stream);

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 5
+    assert kvq.abi_version() == 6
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -233,3 +233,32 @@ def test_paged_validation():
     assert lib.kvq_decode_paged(ctypes.byref(desc), FAKE, ctypes.byref(pg), FAKE, FAKE, 0, 0, 0,
                                 None) == OK  # nothing to do
     assert kvq.paged_pool_bytes(desc, 10) == 10 * 8 * kvq.tile_bytes(128, 128, 64)
+
+
+def _fused(desc, cache=FAKE, paging=None, k=FAKE, v=FAKE, dtype=0, sb=0, sh=0, pos=FAKE, q=FAKE,
+           hq=32, maxlen=100, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.kvq_attn_decode_append(ctypes.byref(desc), cache, paging, k, v, dtype, sb, sh, pos,
+                                      q, 0, hq, maxlen, 0.0, out, 0, ws, ws_bytes, None)
+
+
+def test_fused_append_attention_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    assert _fused(desc, pos=None) == INVALID
+    assert _fused(desc, pos=FAKE + 2) == INVALID
+    assert _fused(desc, k=None) == INVALID
+    assert _fused(desc, k=FAKE + 2) == INVALID
+    assert _fused(desc, dtype=1, v=FAKE + 4) == INVALID
+    assert _fused(desc, dtype=7) == INVALID
+    assert _fused(desc, sb=5) == INVALID
+    assert _fused(desc, sh=-2) == INVALID
+    assert _fused(desc, maxlen=0) == INVALID
+    assert _fused(desc, maxlen=257) == CAPACITY
+    assert _fused(desc, pos=None, maxlen=257) == CAPACITY  # shape errors first
+    assert _fused(desc, hq=24) == UNSUPPORTED
+    assert _fused(desc, ws=None) == WORKSPACE
+    assert _fused(desc, ws_bytes=kvq.attn_workspace_bytes(desc, 32, 100) - 1) == WORKSPACE
+    assert _fused(desc, cache=FAKE + 4) == INVALID
+    assert _fused(desc, q=None) == INVALID
+    assert _fused(desc, paging=ctypes.byref(kvq.Paging(None, 4, 10))) == INVALID
+    assert _fused(desc, paging=ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
+    assert _fused(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
