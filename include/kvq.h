@@ -337,6 +337,15 @@ kvq_status kvq_attn_decode_append(const kvq_layer_desc* desc, void* cache,
                                   float softmax_scale, void* out, kvq_dtype out_dtype,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Multi-query attention over a paged cache: kvq_attn_multi with the cache replaced by
+ * (pool, paging); tokens of tiles mapped to no page are left out of every query's
+ * softmax (a query that sees no present token gives a zero row). */
+kvq_status kvq_attn_multi_paged(const kvq_layer_desc* desc, const void* pool,
+                                const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
+                                uint32_t num_q_heads, uint32_t num_queries, uint32_t seq_len,
+                                float softmax_scale, void* out, kvq_dtype out_dtype,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole
  * number of 64-token tiles. */

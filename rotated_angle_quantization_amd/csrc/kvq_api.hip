@@ -495,10 +495,14 @@ size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint
   return multi_layout(d, nq * (hq / d->num_kv_heads), nsplit).total;
 }
 
-kvq_status kvq_attn_multi(const kvq_layer_desc* d, const void* cache, const void* q,
-                          kvq_dtype q_dtype, uint32_t hq, uint32_t nq, uint32_t seq_len,
-                          float scale, void* out, kvq_dtype out_dtype, void* ws,
-                          size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& pg,
+                     const void* q, kvq_dtype q_dtype, uint32_t hq, uint32_t nq,
+                     uint32_t seq_len, float scale, void* out, kvq_dtype out_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
   kvq_status st = multi_check(d, hq, nq, seq_len);
   if (st != KVQ_OK) return st;
   int nsplit, tps;
@@ -539,8 +543,33 @@ kvq_status kvq_attn_multi(const kvq_layer_desc* d, const void* cache, const void
   a.part_ml = (float*)(base + l.ml);
   a.part_acc = (float*)(base + l.acc);
   a.seq_lens = nullptr;
+  a.pg = pg;
   return hip_status(launch_attn_multi(a, (int)d->head_dim, (int)(nq * g), (const uint8_t*)cache,
                                       (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_attn_multi(const kvq_layer_desc* d, const void* cache, const void* q,
+                          kvq_dtype q_dtype, uint32_t hq, uint32_t nq, uint32_t seq_len,
+                          float scale, void* out, kvq_dtype out_dtype, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return multi_run(d, cache, kNoPaging, q, q_dtype, hq, nq, seq_len, scale, out, out_dtype, ws,
+                   ws_bytes, stream);
+}
+
+kvq_status kvq_attn_multi_paged(const kvq_layer_desc* d, const void* pool,
+                                const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
+                                uint32_t hq, uint32_t nq, uint32_t seq_len, float scale,
+                                void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                                void* stream) {
+  Paging pg;
+  const kvq_status st0 = paging_args(d, paging, &pg);
+  if (st0 != KVQ_OK) return st0;
+  return multi_run(d, pool, pg, q, q_dtype, hq, nq, seq_len, scale, out, out_dtype, ws,
+                   ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -233,6 +233,12 @@ def test_paged_validation():
     assert lib.kvq_decode_paged(ctypes.byref(desc), FAKE, ctypes.byref(pg), FAKE, FAKE, 0, 0, 0,
                                 None) == OK  # nothing to do
     assert kvq.paged_pool_bytes(desc, 10) == 10 * 8 * kvq.tile_bytes(128, 128, 64)
+    multi = lambda paging, **kw: lib.kvq_attn_multi_paged(
+        ctypes.byref(desc), FAKE, paging, FAKE, 0, 32, kw.get("nq", 4), 100, 0.0, FAKE, 0, FAKE,
+        1 << 30, None)
+    assert multi(None) == INVALID
+    assert multi(ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
+    assert multi(ctypes.byref(pg), nq=0) == INVALID
 
 
 def _fused(desc, cache=FAKE, paging=None, k=FAKE, v=FAKE, dtype=0, sb=0, sh=0, pos=FAKE, q=FAKE,

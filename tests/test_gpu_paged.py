@@ -124,3 +124,38 @@ def test_pages_mapped_to_no_page(dev):
     # only tile 3 of sequence 1 is present among the targets (tile 3 of sequence 0,
     # tile 0 of sequence 1 and all of sequence 2 map to no page)
     assert changed == [int(holes[1, 3])], changed
+
+
+def test_paged_multi_query(dev):
+    """Multi-query attention over a pool equals the contiguous call bit for bit; with
+    pages removed, every query attends to the present tokens it may see (oracle)."""
+    desc, tiles, num_pages, table, k, v, _ = setup(dev, seed=6)
+    cont = torch.zeros(kvq.cache_bytes(desc), dtype=torch.uint8, device=dev)
+    kvq.encode(desc, cont, k, v, 0)
+    pool = scatter(cont, desc, tiles, table, num_pages)
+    nq, g = 4, 4
+    q = torch.randn(desc.batch, nq, desc.num_kv_heads * g, desc.head_dim, device=dev).half()
+    for n in (1000, 130):
+        ref = kvq.attn_multi(desc, cont, q, n, out_dtype=torch.float32)
+        got = kvq.attn_multi(desc, pool, q, n, out_dtype=torch.float32,
+                             paging=kvq.make_paging(table, num_pages))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), n
+    holes = table.clone()
+    holes[0, 2] = -1          # tokens 128..191 of sequence 0
+    holes[1, 15] = -1         # the tile holding sequence 1's last tokens (960..999)
+    out = kvq.attn_multi(desc, pool, q, 1000, out_dtype=torch.float32,
+                         paging=kvq.make_paging(holes, num_pages))
+    torch.cuda.synchronize()
+    got = unpack(cont.cpu().numpy(), 128, 128, 64, 3, 2, 1000, 0, 1000)
+    kh, vh = oracle_dequant(got, oc.layer_signs(0, 5, 128), 128, 64)
+    keep = [np.r_[0:128, 192:1000], np.r_[0:960], np.r_[0:1000]]
+    worst = 0.0
+    for b in range(3):
+        for j in range(nq):
+            lim = 1000 - nq + j + 1
+            idx = keep[b][keep[b] < lim]
+            ref = oc.attention(np64(q[b:b + 1, j]), kh[b:b + 1, idx], vh[b:b + 1, idx])
+            worst = max(worst, compare_attention(np64(out[b:b + 1, j]), ref,
+                                                 f"multi holes b={b} j={j}"))
+    note(f"[paged] multi-query with dropped pages: worst rel-L2 {worst:.2e}")
