@@ -644,7 +644,11 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   __syncthreads();
   if (!*s_flag) return;
   // thread (g, e) folds element e of head g over the splits with a running
-  // log-sum-exp, eight splits' loads in flight at a time
+  // log-sum-exp. The partials come from other XCDs through memory, so every load of a
+  // round is issued before any is used: 32 splits' worth at a time (a long single
+  // sequence is cut into 32 splits or more) where the tile loop needs more registers
+  // than that anyway (G >= 4), else 8, which keeps the small kernels' occupancy
+  constexpr int MU = G >= 4 ? 32 : 8;
   auto ld = [](const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
@@ -654,17 +658,17 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
     const float* ml = a.part_ml + 2 * row0;
     const float* pa = a.part_acc + row0 * D + e;
     float mm = -INFINITY, ll = 0.f, aa = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      float mv[8], lv[8], av[8];
+    for (int s0 = 0; s0 < nsplit; s0 += MU) {
+      float mv[MU], lv[MU], av[MU];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < MU; ++u) {
         const int sp = min(s0 + u, nsplit - 1);
         mv[u] = ld(ml + 2 * sp);
         lv[u] = ld(ml + 2 * sp + 1);
         av[u] = ld(pa + (size_t)sp * D);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < MU; ++u) {
         if (s0 + u < nsplit && mv[u] != -INFINITY) {  // skip splits that saw no token
           const float mnew = fmaxf(mm, mv[u]);
           const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv[u] - mnew);
