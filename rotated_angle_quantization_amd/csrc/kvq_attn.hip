@@ -24,6 +24,9 @@
 //   values   lanes are 4 rows x 16 columns; each step takes one token per row, its
 //            weights broadcast along the row with DPP, its 16 radius levels computed
 //            once per row and gathered with a lane permute, cos/sin from LDS.
+//   append   (the fused decode step) the wave that will read the tile of a sequence's
+//            new slot first codes the new token into it, with the append kernel's code,
+//            while the other waves stream their tiles.
 //   merge    waves merge through LDS. With one split the workgroup normalises,
 //            inverse-transforms and stores; otherwise each split writes
 //            (max, sum, acc[d]) per head and the last workgroup of the (batch, kv head)
