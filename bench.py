@@ -404,6 +404,11 @@ def main():
         launch_avg_ms = att_ms / L
     launch_bytes_avg = attn_bytes / L
 
+    att_steps = sorted(e[1].elapsed_time(e[2]) for e, _ in recs)
+
+    def pct(xs, f):  # nearest-rank percentile of a sorted list
+        return xs[min(len(xs) - 1, max(0, int(round(f * (len(xs) - 1)))))]
+
     attn_gbps = attn_bytes / (att_ms * 1e-3) / 1e9
     achieved = launch_bytes_avg / (launch_avg_ms * 1e-3) / 1e9
     tokens = B * T
@@ -431,6 +436,7 @@ def main():
         "encode_tokens_per_s": round(tokens / (enc_ms * 1e-3), 1),
         "encode_ms": round(enc_ms, 4),
         "attn_ms": round(att_ms, 4),
+        "attn_ms_p10_median_p90": [round(pct(att_steps, f), 4) for f in (0.1, 0.5, 0.9)],
         "dequant_ms": round(deq_ms, 4),
         "dequant_out_GBps": round(2 * L * B * T * Hkv * d * 2 / (deq_ms * 1e-3) / 1e9, 2),
         "wall_s_timed": round(wall, 3),
