@@ -19,9 +19,10 @@
  *
  * General conventions
  *  - Every buffer is owned by the caller: the cache, inputs, outputs and workspace.
- *    The library allocates no device memory, keeps no mutable global state and
- *    never synchronises. All device pointers must come from hipMalloc-class
- *    allocations on the current device.
+ *    The library allocates no device memory and never synchronises; its only
+ *    global state is a per-device cache of an occupancy query (filled on first use,
+ *    the same value on every thread). All device pointers must come from
+ *    hipMalloc-class allocations on the current device.
  *  - Device work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
  *    stream). KVQ_OK means the work was enqueued; kernel faults surface at the
  *    caller's next synchronisation on that stream.
