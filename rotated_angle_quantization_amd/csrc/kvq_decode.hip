@@ -16,6 +16,8 @@
 // enters the exponent of the radius decoder.
 #include <hip/hip_fp16.h>
 
+#include <atomic>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -286,19 +288,23 @@ hipError_t launch_decode(const CodecArgs& a, int d, TileGeom geom, const uint8_t
   if (!fn) return hipErrorInvalidValue;
   // One resident wave of workgroups: each walks tiles in grid-stride order, so the
   // grid is the number that fit on the device at once (cached per device and kernel).
-  static int resident_cache[kMaxDevices][4];
+  // (relaxed atomics: threads that race on the first call store the same value)
+  static std::atomic<int> resident_cache[kMaxDevices][4];
   const int kidx = (d == 128 ? 2 : 0) + (f32_out ? 1 : 0);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int resident = dev >= 0 && dev < kMaxDevices ? resident_cache[dev][kidx] : 0;
+  int resident = dev >= 0 && dev < kMaxDevices
+                     ? resident_cache[dev][kidx].load(std::memory_order_relaxed)
+                     : 0;
   if (resident <= 0) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
     if (e != hipSuccess) return e;
     resident = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-    if (dev >= 0 && dev < kMaxDevices) resident_cache[dev][kidx] = resident;
+    if (dev >= 0 && dev < kMaxDevices)
+      resident_cache[dev][kidx].store(resident, std::memory_order_relaxed);
   }
   const dim3 grid((unsigned)(tasks < resident ? tasks : resident)), block(256);
   if (d == 64 && f32_out)
