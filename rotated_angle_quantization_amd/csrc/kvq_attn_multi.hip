@@ -25,7 +25,9 @@ namespace {
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMqWaves = 4;
+// Waves per workgroup: 8 for 16 rows (two waves per SIMD fit its registers, so one
+// wave's LDS round trips overlap another's work), 4 for 32 rows (one per SIMD).
+constexpr int mq_waves(int rb) { return rb == 1 ? 8 : 4; }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __floats2half2_rn(lo, hi));
@@ -53,9 +55,10 @@ __device__ __forceinline__ float row16_sum(float x) {
 // MFMA operand layouts (16x16x16, wave64): lane l holds A[row l % 16][k 4(l/16) .. +3],
 // B[k 4(l/16) .. +3][column l % 16] and D[rows 4(l/16) .. +3][column l % 16].
 template <int D, int BK, int BV, int RB>
-__global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
+__global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs a,
                                                                    const uint8_t* __restrict__ cache) {
   using GE = Geo<D, BK, BV>;
+  constexpr int kMqWaves = mq_waves(RB);
   constexpr int P = D / 2, M = 16 * RB, NS = D / 16;
   constexpr int KROW = P + 1;  // dwords per token row of the key tile (odd: fewer conflicts)
   constexpr int VROW = 33;     // dwords per feature row of the value tile (64 tokens + pad)
@@ -389,8 +392,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void attn_multi_kernel(AttnArgs a,
 
 hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* cache,
                              hipStream_t stream) {
-  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv)), block(kMqWaves * 64);
+  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv));
   const int rb = rows <= 16 ? 1 : 2;
+  const dim3 block(mq_waves(rb) * 64);
 #define KVQ_MQ(D_, BK_, BV_, RB_)                                                             \
   if (d == D_ && a.bk == BK_ && a.bv == BV_ && rb == RB_) {                                   \
     hipLaunchKernelGGL((attn_multi_kernel<D_, BK_, BV_, RB_>), grid, block, 0, stream, a, cache); \
