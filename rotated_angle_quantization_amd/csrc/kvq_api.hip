@@ -174,6 +174,8 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->part_acc = (float*)(base + l.acc);
   a->seq_lens = nullptr;
   a->nq = 1;
+  a->q0 = 0;
+  a->nqc = 1;
   a->pg = Paging{nullptr, 0, 0};
   return KVQ_OK;
 }
@@ -222,9 +224,8 @@ kvq_status multi_check(const kvq_layer_desc* d, uint32_t hq, uint32_t nq, uint32
   return KVQ_OK;
 }
 
-// Sequence split for multi-query attention: one four-wave workgroup per compute unit
-// fits its LDS, so aim for 256 workgroups, with at least four tiles (one per wave) per
-// split and no empty split.
+// Sequence split for multi-query attention: one workgroup per compute unit fits its
+// LDS, so aim for 256 workgroups, with at least four tiles per split and no empty split.
 void multi_split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tiles_per_split) {
   const int ntiles = (int)((seq_len + kTile - 1) / kTile);
   int s = (int)((256 + units - 1) / units);
@@ -544,8 +545,18 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   a.part_acc = (float*)(base + l.acc);
   a.seq_lens = nullptr;
   a.pg = pg;
-  return hip_status(launch_attn_multi(a, (int)d->head_dim, (int)(nq * g), (const uint8_t*)cache,
-                                      (hipStream_t)stream));
+  // launches of at most 16 query rows each (consecutive query tokens), one after the
+  // other on the stream and sharing the workspace: the 16-row kernel keeps two waves
+  // per SIMD, which outweighs reading the cache once per launch
+  const uint32_t per = 16 / g;
+  for (uint32_t q0 = 0; q0 < nq; q0 += per) {
+    a.q0 = (int)q0;
+    a.nqc = (int)(nq - q0 < per ? nq - q0 : per);
+    const hipError_t e = launch_attn_multi(a, (int)d->head_dim, a.nqc * (int)g,
+                                           (const uint8_t*)cache, (hipStream_t)stream);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
 }
 
 }  // namespace

@@ -26,7 +26,8 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // Waves per workgroup: 8 for 16 rows (two waves per SIMD fit its registers, so one
-// wave's LDS round trips overlap another's work), 4 for 32 rows (one per SIMD).
+// wave's LDS round trips overlap another's work), 4 for 32 rows (one per SIMD). The
+// library launches 16-row kernels only, splitting more rows over launches.
 constexpr int mq_waves(int rb) { return rb == 1 ? 8 : 4; }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   const int l16 = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x, bk = blockIdx.y;  // bk = b * hkv + kv head
   const int b = bk / a.hkv, kvh = bk % a.hkv;
-  const int G = a.group, NQ = a.nq, MR = NQ * G;  // real rows (row = query * G + head)
+  // real rows: row = (query - q0) * G + head, for the launch's queries q0 .. q0 + nqc - 1
+  const int G = a.group, NQ = a.nq, Q0 = a.q0, MR = a.nqc * G;
   const int seq_len = a.seq_len;
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   for (int row = wave; row < M; row += kMqWaves) {
     float2 v = make_float2(0.f, 0.f);
     if (row < MR) {
-      const size_t qoff = (((size_t)b * NQ + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
+      const size_t qoff = (((size_t)b * NQ + Q0 + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
       v = rotate_query<D>(a, qoff, min(lane, P - 1));
     }
     if (lane < P) reinterpret_cast<float2*>(s_q)[row * P + lane] = v;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rb + 4 * g4 + r;
-      lim[rb][r] = row < MR ? seq_len - NQ + row / G + 1 : 0;
+      lim[rb][r] = row < MR ? seq_len - NQ + Q0 + row / G + 1 : 0;
     }
   __syncthreads();  // the query staging space becomes the first wave's tile space
 
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   for (int row = wave; row < MR; row += kMqWaves) {
     if (lane < P) {
       const float2 v = reinterpret_cast<const float2*>(s_out)[row * P + lane];
-      const size_t ooff = (((size_t)b * NQ + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
+      const size_t ooff = (((size_t)b * NQ + Q0 + row / G) * a.hq + (size_t)kvh * G + row % G) * D;
       store_output<D>(a, ooff, lane, v.x, v.y);
     }
   }
@@ -403,9 +405,7 @@ hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* 
 #define KVQ_MQ_BV(D_, BK_, RB_) KVQ_MQ(D_, BK_, 6, RB_) KVQ_MQ(D_, BK_, 7, RB_) KVQ_MQ(D_, BK_, 8, RB_)
 #define KVQ_MQ_BK(D_, RB_) KVQ_MQ_BV(D_, 6, RB_) KVQ_MQ_BV(D_, 7, RB_) KVQ_MQ_BV(D_, 8, RB_)
   KVQ_MQ_BK(64, 1)
-  KVQ_MQ_BK(64, 2)
   KVQ_MQ_BK(128, 1)
-  KVQ_MQ_BK(128, 2)
 #undef KVQ_MQ_BK
 #undef KVQ_MQ_BV
 #undef KVQ_MQ

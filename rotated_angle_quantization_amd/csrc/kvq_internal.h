@@ -112,6 +112,7 @@ struct AttnArgs {
   float* part_acc;     // [B, Hq, nsplit, d]
   const unsigned* seq_lens;  // [B] per-entry lengths (device), or null: seq_len for all
   int nq;                    // query tokens per sequence (multi-query attention; else 1)
+  int q0, nqc;               // multi-query: first query token and count of this launch
   Paging pg;
 };
 
