@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -313,6 +313,19 @@ kvq_status kvq_attn_decode_paged(const kvq_layer_desc* desc, const void* pool,
                                  kvq_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                  void* hip_stream);
 
+/* Multi-query attention over a ragged batch: sequence b holds L_b = min(seq_lens[b],
+ * max_seq_len) tokens (seq_lens: device uint32 array [B], 4-byte aligned) whose last
+ * num_queries are the query tokens' own, so query j attends to tokens
+ * [0, L_b - num_queries + j + 1); a query that sees no token (L_b < num_queries - j)
+ * gives a zero row. Sizes, workspace and errors as kvq_attn_multi at
+ * seq_len = max_seq_len (num_queries <= max_seq_len). With every length equal to
+ * max_seq_len the result is that of kvq_attn_multi. */
+kvq_status kvq_attn_multi_varlen(const kvq_layer_desc* desc, const void* cache, const void* q,
+                                 kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t num_queries,
+                                 const uint32_t* seq_lens, uint32_t max_seq_len,
+                                 float softmax_scale, void* out, kvq_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /*
  * One decode step in one launch: kvq_append, then decode attention over the appended
  * sequences. For every sequence b, the token with K/V rows k, v [B, Hkv, d] (element
@@ -340,10 +353,13 @@ kvq_status kvq_attn_decode_append(const kvq_layer_desc* desc, void* cache,
 
 /* Multi-query attention over a paged cache: kvq_attn_multi with the cache replaced by
  * (pool, paging); tokens of tiles mapped to no page are left out of every query's
- * softmax (a query that sees no present token gives a zero row). */
+ * softmax (a query that sees no present token gives a zero row). seq_lens: null (every
+ * sequence is max_seq_len tokens long) or per-sequence lengths as for
+ * kvq_attn_multi_varlen. */
 kvq_status kvq_attn_multi_paged(const kvq_layer_desc* desc, const void* pool,
                                 const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
-                                uint32_t num_q_heads, uint32_t num_queries, uint32_t seq_len,
+                                uint32_t num_q_heads, uint32_t num_queries,
+                                const uint32_t* seq_lens, uint32_t max_seq_len,
                                 float softmax_scale, void* out, kvq_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 

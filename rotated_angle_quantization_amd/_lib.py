@@ -89,8 +89,10 @@ _SIGS = {
                                               _u32, _u32, _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi_workspace_bytes": (_sz, [_P, _u32, _u32, _u32]),
     "kvq_attn_multi_paged": (ctypes.c_int, [_P, _v, ctypes.POINTER(Paging), _v, ctypes.c_int,
-                                            _u32, _u32, _u32, _f32, _v, ctypes.c_int, _v, _sz,
-                                            _v]),
+                                            _u32, _u32, _v, _u32, _f32, _v, ctypes.c_int, _v,
+                                            _sz, _v]),
+    "kvq_attn_multi_varlen": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _v, _u32,
+                                             _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
                                       ctypes.c_int, _v, _sz, _v]),
 }
@@ -264,10 +266,11 @@ def attn_multi_workspace_bytes(desc: LayerDesc, num_q_heads: int, num_queries: i
 
 def attn_multi(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
                softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None,
-               paging: Paging | None = None):
+               paging: Paging | None = None, seq_lens: torch.Tensor | None = None):
     """Multi-query attention: q contiguous [B, NQ, Hq, d]; query token j attends to the
     first seq_len - NQ + j + 1 cached tokens. Returns [B, NQ, Hq, d]. With paging, cache
-    is the pool (kvq_attn_multi_paged)."""
+    is the pool (kvq_attn_multi_paged); with seq_lens (int32 device tensor [B]) sequence b
+    holds min(seq_lens[b], seq_len) tokens (kvq_attn_multi_varlen)."""
     if not q.is_contiguous() or q.dim() != 4:
         raise ValueError("q must be contiguous [B, NQ, Hq, d]")
     nq, hq = q.shape[1], q.shape[2]
@@ -278,12 +281,20 @@ def attn_multi(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: i
         if n == 0:
             raise KvqError(1, "kvq_attn_multi_workspace_bytes")
         workspace = torch.zeros(n, dtype=torch.uint8, device=q.device)
+    lens = seq_lens.data_ptr() if seq_lens is not None else None
     if paging is not None:
         _check(lib.kvq_attn_multi_paged(ctypes.byref(desc), cache.data_ptr(), ctypes.byref(paging),
-                                        q.data_ptr(), _dtype_code(q), hq, nq, seq_len,
+                                        q.data_ptr(), _dtype_code(q), hq, nq, lens, seq_len,
                                         float(softmax_scale), out.data_ptr(), _dtype_code(out),
                                         workspace.data_ptr(), workspace.numel(),
                                         _stream(q.device)), "kvq_attn_multi_paged")
+        return out
+    if seq_lens is not None:
+        _check(lib.kvq_attn_multi_varlen(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
+                                         _dtype_code(q), hq, nq, lens, seq_len,
+                                         float(softmax_scale), out.data_ptr(), _dtype_code(out),
+                                         workspace.data_ptr(), workspace.numel(),
+                                         _stream(q.device)), "kvq_attn_multi_varlen")
         return out
     _check(lib.kvq_attn_multi(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
                               _dtype_code(q), hq, nq, seq_len, float(softmax_scale),

@@ -505,8 +505,8 @@ namespace {
 
 kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& pg,
                      const void* q, kvq_dtype q_dtype, uint32_t hq, uint32_t nq,
-                     uint32_t seq_len, float scale, void* out, kvq_dtype out_dtype, void* ws,
-                     size_t ws_bytes, void* stream) {
+                     const uint32_t* seq_lens, uint32_t seq_len, float scale, void* out,
+                     kvq_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
   kvq_status st = multi_check(d, hq, nq, seq_len);
   if (st != KVQ_OK) return st;
   int nsplit, tps;
@@ -546,7 +546,7 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   a.tickets = (unsigned*)(base + l.tickets);
   a.part_ml = (float*)(base + l.ml);
   a.part_acc = (float*)(base + l.acc);
-  a.seq_lens = nullptr;
+  a.seq_lens = seq_lens;
   a.pg = pg;
   // launches of at most 16 query rows each (consecutive query tokens), one after the
   // other on the stream and sharing the workspace: the 16-row kernel keeps two waves
@@ -570,20 +570,34 @@ kvq_status kvq_attn_multi(const kvq_layer_desc* d, const void* cache, const void
                           kvq_dtype q_dtype, uint32_t hq, uint32_t nq, uint32_t seq_len,
                           float scale, void* out, kvq_dtype out_dtype, void* ws,
                           size_t ws_bytes, void* stream) {
-  return multi_run(d, cache, kNoPaging, q, q_dtype, hq, nq, seq_len, scale, out, out_dtype, ws,
-                   ws_bytes, stream);
+  return multi_run(d, cache, kNoPaging, q, q_dtype, hq, nq, nullptr, seq_len, scale, out,
+                   out_dtype, ws, ws_bytes, stream);
+}
+
+kvq_status kvq_attn_multi_varlen(const kvq_layer_desc* d, const void* cache, const void* q,
+                                 kvq_dtype q_dtype, uint32_t hq, uint32_t nq,
+                                 const uint32_t* seq_lens, uint32_t max_seq_len, float scale,
+                                 void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!seq_lens || ((uintptr_t)seq_lens % 4)) {
+    const kvq_status st = multi_check(d, hq, nq, max_seq_len);  // shape errors first
+    return st != KVQ_OK ? st : KVQ_ERR_INVALID_ARGUMENT;
+  }
+  return multi_run(d, cache, kNoPaging, q, q_dtype, hq, nq, seq_lens, max_seq_len, scale, out,
+                   out_dtype, ws, ws_bytes, stream);
 }
 
 kvq_status kvq_attn_multi_paged(const kvq_layer_desc* d, const void* pool,
                                 const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
-                                uint32_t hq, uint32_t nq, uint32_t seq_len, float scale,
-                                void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                uint32_t hq, uint32_t nq, const uint32_t* seq_lens,
+                                uint32_t max_seq_len, float scale, void* out,
+                                kvq_dtype out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (seq_lens && ((uintptr_t)seq_lens % 4)) return KVQ_ERR_INVALID_ARGUMENT;
   Paging pg;
   const kvq_status st0 = paging_args(d, paging, &pg);
   if (st0 != KVQ_OK) return st0;
-  return multi_run(d, pool, pg, q, q_dtype, hq, nq, seq_len, scale, out, out_dtype, ws,
-                   ws_bytes, stream);
+  return multi_run(d, pool, pg, q, q_dtype, hq, nq, seq_lens, max_seq_len, scale, out,
+                   out_dtype, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

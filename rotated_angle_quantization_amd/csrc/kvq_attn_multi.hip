@@ -81,9 +81,27 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   const int b = bk / a.hkv, kvh = bk % a.hkv;
   // real rows: row = (query - q0) * G + head, for the launch's queries q0 .. q0 + nqc - 1
   const int G = a.group, NQ = a.nq, Q0 = a.q0, MR = a.nqc * G;
-  const int seq_len = a.seq_len;
+  // this sequence's length (per-sequence lengths are clamped to the planned maximum),
+  // its tiles and the splits that cover them; a.nsplit stays the stride of the partials
+  const int seq_len = a.seq_lens ? (int)min(a.seq_lens[b], (unsigned)a.seq_len) : a.seq_len;
+  const int ntiles = (seq_len + kTile - 1) / kTile;
+  const int nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (split >= nsplit) {
+    if (split == 0) {  // an empty sequence: every query row attends to nothing
+      for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
+        const int row = idx / D, e = idx % D;
+        const size_t o =
+            (((size_t)b * NQ + Q0 + row / G) * a.hq + (size_t)kvh * G + row % G) * D + e;
+        if (a.out_f32)
+          static_cast<float*>(a.out)[o] = 0.f;
+        else
+          static_cast<__half*>(a.out)[o] = __float2half(0.f);
+      }
+    }
+    return;
+  }
   const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
+  const int tile_end = min(tile_begin + a.tiles_per_split, ntiles);
 
   for (int c = tid; c < NKT; c += kMqWaves * 64) {
     float sn = 0.f, co = 0.f;
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
       }
   }
   __syncthreads();
-  const bool single = a.nsplit == 1;
+  const bool single = nsplit == 1;
   float* s_out = reinterpret_cast<float*>(s_p);  // normalised rows when single: [M][D]
   static_assert(M * D <= kMqWaves * M * PROW, "output staging fits the probability space");
   for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
@@ -355,14 +373,14 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
     if (tid == 0) {
       const unsigned t = __hip_atomic_fetch_add(a.tickets + bk, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_SYSTEM);
-      s_flag = t == (unsigned)(a.nsplit - 1);
+      s_flag = t == (unsigned)(nsplit - 1);
     }
     __syncthreads();
     if (!s_flag) return;
     for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
       const int row = idx / D, e = idx % D;
       float mm = -INFINITY, ll = 0.f, aa = 0.f;
-      for (int sp = 0; sp < a.nsplit; ++sp) {
+      for (int sp = 0; sp < nsplit; ++sp) {
         const size_t rowi = ((size_t)bk * a.nsplit + sp) * M + row;
         const float mv = __hip_atomic_load(a.part_ml + 2 * rowi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (mv == -INFINITY) continue;  // this split saw no token of the row

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 6
+    assert kvq.abi_version() == 7
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -234,11 +234,25 @@ def test_paged_validation():
                                 None) == OK  # nothing to do
     assert kvq.paged_pool_bytes(desc, 10) == 10 * 8 * kvq.tile_bytes(128, 128, 64)
     multi = lambda paging, **kw: lib.kvq_attn_multi_paged(
-        ctypes.byref(desc), FAKE, paging, FAKE, 0, 32, kw.get("nq", 4), 100, 0.0, FAKE, 0, FAKE,
-        1 << 30, None)
+        ctypes.byref(desc), FAKE, paging, FAKE, 0, 32, kw.get("nq", 4), kw.get("lens"), 100, 0.0,
+        FAKE, 0, FAKE, 1 << 30, None)
     assert multi(None) == INVALID
     assert multi(ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
     assert multi(ctypes.byref(pg), nq=0) == INVALID
+    assert multi(ctypes.byref(pg), lens=FAKE + 2) == INVALID
+
+
+def test_attention_multi_varlen_validation():
+    desc = kvq.make_desc(128, 8, 2, 256, 128, 64)
+    mv = lambda **kw: lib.kvq_attn_multi_varlen(
+        ctypes.byref(desc), FAKE, FAKE, 0, kw.get("hq", 32), kw.get("nq", 4), kw.get("lens", FAKE),
+        kw.get("maxlen", 100), 0.0, FAKE, 0, FAKE, 1 << 30, None)
+    assert mv(lens=None) == INVALID
+    assert mv(lens=FAKE + 2) == INVALID
+    assert mv(maxlen=257) == CAPACITY
+    assert mv(lens=None, maxlen=257) == CAPACITY  # shape errors first
+    assert mv(nq=101) == INVALID
+    assert mv(hq=24) == UNSUPPORTED
 
 
 def _fused(desc, cache=FAKE, paging=None, k=FAKE, v=FAKE, dtype=0, sb=0, sh=0, pos=FAKE, q=FAKE,

@@ -114,3 +114,41 @@ def test_multi_query_workspace_reuse(dev):
         assert torch.equal(got, fresh), n
     assert torch.equal(kvq.attn_multi(desc, cache, q, 4096, workspace=ws), ref)
     assert int(ws[: 4 * 2 * cfg.hkv].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("g,nq", [(4, 4), (4, 8), (1, 32), (8, 3)])
+def test_multi_query_ragged_batch(dev, g, nq):
+    """Per-sequence lengths (kvq_attn_multi_varlen): query j of sequence b attends to the
+    first L_b - NQ + j + 1 tokens (none: a zero row); lengths above the bound are clamped;
+    with every length at the bound the result is that of the fixed-length call."""
+    torch.manual_seed(11 + g + nq)
+    d, hkv, cap = 128, 2, 1000
+    lens = [1000, 3, 0, 640, 65, 1500]  # 1500 is clamped to the bound (1000)
+    bsz = len(lens)
+    k = (torch.randn(bsz, cap, hkv, d, device=dev) * 1.5).half()
+    v = torch.randn(bsz, cap, hkv, d, device=dev).half()
+    q = torch.randn(bsz, nq, hkv * g, d, device=dev).half()
+    desc = kvq.make_desc(d, hkv, bsz, cap, 128, 64, 2, 0)
+    cache = kvq.alloc_cache(desc, dev)
+    kvq.encode(desc, cache, k, v, 0)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out = kvq.attn_multi(desc, cache, q, cap, seq_lens=sl, out_dtype=torch.float32)
+    full = torch.full_like(sl, cap)
+    same = kvq.attn_multi(desc, cache, q, cap, seq_lens=full, out_dtype=torch.float32)
+    ref_fixed = kvq.attn_multi(desc, cache, q, cap, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(same, ref_fixed)
+    got = unpack(cache.cpu().numpy(), d, 128, 64, bsz, hkv, cap, 0, cap)
+    kh, vh = oracle_dequant(got, oc.layer_signs(0, 2, d), 128, 64)
+    qn, on = np64(q), np64(out)
+    worst = 0.0
+    for b, length in enumerate(min(x, cap) for x in lens):
+        for j in range(nq):
+            n = length - nq + j + 1
+            if n <= 0:
+                assert not np.any(on[b, j]), (b, j)
+                continue
+            ref = oc.attention(qn[b:b + 1, j], kh[b:b + 1, :n], vh[b:b + 1, :n])
+            worst = max(worst, compare_attention(on[b:b + 1, j].reshape(-1, d),
+                                                 ref.reshape(-1, d), f"ragged b={b} j={j}"))
+    note(f"[multi] ragged batch G={g} NQ={nq}: worst rel-L2 {worst:.2e}")
