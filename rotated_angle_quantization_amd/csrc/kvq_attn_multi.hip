@@ -379,18 +379,31 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
     if (!s_flag) return;
     for (int idx = tid; idx < MR * D; idx += kMqWaves * 64) {
       const int row = idx / D, e = idx % D;
+      // eight splits' loads in flight per round (the partials come from other XCDs
+      // through memory)
+      auto ld = [](const float* p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
       float mm = -INFINITY, ll = 0.f, aa = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const size_t rowi = ((size_t)bk * a.nsplit + sp) * M + row;
-        const float mv = __hip_atomic_load(a.part_ml + 2 * rowi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (mv == -INFINITY) continue;  // this split saw no token of the row
-        const float lv = __hip_atomic_load(a.part_ml + 2 * rowi + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float av = __hip_atomic_load(a.part_acc + rowi * D + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float mnew = fmaxf(mm, mv);
-        const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv - mnew);
-        ll = ll * c0 + lv * c1;
-        aa = aa * c0 + av * c1;
-        mm = mnew;
+      for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float mv[8], lv[8], av[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const size_t rowi = ((size_t)bk * a.nsplit + min(s0 + u, nsplit - 1)) * M + row;
+          mv[u] = ld(a.part_ml + 2 * rowi);
+          lv[u] = ld(a.part_ml + 2 * rowi + 1);
+          av[u] = ld(a.part_acc + rowi * D + e);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u < nsplit && mv[u] != -INFINITY) {  // skip splits that saw no token
+            const float mnew = fmaxf(mm, mv[u]);
+            const float c0 = fast_exp2(mm - mnew), c1 = fast_exp2(mv[u] - mnew);
+            ll = ll * c0 + lv[u] * c1;
+            aa = aa * c0 + av[u] * c1;
+            mm = mnew;
+          }
+        }
       }
       s_out[idx] = ll > 0.f ? aa / ll : 0.f;
     }
