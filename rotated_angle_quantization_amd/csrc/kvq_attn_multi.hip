@@ -103,6 +103,34 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, ntiles);
 
+  const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
+
+  // The planes of this wave's next tile are loaded while the current one is processed,
+  // and the first tile's are requested before the set-up below, whose work then covers
+  // their latency. A tile the page table maps to no page reads page 0 and counts as
+  // holding no token.
+  struct Planes {
+    uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8], ks, vp;
+    bool present;
+  };
+  auto load_planes = [&](Planes& t, int tile) {
+    const long long off = tile_offset(a.pg, b, kvh, a.hkv, a.tiles_per_seq, tile, GE::BYTES);
+    t.present = off >= 0;
+    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(cache + (off >= 0 ? off : 0));
+#pragma unroll
+    for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
+#pragma unroll
+    for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
+    t.ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
+    t.vp = w32[GE::OFF_VP / 4 + lane];
+#pragma unroll
+    for (int w = 0; w < 2 * BV; ++w) t.va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
+  };
+  Planes nxt;
+  if (tile_begin + wave < tile_end) load_planes(nxt, tile_begin + wave);
+
   for (int c = tid; c < NKT; c += kMqWaves * 64) {
     float sn = 0.f, co = 0.f;
     if (c < a.n_k) sincospif(2.0f * (float)c / (float)a.n_k, &sn, &co);
@@ -157,32 +185,6 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   }
   uint32_t* kb = s_wave[wave];
   uint32_t* pb = s_p[wave];
-  const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
-
-  // The planes of this wave's next tile are loaded while the current one is processed
-  // (one wave per SIMD here, so nothing else would hide the load latency).
-  // A tile the page table maps to no page reads page 0 and counts as holding no token.
-  struct Planes {
-    uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8], ks, vp;
-    bool present;
-  };
-  auto load_planes = [&](Planes& t, int tile) {
-    const long long off = tile_offset(a.pg, b, kvh, a.hkv, a.tiles_per_seq, tile, GE::BYTES);
-    t.present = off >= 0;
-    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(cache + (off >= 0 ? off : 0));
-#pragma unroll
-    for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
-#pragma unroll
-    for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
-    t.ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
-    t.vp = w32[GE::OFF_VP / 4 + lane];
-#pragma unroll
-    for (int w = 0; w < 2 * BV; ++w) t.va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
-  };
-  Planes nxt;
-  if (tile_begin + wave < tile_end) load_planes(nxt, tile_begin + wave);
 
   for (int tile = tile_begin + wave; tile < tile_end; tile += kMqWaves) {
     const Planes cur = nxt;
