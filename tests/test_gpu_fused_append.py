@@ -52,10 +52,10 @@ def step_both(desc, cache, kn, vn, pos, q, maxlen, ws):
     return fused, out_f, sep, out_s
 
 
-# (d, G, n_K, n_V): full key table, half table (n a power of two), no table (n_K = 200
-# does not fit at G = 8), and d = 64
+# (d, G, n_K, n_V): half table (n a power of two), full table, no table (n_K = 200 does
+# not fit at G = 8), for d = 128 and d = 64
 CASES = [(128, 4, 128, 64), (128, 4, 100, 40), (128, 8, 200, 256), (64, 8, 128, 64),
-         (64, 1, 256, 128)]
+         (64, 1, 256, 128), (64, 4, 100, 40), (64, 8, 200, 100)]
 
 
 @pytest.mark.parametrize("d,g,nk,nv", CASES)
