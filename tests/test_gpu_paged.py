@@ -48,7 +48,8 @@ def scatter(cache, desc, tiles, table, num_pages):
     return pool.flatten()
 
 
-@pytest.mark.parametrize("d,g,nk,nv", [(128, 4, 128, 64), (64, 8, 128, 64), (128, 8, 256, 256)])
+@pytest.mark.parametrize("d,g,nk,nv", [(128, 4, 128, 64), (64, 8, 128, 64), (128, 8, 256, 256),
+                                     (128, 4, 100, 40)])
 def test_paged_paths_equal_contiguous(dev, d, g, nk, nv):
     desc, tiles, num_pages, table, k, v, q = setup(dev, d, g, nk, nv)
     paging = kvq.make_paging(table, num_pages)
