@@ -231,6 +231,29 @@ def test_degenerate_vectors(dev):
 # ----------------------------------------------------------------- online / determinism
 
 
+@pytest.mark.parametrize("d,nk,nv", [(128, 128, 64), (128, 100, 100), (64, 256, 33),
+                                     (128, 200, 128)])
+def test_random_chunkings_equal_one_shot(dev, d, nk, nv):
+    """Encoding a sequence in seeded random chunks (partial tiles at both ends, value words
+    of odd widths shared across chunk edges) leaves the one-shot bytes."""
+    rng = np.random.default_rng(d + nk + nv)
+    cfg = get("mistral7b")
+    k, v = layer_kv(cfg, 5, dev, seq=700, batch=2)
+    if d == 64:
+        k, v = k[..., :64].contiguous(), v[..., :64].contiguous()
+    desc = kvq.make_desc(d, cfg.hkv, 2, 704, nk, nv, 5, 0)
+    one = torch.zeros(kvq.cache_bytes(desc), dtype=torch.uint8, device=dev)
+    kvq.encode(desc, one, k, v, 0)
+    for trial in range(3):
+        cuts = np.sort(rng.choice(np.arange(1, 700), size=int(rng.integers(3, 12)), replace=False))
+        edges = [0, *cuts.tolist(), 700]
+        chunked = torch.zeros_like(one)
+        for lo, hi in zip(edges[:-1], edges[1:]):
+            kvq.encode(desc, chunked, k[:, lo:hi], v[:, lo:hi], lo)
+        torch.cuda.synchronize()
+        assert torch.equal(one, chunked), (trial, edges)
+
+
 def test_chunked_append_equals_one_shot(dev):
     cfg = get("tinyllama")
     k, v = layer_kv(cfg, 2, dev, seq=300)
