@@ -69,22 +69,44 @@ __device__ __forceinline__ float angle_f32(float a, float b) {
 // (rounding of the bin width adds < 4e-7 rad). When that distance is below kAngleMargin
 // the pair is compared in binary64 with the edge's direction (bedge[k] = (cos, sin) of
 // (k + 1/2) 2 pi / n): on or past the edge means the upper bin, as the floor above gives
-// at an exact half. The estimate runs for zero pairs too (it yields NaN, which fails the
-// margin test and converts to 0) and the zero test only selects the result, so no
-// branch surrounds the common path.
+// at an exact half. The error bound assumes the pair rounds to normal fp32 numbers well
+// inside the range, where the reciprocal is exact to an ulp: a pair whose larger
+// component lies outside [2^-60, 2^60] (tiny vectors, whose fp32 values are subnormal or
+// zero, or fp32 inputs near the top of the range, which overflow fp32 after rotation) is
+// first scaled by a power of two in binary64 (exact, and the angle is unchanged) and
+// estimated again; a non-finite estimate also fails the margin test. The estimate runs
+// for zero pairs too and the zero test only selects the result, so no branch surrounds
+// the common path.
 constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
+constexpr float kAngleRangeLo = 0x1p-60f, kAngleRangeHi = 0x1p60f;
 template <class Edge>  // edge(k) = (cos, sin) of (k + 1/2) 2 pi / n in binary64
 __device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
                                           float bins_per_rad_f, float bin_rad_f,
                                           const Edge& edge) {
-  const float th = angle_f32((float)a, (float)b);
-  const float cf = rintf(th * bins_per_rad_f);
-  const float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
+  float af = (float)a, bf = (float)b;
+  float th = angle_f32(af, bf);
+  float cf = rintf(th * bins_per_rad_f);
+  float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
   int c = (int)cf;  // in [-n/2, n/2]
-  if (__builtin_expect(0.5f * bin_rad_f - fabsf(res) < kAngleMargin, 0)) {
+  const float mxf = fmaxf(fabsf(af), fabsf(bf));
+  const bool in_range = mxf >= kAngleRangeLo && mxf <= kAngleRangeHi;
+  const bool near_edge = !(0.5f * bin_rad_f - fabsf(res) >= kAngleMargin);  // NaN: near
+  if (__builtin_expect((near_edge || !in_range) && !zero, 0)) {
+    if (!in_range) {
+      // larger component scaled into [1/2, 1): exact in binary64
+      const double sc = pow2(-__builtin_amdgcn_frexp_exp(fmax(fabs(a), fabs(b))));
+      af = (float)(a * sc);
+      bf = (float)(b * sc);
+      th = angle_f32(af, bf);
+      cf = rintf(th * bins_per_rad_f);
+      res = fmaf(-cf, bin_rad_f, th);
+      c = (int)cf;
+    }
     const int k = res > 0.f ? c : c - 1;  // edge between centres k and k + 1
     const int kk = k < 0 ? k + n : (k >= n ? k - n : k);
     const double2 e = edge(kk);
+    // the sign of the cross product with the edge direction is that of the pair's
+    // angle relative to the edge (exact scaling leaves it unchanged)
     c = fma(e.x, b, -e.y * a) >= 0.0 ? k + 1 : k;
   }
   // c is in [-n/2 - 1, n/2 + 1]: wrap into [0, n) as min(c + n, c) in unsigned terms
@@ -119,7 +141,9 @@ __device__ __forceinline__ KeyScale key_scale(double max_r2) {
 __device__ __forceinline__ int key_level(double r2, const KeyScale& k) {
   int rho = 0;
   if (k.s > 0.0) {
-    const float t = __builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f;
+    // capped so that a radius past the fp32 range (fp32 inputs near its top) converts
+    // to a level above 255 rather than to an undefined integer
+    const float t = fminf(__builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f, 256.f);
     const float m = rintf(t);
     rho = (int)floorf(t);
     if (__builtin_expect(fabsf(t - m) < 5e-4f, 0)) {
@@ -162,7 +186,7 @@ __device__ __forceinline__ int value_level(double r2, const ValueScale& v) {
     // <= 7e-7 (lr) and 4e-7 (l2), |dt| <= 7.5 (7e-7 + 2 * 4e-7) / l2 plus ~1e-6 of fp32
     // rounding; the margin below is more than twice that.
     const float lr = __log2f((float)r2 * v.inv_smin2);
-    const float t = lr * v.scale + 0.5f;
+    const float t = fminf(lr * v.scale + 0.5f, 16.f);  // capped: r^2 past the fp32 range
     const float fl = floorf(t);
     const float margin = v.scale * (4e-6f + 1e-6f * fabsf(lr)) + 2e-5f;
     rho = (int)fl;

@@ -29,7 +29,7 @@ def np64(t: torch.Tensor) -> np.ndarray:
 
 
 def run_full_check(dev, k, v, q, d, n_k, n_v, layer=0, seed=0, capacity=None, seq_len=None,
-                   attn_checks=True, tag=""):
+                   attn_checks=True, tag="", fp16_dequant=True):
     """Encode k/v [B, T, Hkv, d] on the GPU, then compare every code, every dequantised
     vector and every attention output against the oracle."""
     bsz, t, hkv, _ = k.shape
@@ -47,17 +47,21 @@ def run_full_check(dev, k, v, q, d, n_k, n_v, layer=0, seed=0, capacity=None, se
     stats = compare_codes(got, ek, ev)
     # dequant: both sides decode the same bytes
     kh_ref, vh_ref = oracle_dequant(got, sg, n_k, n_v)
-    for dt in (torch.float32, torch.float16):
+    for dt in (torch.float32, torch.float16) if fp16_dequant else (torch.float32,):
         kh, vh = kvq.decode(desc, cache, 0, t, out_dtype=dt)
         torch.cuda.synchronize()
         f16 = dt == torch.float16
         compare_dequant(np64(kh), kh_ref, xk, f"{tag} keys {dt}", fp16_out=f16)
         compare_dequant(np64(vh), vh_ref, xv, f"{tag} values {dt}", fp16_out=f16)
     if attn_checks and q is not None:
+        ref = oc.attention(np64(q), kh_ref[:, :seq_len], vh_ref[:, :seq_len])
+        # both output types; fp16 is the one the benchmark times (its rounding adds at
+        # most 2^-11 relative per element, inside the 2e-3 bound)
+        out16 = kvq.attn_decode(desc, cache, q, seq_len, out_dtype=torch.float16)
         out = kvq.attn_decode(desc, cache, q, seq_len, out_dtype=torch.float32)
         torch.cuda.synchronize()
-        ref = oc.attention(np64(q), kh_ref[:, :seq_len], vh_ref[:, :seq_len])
         stats["attn_rel"] = compare_attention(np64(out), ref, f"{tag} attention")
+        stats["attn_rel_f16out"] = compare_attention(np64(out16), ref, f"{tag} attention fp16 out")
         # end to end against an independent oracle encode (reported, not gated)
         kh_o = oc.dequant_k(ek["angle"], ek["radius"], ek["scale"], n_k, sg)
         vh_o = oc.dequant_v(ev["angle"], ev["radius"], ev["s_min"], ev["s_max"], n_v, sg)
@@ -100,6 +104,7 @@ def sampled_check(dev, name, layer, n_heads_attn=2, n_tiles=6, seed=0):
     cache = kvq.alloc_cache(desc, dev)
     kvq.encode(desc, cache, k, v, 0)
     out = kvq.attn_decode(desc, cache, q, t, out_dtype=torch.float32)
+    out16 = kvq.attn_decode(desc, cache, q, t, out_dtype=torch.float16)  # as benchmarked
     torch.cuda.synchronize()
     sg = oc.layer_signs(seed, layer, d)
     rng = np.random.default_rng(layer + 17)
@@ -121,7 +126,7 @@ def sampled_check(dev, name, layer, n_heads_attn=2, n_tiles=6, seed=0):
             compare_dequant(np64(kh[b:b + 1, :, h:h + 1]), kh_ref, xk, f"{name} keys")
             compare_dequant(np64(vh[b:b + 1, :, h:h + 1]), vh_ref, xv, f"{name} values")
     # attention on sampled (b, query head) over the full sequence
-    worst = 0.0
+    worst = worst16 = 0.0
     g = cfg.group
     for _ in range(n_heads_attn):
         b, hq = int(rng.integers(bsz)), int(rng.integers(cfg.hq))
@@ -131,7 +136,10 @@ def sampled_check(dev, name, layer, n_heads_attn=2, n_tiles=6, seed=0):
         ref = oc.attention(np64(q[b:b + 1, hq:hq + 1]), kh_ref, vh_ref)
         worst = max(worst, compare_attention(np64(out[b:b + 1, hq:hq + 1]), ref,
                                              f"{name} b{b} h{hq}"))
-    note(f"[sampled] {name} layer {layer} ok, attention worst rel {worst:.2e}")
+        worst16 = max(worst16, compare_attention(np64(out16[b:b + 1, hq:hq + 1]), ref,
+                                                 f"{name} b{b} h{hq} fp16 out"))
+    note(f"[sampled] {name} layer {layer} ok, attention worst rel {worst:.2e} "
+         f"(fp16 out {worst16:.2e})")
     del k, v, cache
     torch.cuda.empty_cache()
 
@@ -226,6 +234,36 @@ def test_degenerate_vectors(dev):
     k[0, 6, 0] = sg * h[:, 9]  # rotates to a one-hot: angles on bin centres
     q = torch.randn(1, 4, d, device=dev)
     run_full_check(dev, k.half(), v.half(), q.half(), d, 128, 64, tag="degenerate")
+
+
+def test_degenerate_vectors_fp32_extremes(dev):
+    """fp32 inputs at the ends of the range: pairs whose fp32 values are subnormal or
+    round to zero (the angle estimate would divide by a flushed reciprocal) and pairs
+    that overflow fp32 after the rotation get the codes of the binary64 definition."""
+    d = 128
+    torch.manual_seed(9)
+    k = torch.randn(1, 70, 2, d, device=dev)
+    v = torch.randn(1, 70, 2, d, device=dev)
+    sg = torch.tensor(oc.layer_signs(0, 0, d), device=dev, dtype=torch.float32)
+    h = torch.tensor(oc.hadamard(d), device=dev, dtype=torch.float32)
+    k[0, 0, 0] = sg * h[:, 9] * 1e-41   # rotates to (0, tiny) in pair 4: code n/4
+    k[0, 1, 0] = sg * h[:, 8] * 1e-41   # (tiny, 0): code 0
+    v[0, 0, 1] = sg * h[:, 11] * 1e-40
+    k[0, 2] = torch.randn(2, d, device=dev) * 1e-39  # subnormal fp32 inputs
+    v[0, 3] = torch.randn(2, d, device=dev) * 1e-38
+    k[0, 4] = torch.randn(2, d, device=dev) * 1e-30
+    k[0, 5, 0] = sg * h[:, 3] * 1e38    # rotates to 1.1e39 > the fp32 range
+    v[0, 5, 1] = sg * h[:, 6] * 1e38
+    k[0, 6] = torch.randn(2, d, device=dev) * 2e37
+    v[0, 7] = torch.randn(2, d, device=dev) * 2e37
+    q = torch.randn(1, 4, d, device=dev)
+    # dequantised elements of the saturated vectors exceed the fp16 range (a radius of
+    # 65504 in every pair), so only the fp32 output is compared for them
+    _, cache, _ = run_full_check(dev, k, v, q, d, 128, 64, tag="fp32 extremes",
+                                 fp16_dequant=False)
+    got = unpack(cache.cpu().numpy(), d, 128, 64, 1, 2, 70, 0, 70)
+    assert got["k_angle"][0, 0, 0, 4] == 32 and got["k_angle"][0, 1, 0, 4] == 0
+    assert got["v_angle"][0, 0, 1, 5] == 16
 
 
 # ----------------------------------------------------------------- online / determinism
