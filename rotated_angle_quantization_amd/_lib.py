@@ -121,6 +121,75 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+# Argument checks made before any library call: the kernels take raw pointers, so a
+# buffer smaller than the descriptor says, a tensor of the wrong shape, type or layout,
+# or one in host memory would be read or written out of bounds on the device. Shapes
+# and types are checked first, devices last.
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _float_tensor(t, name: str, shape: tuple, contiguous: bool = True) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(t.dtype in (torch.float16, torch.float32), f"{name} must be float16 or float32, not {t.dtype}")
+    if contiguous:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _index_tensor(t, name: str, n: int) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.dtype in (torch.int32, torch.uint32), f"{name} must be int32 (or uint32), not {t.dtype}")
+    _need(t.dim() == 1 and t.numel() == n and t.is_contiguous(),
+          f"{name} must be a contiguous 1-d tensor of {n} entries, got shape {tuple(t.shape)}")
+
+
+def _byte_buffer(t, name: str, nbytes: int) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.dtype == torch.uint8 and t.is_contiguous(), f"{name} must be a contiguous uint8 tensor")
+    _need(t.numel() >= nbytes, f"{name} holds {t.numel()} bytes, {nbytes} are needed")
+
+
+def _kv_rows(k, v, shape: tuple) -> None:
+    """K and V rows: the given shape, d contiguous, one dtype and one set of strides."""
+    for t, name in ((k, "k"), (v, "v")):
+        _float_tensor(t, name, shape, contiguous=False)
+        _need(t.stride(-1) == 1, f"{name} must have its last (head_dim) axis contiguous")
+    _need(k.dtype == v.dtype and k.stride() == v.stride(), "k and v must share dtype and strides")
+
+
+def _same_device(*named) -> None:
+    """Every tensor on one CUDA (HIP) device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        _need(t.device.type == "cuda", f"{name} must be in GPU memory, not on {t.device}")
+        if dev is None:
+            dev = t.device
+        _need(t.device == dev, f"{name} is on {t.device}, other arguments on {dev}")
+
+
+def _layer_cache(desc, cache, name: str = "cache") -> None:
+    n = cache_bytes(desc)
+    _need(n > 0, f"invalid layer descriptor {desc!r}")
+    _byte_buffer(cache, name, n)
+
+
+def _check_out(out, q_shape) -> None:
+    if out is not None:
+        _float_tensor(out, "out", q_shape)
+
+
+def _attn_out(out, q_shape, out_dtype, q):
+    if out is None:
+        return torch.empty(q_shape, dtype=out_dtype or q.dtype, device=q.device)
+    return out
+
+
 def make_desc(head_dim, num_kv_heads, batch, capacity, n_bins_k, n_bins_v, layer=0,
               seed=0) -> LayerDesc:
     return LayerDesc(head_dim, num_kv_heads, batch, capacity, n_bins_k, n_bins_v, layer, 0,
@@ -155,14 +224,23 @@ def alloc_cache(desc: LayerDesc, device="cuda") -> torch.Tensor:
 def encode(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            t0: int = 0) -> None:
     """Append K/V tokens [t0, t0 + ntok): k, v are [B, ntok, Hkv, d] with matching strides."""
-    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
-        raise ValueError("k and v must share shape, strides and dtype")
-    if k.dim() != 4 or k.stride(3) != 1:
-        raise ValueError("k/v must be [B, ntok, Hkv, d] with d contiguous")
+    _need(isinstance(k, torch.Tensor) and k.dim() == 4, "k/v must be [B, ntok, Hkv, d]")
     ntok = k.shape[1]
+    _kv_rows(k, v, (desc.batch, ntok, desc.num_kv_heads, desc.head_dim))
+    _layer_cache(desc, cache)
+    _same_device(("cache", cache), ("k", k), ("v", v))
     _check(lib.kvq_encode(ctypes.byref(desc), cache.data_ptr(), k.data_ptr(), v.data_ptr(),
                           _dtype_code(k), k.stride(0), k.stride(1), k.stride(2), t0, ntok,
                           _stream(cache.device)), "kvq_encode")
+
+
+def _token_rows(desc, k, v):
+    """One token per sequence: [B, Hkv, d] (or [B, 1, Hkv, d]), d contiguous."""
+    if isinstance(k, torch.Tensor) and isinstance(v, torch.Tensor) and k.dim() == 4 \
+            and k.shape[1] == 1 and v.dim() == 4:
+        k, v = k[:, 0], v[:, 0]
+    _kv_rows(k, v, (desc.batch, desc.num_kv_heads, desc.head_dim))
+    return k, v
 
 
 def append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -170,15 +248,10 @@ def append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     """Encode one token per sequence at slot positions[b] of sequence b.
     k, v: [B, Hkv, d] (or [B, 1, Hkv, d]) with d contiguous, fp16 or fp32; positions:
     int32 device tensor [B]."""
-    if k.dim() == 4 and k.shape[1] == 1:
-        k, v = k[:, 0], v[:, 0]
-    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
-        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
-    if k.dtype != v.dtype:
-        raise ValueError("k and v must have the same dtype")
-    if positions.dtype not in (torch.int32, torch.uint32) or not positions.is_contiguous() \
-            or positions.numel() != k.shape[0] or positions.device != k.device:
-        raise ValueError("positions must be a contiguous int32 device tensor [B] on k's device")
+    k, v = _token_rows(desc, k, v)
+    _index_tensor(positions, "positions", desc.batch)
+    _layer_cache(desc, cache)
+    _same_device(("cache", cache), ("k", k), ("v", v), ("positions", positions))
     _check(lib.kvq_append(ctypes.byref(desc), cache.data_ptr(), k.data_ptr(), v.data_ptr(),
                           _dtype_code(k), k.stride(0), k.stride(1), positions.data_ptr(),
                           _stream(cache.device)), "kvq_append")
@@ -188,11 +261,17 @@ def decode(desc: LayerDesc, cache: torch.Tensor, t0: int, ntok: int,
            out_dtype=torch.float16, out: tuple | None = None):
     """Dequantise tokens [t0, t0 + ntok) -> (k_hat, v_hat), each [B, ntok, Hkv, d]."""
     shape = (desc.batch, ntok, desc.num_kv_heads, desc.head_dim)
+    _layer_cache(desc, cache)
     if out is None:
+        _same_device(("cache", cache))
         k_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
         v_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
     else:
         k_out, v_out = out
+        _float_tensor(k_out, "k_out", shape)
+        _float_tensor(v_out, "v_out", shape)
+        _need(k_out.dtype == v_out.dtype, "k_out and v_out must share a dtype")
+    _same_device(("cache", cache), ("k_out", k_out), ("v_out", v_out))
     _check(lib.kvq_decode(ctypes.byref(desc), cache.data_ptr(), k_out.data_ptr(),
                           v_out.data_ptr(), _dtype_code(k_out), t0, ntok,
                           _stream(cache.device)), "kvq_decode")
@@ -216,17 +295,32 @@ def alloc_workspace(desc: LayerDesc, num_q_heads: int, seq_len: int, device="cud
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+def _query(desc, q, nq: int | None = None) -> int:
+    """Query rows [B, Hq, d] (or [B, NQ, Hq, d] when nq is given); returns Hq."""
+    _need(isinstance(q, torch.Tensor), "q must be a torch tensor")
+    if nq is None:
+        _need(q.dim() == 3, f"q must be [B, Hq, d], got shape {tuple(q.shape)}")
+        hq = q.shape[1]
+        _float_tensor(q, "q", (desc.batch, hq, desc.head_dim))
+    else:
+        _need(q.dim() == 4, f"q must be [B, NQ, Hq, d], got shape {tuple(q.shape)}")
+        hq = q.shape[2]
+        _float_tensor(q, "q", (desc.batch, nq, hq, desc.head_dim))
+    return hq
+
+
 def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
                 softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None):
     """o[b, h] = softmax(scale q.k_hat) v_hat over the first seq_len cached tokens.
     q: contiguous [B, Hq, d] (fp16 or fp32); returns [B, Hq, d]."""
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
-    hq = q.shape[1]
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    hq = _query(desc, q)
+    _layer_cache(desc, cache)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("q", q), ("out", out), ("workspace", workspace))
+    out = _attn_out(out, q.shape, out_dtype, q)
     if workspace is None:
         workspace = alloc_workspace(desc, hq, seq_len, q.device)
+    _byte_buffer(workspace, "workspace", attn_workspace_bytes(desc, hq, seq_len))
     _check(lib.kvq_attn_decode(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
                                _dtype_code(q), hq, seq_len, float(softmax_scale),
                                out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
@@ -240,16 +334,16 @@ def attn_decode_varlen(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor,
     """attn_decode with a length per sequence: entry b attends to its first seq_lens[b]
     cached tokens. seq_lens: int32 (or uint32 bits) device tensor [B], every entry
     <= max_seq_len (larger entries count as max_seq_len; 0 gives a zero output)."""
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
-    if seq_lens.dtype not in (torch.int32, torch.uint32) or not seq_lens.is_contiguous() \
-            or seq_lens.numel() != q.shape[0] or seq_lens.device != q.device:
-        raise ValueError("seq_lens must be a contiguous int32 device tensor [B] on q's device")
-    hq = q.shape[1]
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    hq = _query(desc, q)
+    _index_tensor(seq_lens, "seq_lens", desc.batch)
+    _layer_cache(desc, cache)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("q", q), ("seq_lens", seq_lens), ("out", out),
+                 ("workspace", workspace))
+    out = _attn_out(out, q.shape, out_dtype, q)
     if workspace is None:
         workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    _byte_buffer(workspace, "workspace", attn_workspace_bytes(desc, hq, max_seq_len))
     _check(lib.kvq_attn_decode_varlen(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
                                       _dtype_code(q), hq, seq_lens.data_ptr(), max_seq_len,
                                       float(softmax_scale), out.data_ptr(), _dtype_code(out),
@@ -271,16 +365,27 @@ def attn_multi(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: i
     first seq_len - NQ + j + 1 cached tokens. Returns [B, NQ, Hq, d]. With paging, cache
     is the pool (kvq_attn_multi_paged); with seq_lens (int32 device tensor [B]) sequence b
     holds min(seq_lens[b], seq_len) tokens (kvq_attn_multi_varlen)."""
-    if not q.is_contiguous() or q.dim() != 4:
-        raise ValueError("q must be contiguous [B, NQ, Hq, d]")
-    nq, hq = q.shape[1], q.shape[2]
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _need(isinstance(q, torch.Tensor) and q.dim() == 4, "q must be [B, NQ, Hq, d]")
+    nq = q.shape[1]
+    hq = _query(desc, q, nq)
+    if seq_lens is not None:
+        _index_tensor(seq_lens, "seq_lens", desc.batch)
+    if paging is not None:
+        _paging(desc, paging)
+        _byte_buffer(cache, "pool", paged_pool_bytes(desc, paging.num_pages))
+    else:
+        _layer_cache(desc, cache)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("q", q), ("seq_lens", seq_lens), ("out", out),
+                 ("workspace", workspace),
+                 ("page_table", paging.table if paging is not None else None))
+    out = _attn_out(out, q.shape, out_dtype, q)
+    n = attn_multi_workspace_bytes(desc, hq, nq, seq_len)
+    if n == 0:
+        raise KvqError(1, "kvq_attn_multi_workspace_bytes")
     if workspace is None:
-        n = attn_multi_workspace_bytes(desc, hq, nq, seq_len)
-        if n == 0:
-            raise KvqError(1, "kvq_attn_multi_workspace_bytes")
         workspace = torch.zeros(n, dtype=torch.uint8, device=q.device)
+    _byte_buffer(workspace, "workspace", n)
     lens = seq_lens.data_ptr() if seq_lens is not None else None
     if paging is not None:
         _check(lib.kvq_attn_multi_paged(ctypes.byref(desc), cache.data_ptr(), ctypes.byref(paging),
@@ -312,13 +417,27 @@ def make_paging(page_table: torch.Tensor, num_pages: int) -> Paging:
     stay alive while calls that use the returned description are in flight."""
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
         raise ValueError("page_table must be a contiguous int32 tensor [batch, pages_per_seq]")
-    return Paging(page_table.data_ptr(), page_table.shape[1], num_pages)
+    pg = Paging(page_table.data_ptr(), page_table.shape[1], num_pages)
+    pg.table = page_table  # kept alive with the description, and checked against the layer
+    return pg
+
+
+def _paging(desc, paging) -> None:
+    """The page table covers every sequence of the layer."""
+    _need(isinstance(paging, Paging), "paging must come from make_paging")
+    table = getattr(paging, "table", None)
+    _need(table is not None, "paging must come from make_paging (it keeps the table tensor)")
+    _need(table.shape[0] >= desc.batch, f"page table has {table.shape[0]} rows, the layer "
+                                         f"has {desc.batch} sequences")
 
 
 def encode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.Tensor,
                  v: torch.Tensor, t0: int = 0):
-    if k.dim() != 4 or k.stride(3) != 1 or k.shape != v.shape or k.stride() != v.stride():
-        raise ValueError("k/v must be [B, ntok, Hkv, d] with d contiguous and equal strides")
+    _need(isinstance(k, torch.Tensor) and k.dim() == 4, "k/v must be [B, ntok, Hkv, d]")
+    _kv_rows(k, v, (desc.batch, k.shape[1], desc.num_kv_heads, desc.head_dim))
+    _paging(desc, paging)
+    _byte_buffer(pool, "pool", paged_pool_bytes(desc, paging.num_pages))
+    _same_device(("pool", pool), ("k", k), ("v", v), ("page_table", paging.table))
     _check(lib.kvq_encode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
                                 k.data_ptr(), v.data_ptr(), _dtype_code(k), k.stride(0),
                                 k.stride(1), k.stride(2), t0, k.shape[1], _stream(pool.device)),
@@ -327,10 +446,12 @@ def encode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.T
 
 def append_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.Tensor,
                  v: torch.Tensor, positions: torch.Tensor):
-    if k.dim() == 4 and k.shape[1] == 1:
-        k, v = k[:, 0], v[:, 0]
-    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
-        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
+    k, v = _token_rows(desc, k, v)
+    _index_tensor(positions, "positions", desc.batch)
+    _paging(desc, paging)
+    _byte_buffer(pool, "pool", paged_pool_bytes(desc, paging.num_pages))
+    _same_device(("pool", pool), ("k", k), ("v", v), ("positions", positions),
+                 ("page_table", paging.table))
     _check(lib.kvq_append_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
                                 k.data_ptr(), v.data_ptr(), _dtype_code(k), k.stride(0),
                                 k.stride(1), positions.data_ptr(), _stream(pool.device)),
@@ -340,6 +461,9 @@ def append_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, k: torch.T
 def decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, t0: int, ntok: int,
                  out_dtype=torch.float16):
     shape = (desc.batch, ntok, desc.num_kv_heads, desc.head_dim)
+    _paging(desc, paging)
+    _byte_buffer(pool, "pool", paged_pool_bytes(desc, paging.num_pages))
+    _same_device(("pool", pool), ("page_table", paging.table))
     k_out = torch.empty(shape, dtype=out_dtype, device=pool.device)
     v_out = torch.empty(shape, dtype=out_dtype, device=pool.device)
     _check(lib.kvq_decode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
@@ -351,13 +475,18 @@ def decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, t0: int, n
 def attn_decode_paged(desc: LayerDesc, pool: torch.Tensor, paging: Paging, q: torch.Tensor,
                       max_seq_len: int, seq_lens: torch.Tensor | None = None,
                       softmax_scale: float = 0.0, out_dtype=None, workspace=None, out=None):
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
-    hq = q.shape[1]
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    hq = _query(desc, q)
+    if seq_lens is not None:
+        _index_tensor(seq_lens, "seq_lens", desc.batch)
+    _paging(desc, paging)
+    _byte_buffer(pool, "pool", paged_pool_bytes(desc, paging.num_pages))
+    _check_out(out, q.shape)
+    _same_device(("pool", pool), ("q", q), ("seq_lens", seq_lens), ("out", out),
+                 ("workspace", workspace), ("page_table", paging.table))
+    out = _attn_out(out, q.shape, out_dtype, q)
     if workspace is None:
         workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    _byte_buffer(workspace, "workspace", attn_workspace_bytes(desc, hq, max_seq_len))
     lens = seq_lens.data_ptr() if seq_lens is not None else None
     _check(lib.kvq_attn_decode_paged(ctypes.byref(desc), pool.data_ptr(), ctypes.byref(paging),
                                      q.data_ptr(), _dtype_code(q), hq, lens, max_seq_len,
@@ -374,22 +503,22 @@ def attn_decode_append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v:
     """One decode step in one launch: code the token k/v [B, Hkv, d] of sequence b at slot
     positions[b] (int32 device tensor [B]), then attend with q [B, Hq, d] over
     min(positions[b] + 1, max_seq_len) tokens. cache is the pool when paging is given."""
-    if k.dim() == 4 and k.shape[1] == 1:
-        k, v = k[:, 0], v[:, 0]
-    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
-        raise ValueError("k/v must be [B, Hkv, d] with d contiguous and equal strides")
-    if k.dtype != v.dtype:
-        raise ValueError("k and v must have the same dtype")
-    if positions.dtype not in (torch.int32, torch.uint32) or not positions.is_contiguous() \
-            or positions.numel() != k.shape[0] or positions.device != k.device:
-        raise ValueError("positions must be a contiguous int32 device tensor [B] on k's device")
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
-    hq = q.shape[1]
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    k, v = _token_rows(desc, k, v)
+    _index_tensor(positions, "positions", desc.batch)
+    hq = _query(desc, q)
+    if paging is not None:
+        _paging(desc, paging)
+        _byte_buffer(cache, "pool", paged_pool_bytes(desc, paging.num_pages))
+    else:
+        _layer_cache(desc, cache)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("k", k), ("v", v), ("positions", positions), ("q", q),
+                 ("out", out), ("workspace", workspace),
+                 ("page_table", paging.table if paging is not None else None))
+    out = _attn_out(out, q.shape, out_dtype, q)
     if workspace is None:
         workspace = alloc_workspace(desc, hq, max_seq_len, q.device)
+    _byte_buffer(workspace, "workspace", attn_workspace_bytes(desc, hq, max_seq_len))
     pg = ctypes.byref(paging) if paging is not None else None
     _check(lib.kvq_attn_decode_append(ctypes.byref(desc), cache.data_ptr(), pg, k.data_ptr(),
                                       v.data_ptr(), _dtype_code(k), k.stride(0), k.stride(1),
