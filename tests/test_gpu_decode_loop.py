@@ -61,14 +61,15 @@ def test_attention_varlen_matches_oracle(dev, d, g, nk, nv):
     kvq.encode(desc, cache, k, v, 0)
     seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
     ws = kvq.alloc_workspace(desc, hkv * g, cap, dev)
-    out = kvq.attn_decode_varlen(desc, cache, q, seq_lens, cap, out_dtype=torch.float32,
-                                 workspace=ws)
-    torch.cuda.synchronize()
-    got = np64(out)
-    assert not np.any(got[2]), "a zero-length sequence gives a zero output"
     ref = oracle_varlen(cache, desc, q, lens)
-    rel = compare_attention(np.delete(got, 2, 0), np.delete(ref, 2, 0), f"varlen d{d} G{g}")
-    note(f"[varlen] worst rel-L2 {rel:.2e}")
+    for dt in (torch.float32, torch.float16):
+        out = kvq.attn_decode_varlen(desc, cache, q, seq_lens, cap, out_dtype=dt, workspace=ws)
+        torch.cuda.synchronize()
+        got = np64(out)
+        assert not np.any(got[2]), "a zero-length sequence gives a zero output"
+        rel = compare_attention(np.delete(got, 2, 0), np.delete(ref, 2, 0),
+                                f"varlen d{d} G{g} {dt}")
+        note(f"[varlen] {dt} worst rel-L2 {rel:.2e}")
     assert int(ws[: 4 * bsz * hkv].count_nonzero()) == 0, "split counters back at zero"
 
 
@@ -157,10 +158,13 @@ def test_ragged_decode_loop(dev):
         q = query(cfg, 10, dev, batch=bsz, seed=step)
         out = kvq.attn_decode_varlen(desc, cache, q, positions + 1, cap,
                                      out_dtype=torch.float32, workspace=ws)
+        out16 = kvq.attn_decode_varlen(desc, cache, q, positions + 1, cap,
+                                       out_dtype=torch.float16, workspace=ws)
         torch.cuda.synchronize()
         ref = oracle_varlen(cache, desc, q, lens)
         rel = compare_attention(np64(out), ref, f"decode step {step}")
-        note(f"[decode loop] step {step} lens {lens} rel-L2 {rel:.2e}")
+        rel16 = compare_attention(np64(out16), ref, f"decode step {step} fp16 out")
+        note(f"[decode loop] step {step} lens {lens} rel-L2 {rel:.2e} (fp16 out {rel16:.2e})")
     # the appended caches equal a one-shot encode of the same tokens
     truth = kvq.alloc_cache(desc, dev)
     kvq.encode(desc, truth, k[:, :max(lens)], v[:, :max(lens)], 0)

@@ -85,6 +85,8 @@ def test_fused_step_matches_oracle(dev):
     vn = torch.randn(bsz, hkv, d, device=dev).half()
     q = torch.randn(bsz, hkv * g, d, device=dev).half()
     out = kvq.attn_decode_append(desc, cache, kn, vn, pos, q, cap, out_dtype=torch.float32)
+    # the same step again with fp16 output (the appended bytes are rewritten unchanged)
+    out16 = kvq.attn_decode_append(desc, cache, kn, vn, pos, q, cap, out_dtype=torch.float16)
     torch.cuda.synchronize()
     codes = unpack(cache.cpu().numpy(), d, nk, nv, bsz, hkv, cap, 0, cap)
     kh, vh = oracle_dequant(codes, oc.layer_signs(0, 3, d), nk, nv)
@@ -100,7 +102,8 @@ def test_fused_step_matches_oracle(dev):
     for b, p in enumerate(pos.tolist()):
         ref = oc.attention(np64(q[b:b + 1]), kh[b:b + 1, :p + 1], vh[b:b + 1, :p + 1])
         worst = max(worst, compare_attention(np64(out[b:b + 1]), ref, f"fused b={b}"))
-    note(f"[fused append] worst rel-L2 against the oracle {worst:.2e}")
+        worst = max(worst, compare_attention(np64(out16[b:b + 1]), ref, f"fused b={b} fp16"))
+    note(f"[fused append] worst rel-L2 against the oracle (fp32 and fp16 out) {worst:.2e}")
 
 
 def test_fused_decode_loop(dev):

@@ -100,6 +100,7 @@ def test_pages_mapped_to_no_page(dev):
     # attention drops the absent tokens (the oracle over the present ones); a sequence
     # with none gives zeros
     out = kvq.attn_decode_paged(desc, pool, paging, q, 1000, out_dtype=torch.float32)
+    out16 = kvq.attn_decode_paged(desc, pool, paging, q, 1000, out_dtype=torch.float16)
     torch.cuda.synchronize()
     got = unpack(cont.cpu().numpy(), 128, 128, 64, 3, 2, 1000, 0, 1000)
     kh, vh = oracle_dequant(got, oc.layer_signs(0, 5, 128), 128, 64)
@@ -107,8 +108,10 @@ def test_pages_mapped_to_no_page(dev):
     for b in range(2):
         ref = oc.attention(np64(q[b:b + 1]), kh[b:b + 1, keep[b]], vh[b:b + 1, keep[b]])
         rel = compare_attention(np64(out[b:b + 1]), ref, f"holes seq {b}")
-        note(f"[paged] sequence {b} with a dropped page: rel-L2 {rel:.2e}")
+        rel16 = compare_attention(np64(out16[b:b + 1]), ref, f"holes seq {b} fp16 out")
+        note(f"[paged] sequence {b} with a dropped page: rel-L2 {rel:.2e} (fp16 {rel16:.2e})")
     assert not torch.any(out[2])
+    assert not torch.any(out16[2])
     # dequantisation returns zero vectors for absent slots
     kd, vd = kvq.decode_paged(desc, pool, paging, 0, 1000, torch.float32)
     torch.cuda.synchronize()

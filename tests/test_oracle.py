@@ -24,6 +24,17 @@ def test_splitmix64_published_values():
         state = (state + oc.SPLITMIX_GAMMA) & oc.MASK64
 
 
+def test_signs_equal_worked_vectors():
+    """Sign vectors worked out in bash 64-bit arithmetic from the published SplitMix64
+    definition (tests/golden/layer_signs_worked.sh), including (seed, layer) pairs where
+    seed ^ layer differs from seed + layer."""
+    rows = read_golden("layer_signs.txt")
+    assert len(rows) == 3
+    for seed, layer, d, *signs in rows:
+        got = oc.layer_signs(int(seed), int(layer), int(d))
+        assert got.tolist() == [float(x) for x in signs], (seed, layer)
+
+
 def test_signs_are_pm1_balanced_and_seeded():
     s = oc.layer_signs(0, 0, 4096)
     assert set(np.unique(s)) == {-1.0, 1.0}
