@@ -44,8 +44,9 @@ def parse():
                     help="launch the per-layer attention calls one by one with HIP events "
                          "around each (default: the 32-layer sweep is captured once in a "
                          "HIP graph and replayed)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate oracle CPU time (all cores together) of the baseline "
+                         "sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (used to "
                          "scale rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -64,14 +65,33 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def attn_lds_bytes(d, group, bk, bv, mode):
+    """LDS bytes of one decode-attention variant (the library's own layout: cos/sin
+    tables, rotated query, flag word, then the score table and the waves' value rows,
+    or the merge buffers)."""
+    p = d // 2
+    nw = 8 if mode & 3 == 3 else (12 if mode & 3 and group <= 4 else 8)
+    hg = group // 4 if group > 4 else 1
+    tab = {1: p * (1 << bk) * group * 4, 2: p * (1 << (bk - 1)) * group * 4}.get(mode & 3, 0)
+    rows = nw * (hg * 4 * 64 + 64 * 16) * 4 if mode & 4 else 0
+    merge = nw * group * (d + 2) * 4
+    return (1 << bk) * 8 + (1 << bv) * 8 + group * d * 4 + 16 + max(tab + rows, merge)
+
+
 def attn_kernel_name(d, group, n_k, n_v):
     """Name of the attention-kernel instantiation the library launches for this shape:
-    key-table mode 2 (half table) when n_k is a power of two and half of the
-    P * 2^bk * G * 4-byte score table fits in 128 KiB of LDS, else 1 when the full
-    table fits, else 0."""
+    the score table (half for power-of-two n_k, else full) with the value sum on the
+    matrix cores (mode 6 / 5) for up to four query heads per kv head when both fit in
+    160 KiB of LDS, else the score table with the vector value sum (mode 2 / 1) when it
+    fits, else matrix-core products for both (mode 7)."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
-    full = (d // 2) * (1 << bk) * group * 4
-    mode = 2 if n_k == 1 << bk and full // 2 <= 128 * 1024 else (1 if full <= 128 * 1024 else 0)
+    mode = 7
+    if group <= 4:
+        tab = 2 if n_k == 1 << bk else 1
+        if attn_lds_bytes(d, group, bk, bv, tab | 4) <= 160 * 1024:
+            mode = tab | 4
+        elif attn_lds_bytes(d, group, bk, bv, tab) <= 160 * 1024:
+            mode = tab
     return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {mode}>"
 
 
@@ -102,34 +122,46 @@ def record_bytes(d, n_k, n_v, tokens):
     return tokens * kvq.tile_bytes(d, n_k, n_v) // 64
 
 
-def cpu_baseline(cfg, budget_s):
-    """Time the oracle (as it stands) on a bounded sample of the same workload: decode
-    attention from packed bytes for one (batch, kv head) over a token prefix, and
-    encode of a token sample. Single-threaded BLAS."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_slice(args):
+    """One (layer, batch, kv head) slice of the oracle baseline: encode its K/V token
+    sample, pack the codes into tiles, then decode attention for the G query heads of
+    that kv head from the packed bytes (unpack + dequantise + attention). Runs in a
+    worker process with one BLAS thread."""
+    import time as _time
+
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
 
     from oracle import codec as oc
     from oracle import layout as ol
-    from synthetic import layer_kv, query
+    from synthetic import get, layer_kv, query
 
-    layer = cfg.boosted_layers  # first non-boosted layer
+    name, layer, b, h, tokens = args
+    cfg = get(name)
     n_k, n_v = cfg.bins(layer)
     d, g = cfg.d, cfg.group
-    sg = oc.layer_signs(0, layer, d)
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
-        # a token prefix of one (batch 0, kv head 0) sequence, generated on the CPU
-        tokens = 4096
-        k, v = layer_kv(cfg, layer, "cpu", seq=tokens, batch=1)
-        q = query(cfg, layer, "cpu", batch=1)[:, :g]
-        xk = k[0, :, 0].double().numpy()
-        xv = v[0, :, 0].double().numpy()
-        # encode sample (oracle), then pack with the oracle's packer to get bytes
-        t0 = time.perf_counter()
+        k, v = layer_kv(cfg, layer, "cpu", seq=tokens, batch=b + 1)
+        q = query(cfg, layer, "cpu", batch=b + 1)
+        xk = k[b, :, h].double().numpy()
+        xv = v[b, :, h].double().numpy()
+        qn = q[b:b + 1, h * g:(h + 1) * g].double().numpy()
+        sg = oc.layer_signs(0, layer, d)
+        t0 = _time.perf_counter()
         ek, ev = oc.encode_k(xk, sg, n_k), oc.encode_v(xv, sg, n_v)
-        enc_s = time.perf_counter() - t0
+        enc_s = _time.perf_counter() - t0
         tiles = []
         for t in range(tokens // 64):
             s = slice(t * 64, t * 64 + 64)
@@ -137,26 +169,61 @@ def cpu_baseline(cfg, budget_s):
                                       ek["scale"][s], ev["angle"][s], ev["radius"][s],
                                       ev["s_min"][s], ev["s_max"][s]))
         cache = np.stack(tiles)
-        # decode attention from bytes, repeated to fill the time budget
-        reps, att_s = 0, 0.0
-        qn = q.double().numpy()
-        while att_s < budget_s and reps < 1000:
-            t0 = time.perf_counter()
-            u = ol.unpack_tiles(cache, d, n_k, n_v)
-            u = {kk: vv.reshape((tokens,) + vv.shape[2:]) for kk, vv in u.items()}
-            kh = oc.dequant_k(u["k_angle"], u["k_radius"], u["k_scale"], n_k, sg)
-            vh = oc.dequant_v(u["v_angle"], u["v_radius"], u["v_smin"], u["v_smax"], n_v, sg)
-            oc.attention(qn, kh[None, :, None], vh[None, :, None])
-            att_s += time.perf_counter() - t0
-            reps += 1
-    gbps = reps * record_bytes(d, n_k, n_v, tokens) / att_s / 1e9
+        t0 = _time.perf_counter()
+        u = ol.unpack_tiles(cache, d, n_k, n_v)
+        u = {kk: vv.reshape((tokens,) + vv.shape[2:]) for kk, vv in u.items()}
+        kh = oc.dequant_k(u["k_angle"], u["k_radius"], u["k_scale"], n_k, sg)
+        vh = oc.dequant_v(u["v_angle"], u["v_radius"], u["v_smin"], u["v_smax"], n_v, sg)
+        oc.attention(qn, kh[None, :, None], vh[None, :, None])
+        att_s = _time.perf_counter() - t0
+    return enc_s, att_s, cache.nbytes
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (as it stands) on the host cores, over a bounded sample of the parity
+    subset of the workload: layers {0, first non-boosted, last}, batch entries
+    {0, B - 1}, every kv head, the first `tokens` tokens of each sequence; one worker
+    process per core over independent (layer, batch, kv head) slices. Encode and decode
+    attention (from packed bytes) are timed separately inside each slice; throughputs
+    are the slices' totals over the pool's wall time, scaled by the share of it each
+    phase took."""
+    import multiprocessing as mp
+
+    cores = len(os.sched_getaffinity(0))
+    layers = sorted({0, min(cfg.boosted_layers, cfg.layers - 1), cfg.layers - 1})
+    batches = sorted({0, cfg.batch - 1})
+    # budget_s of oracle CPU time in total: encode and decode attention together cost
+    # the oracle about 25 us per token-head (d = 128, measured on these hosts)
+    slices = len(layers) * len(batches) * cfg.hkv
+    tokens = max(64, min(cfg.seq, int(budget_s / 25e-6 / slices)) // 64 * 64)
+    work = [(cfg.name, layer, b, h, tokens) for layer in layers for b in batches
+            for h in range(cfg.hkv)]
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(processes=cores) as pool:
+        res = pool.map(_oracle_slice, work)
+    wall = time.perf_counter() - t0
+    enc_s = sum(r[0] for r in res)
+    att_s = sum(r[1] for r in res)
+    nbytes = sum(r[2] for r in res)
+    token_heads = tokens * len(work)
+    # independent slices on `cores` workers: the pool's rate is the per-core rate times
+    # the cores (input generation and process start-up are not the oracle's work)
+    enc_wall = enc_s / cores
+    att_wall = att_s / cores
     return {
-        "value": gbps, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{cfg.name} layer {layer}: oracle decode attention from packed bytes "
-                   f"(unpack + dequant + attention for G={g} query heads) over {tokens} "
-                   f"tokens of one (batch, kv head), repeated {reps}x in {att_s:.1f} s; "
-                   f"oracle encode of the same {tokens} K/V token-heads took {enc_s:.2f} s"),
-        "encode_token_heads_per_s": tokens / enc_s,
+        "value": nbytes / att_wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": (f"{cfg.name}: layers {layers}, batch entries {batches}, all {cfg.hkv} kv "
+                   f"heads, first {tokens} tokens each ({len(work)} slices, "
+                   f"{token_heads} token-heads); oracle decode attention from packed bytes "
+                   f"(unpack + dequant + attention for G={cfg.group} query heads) and "
+                   f"oracle encode, one worker process per core; {enc_s + att_s:.1f} s of "
+                   f"oracle CPU time in {wall:.1f} s wall (incl. worker start-up and input "
+                   f"generation); rates = slice totals / (CPU time / cores)"),
+        "decode_token_heads_per_s": token_heads / att_wall,
+        "encode_token_heads_per_s": token_heads / enc_wall,
+        "cpu_seconds": enc_s + att_s,
+        "wall_s": wall,
     }
 
 

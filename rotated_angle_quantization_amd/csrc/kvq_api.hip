@@ -1,6 +1,7 @@
 // C ABI of libkvq: host-side validation, sign generation, sizing and dispatch.
 // Nothing here touches the device before every argument has been checked.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kvq_internal.h"
@@ -75,18 +76,22 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
   return a;
 }
 
-// Whether decode attention uses the LDS key-score table for this shape.
-// Key-table mode of the decode kernel: 1 = full score table in LDS, 2 = half table
-// (n a power of two; rows c >= n/2 are the negated rows c - n/2), 0 = no table.
+// Decode-attention variant for this shape (see attn_mode in kvq_internal.h). Builds
+// with KVQ_ATTN_ALL_MODES compiled in every variant and read KVQ_ATTN_MODE (0-3, 5-7)
+// to force one, for comparisons.
 int key_table_mode(const kvq_layer_desc* d, uint32_t hq) {
   const int g = (int)(hq / d->num_kv_heads);
-  const int bk = code_bits(d->n_bins_k);
-  const long bytes = key_table_bytes((int)d->head_dim, g, bk);
-  // the half table whenever n is a power of two: half the LDS, fewer bank conflicts,
-  // for one extra sign operation per pair
-  if (d->n_bins_k == (1u << bk) && bytes / 2 <= kKeyTableMaxBytes) return 2;
-  if (bytes <= kKeyTableMaxBytes) return 1;
-  return 0;
+  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
+#ifdef KVQ_ATTN_ALL_MODES
+  if (const char* e = getenv("KVQ_ATTN_MODE")) {
+    const int m = atoi(e);
+    const bool half_ok = d->n_bins_k == (1u << bk);
+    if (m >= 0 && m <= 7 && m != 4 && ((m & 3) != 2 || half_ok) &&
+        attn_lds_bytes((int)d->head_dim, g, bk, bv, m) <= kLdsBytesMax)
+      return m;
+  }
+#endif
+  return attn_mode((int)d->head_dim, g, (int)d->n_bins_k, bk, bv);
 }
 
 // Sequence split for decode attention. Each wave of a workgroup streams whole tiles; aim
@@ -187,6 +192,17 @@ kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_
 
 const AppendArgs kNoAppend = {nullptr, nullptr, nullptr, 0, 0, 0, 0, 0.0, 0.0, 0.0};
 
+// Cache, query and output pointers and types of a decode-attention call.
+kvq_status attn_io_check(const void* cache, const void* q, kvq_dtype q_dtype, const void* out,
+                         kvq_dtype out_dtype) {
+  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  return KVQ_OK;
+}
+
 kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg, const void* q,
                     kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len, const uint32_t* seq_lens,
                     float scale, void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
@@ -194,11 +210,8 @@ kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg
   AttnArgs a;
   kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
   if (st != KVQ_OK) return st;
-  if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
-    return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
-  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  st = attn_io_check(cache, q, q_dtype, out, out_dtype);
+  if (st != KVQ_OK) return st;
   a.q = q;
   a.q_f32 = q_dtype == KVQ_F32;
   a.out = out;
@@ -601,3 +614,4 @@ kvq_status kvq_attn_multi_paged(const kvq_layer_desc* d, const void* pool,
 }
 
 }  // extern "C"
+

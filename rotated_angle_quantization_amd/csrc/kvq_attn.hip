@@ -82,11 +82,10 @@ struct TileRegs {
   uint32_t va[C::PPL][C::VAW], vr[C::PPL][2];
 };
 
-// Key planes of one tile (lane = token slot).
-template <int D, int G, int BK, int BV>
-__device__ __forceinline__ void load_tile_keys(TileRegs<D, G, BK, BV>& t, const uint8_t* tp,
-                                               int lane) {
-  using GE = typename SplitCfg<D, G, BK, BV>::GE;
+// Key planes of one tile (lane = token slot); R is either register set below.
+template <int D, int BK, int BV, class R>
+__device__ __forceinline__ void load_tile_keys(R& t, const uint8_t* tp, int lane) {
+  using GE = Geo<D, BK, BV>;
   const uint32_t* w32 = reinterpret_cast<const uint32_t*>(tp);
 #pragma unroll
   for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
@@ -176,9 +175,73 @@ __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
 }
 
+// ---------------------------------------------------------------- matrix-core mode
+//
+// KTM 3: both products of a tile run on the matrix cores in fp32
+// (v_mfma_f32_4x4x1f32: sixteen independent 4x4 blocks, k = 1). Lane 4b + i supplies
+// row i of block b's A operand, lane 4b + j column j of its B operand, and lane 4b + j
+// receives D[b][0..3][j] in its four result registers (checked on the GPU against a host
+// product). With the query heads of a kv head as the four rows:
+//   scores  lane = token: A = q~[head][e] (lane l holds head l & 3), B = the token's
+//           reconstructed rotated key element rho * (cos, sin)[code]; one product per
+//           element e leaves the four heads' scores in the token's lane.
+//   values  lane = pair (d = 128) or pair and token half (d = 64): A = the softmax weight
+//           of token t for head l & 3, B = level(rho) * (cos, sin)[code] of token t in
+//           the lane's pair; the rotated-domain sums of the four heads accumulate in
+//           the pair's lane.
+// Each product is one instruction for 64 (token or pair, head) terms, where the vector
+// path spends one FMA per 16: the VALU keeps only code unpacking, table lookups and the
+// two multiplies per element. Rows past G are zero.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, int G, int BK, int BV>
+struct MxCfg {
+  static constexpr int P = D / 2;
+  static constexpr int HG = G > 4 ? G / 4 : 1;         // groups of four heads (rows)
+  static constexpr int VT = D == 128 ? 64 : 32;        // value tokens per lane
+  static constexpr int VAW = VT * BV / 32;             // value angle words per lane
+  static constexpr int VRW = VT / 8;                   // value radius words per lane
+  // query operands in registers (128 VGPRs at d = 128), unless the extra words of
+  // 8-bit key codes would then spill: then they are read from LDS per pair
+  static constexpr bool QREG = HG * D <= 128 && BK < 8;
+  static constexpr int PS_FLOATS = HG * 4 * kTile;     // per wave: weights [HG][4][64]
+  static constexpr int LEV_FLOATS = kTile * 16;        // per wave: levels [64][16]
+  static constexpr int WAVE_BYTES = (PS_FLOATS + LEV_FLOATS) * 4;
+};
+
+// Registers of one tile in matrix-core mode: key planes with lane = token, value planes
+// with lane = pair (and token half for d = 64), value parameters with lane = token.
+template <int D, int G, int BK, int BV>
+struct MxRegs {
+  using GE = Geo<D, BK, BV>;
+  using M = MxCfg<D, G, BK, BV>;
+  uint32_t ka[GE::WKA], kr[GE::WKR], ks, vp;
+  uint32_t va[M::VAW], vr[M::VRW];
+};
+
+template <int D, int G, int BK, int BV>
+__device__ __forceinline__ void load_tile_values_mx(MxRegs<D, G, BK, BV>& t, const uint8_t* tp,
+                                                    int lane) {
+  using GE = Geo<D, BK, BV>;
+  using M = MxCfg<D, G, BK, BV>;
+  constexpr int P = D / 2;
+  const uint32_t* w32 = reinterpret_cast<const uint32_t*>(tp);
+  const int pr = lane & (P - 1), th = D == 128 ? 0 : lane >> 5;
+  t.vp = w32[GE::OFF_VP / 4 + lane];
+#pragma unroll
+  for (int w = 0; w < M::VAW; ++w) t.va[w] = w32[GE::OFF_VA / 4 + (th * M::VAW + w) * P + pr];
+#pragma unroll
+  for (int w = 0; w < M::VRW; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + (th * M::VRW + w) * P + pr];
+}
+
 // Waves per split workgroup: 12 (three per SIMD) when the key table is used with up to
-// four heads per kv head, which leaves the kernel under 168 VGPRs; otherwise 8.
-constexpr int split_waves(bool key_table, int group) { return key_table && group <= 4 ? 12 : 8; }
+// four heads per kv head, which leaves the kernel under 168 VGPRs; 8 in matrix-core mode
+// (two per SIMD: the query operands take 128 VGPRs) and otherwise.
+constexpr int split_waves(int ktm, int group) { return attn_waves(ktm, group); }
 
 // One workgroup per (split, batch * kv head). KTM (key-table mode) 1: scores read a
 // per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n)
@@ -188,23 +251,32 @@ constexpr int split_waves(bool key_table, int group) { return key_table && group
 // pair, and it admits n = 256 at four heads. KTM 0: scores use the cos/sin table and the
 // rotated query from scalar registers.
 template <int D, int G, int BK, int BV, int KTM>
-__global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_kernel(
+__global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot,
     AppendArgs app) {
   using C = SplitCfg<D, G, BK, BV>;
   using GE = typename C::GE;
-  constexpr bool KT = KTM != 0, HALF = KTM == 2;
-  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KT, G);
+  using M = MxCfg<D, G, BK, BV>;
+  // Key mode (KTM & 3): 0 scalar-loaded query, 1 full score table, 2 half score table,
+  // 3 matrix cores; bit 2 of KTM: values on the matrix cores. KT: the query is rotated
+  // in the kernel; TAB: scores from the LDS score table.
+  constexpr int KMODE = KTM & 3;
+  constexpr bool KT = KMODE != 0, HALF = KMODE == 2, MXK = KMODE == 3, TAB = KT && !MXK;
+  constexpr bool MXV = (KTM & 4) != 0, MX = MXK || MXV;
+  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KTM, G);
   constexpr int NTAB = HALF ? NKT / 2 : NKT;  // table rows per pair
-  constexpr int TAB_BYTES = P * NTAB * G * 4;
+  // LDS used during the tile loop: the score table, then the waves' value rows
+  constexpr int TAB_BYTES = (TAB ? P * NTAB * G * 4 : 0) + (MXV ? NW * M::WAVE_BYTES : 0);
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
-  constexpr int UNION_BYTES = (KT && TAB_BYTES > MERGE_BYTES) ? TAB_BYTES : MERGE_BYTES;
+  constexpr int UNION_BYTES = TAB_BYTES > MERGE_BYTES ? TAB_BYTES : MERGE_BYTES;
   // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
   // instruction's immediate offset; then the rotated query (later the normalised
   // output), a flag, and the key table (or the merge buffers)
   constexpr int LUTK_OFF = 0, LUTV_OFF = NKT * 8, Q_OFF = LUTV_OFF + (1 << BV) * 8;
   constexpr int FLAG_OFF = Q_OFF + G * D * 4, UNION_OFF = FLAG_OFF + 16;
   __shared__ __align__(16) char smem[UNION_OFF + UNION_BYTES];
+  static_assert(UNION_OFF + UNION_BYTES == attn_lds_bytes(D, G, BK, BV, KTM),
+                "LDS layout and its host-side model disagree");
   float2* lut_k = reinterpret_cast<float2*>(smem + LUTK_OFF);
   float2* lut_v = reinterpret_cast<float2*>(smem + LUTV_OFF);
   float* s_q = reinterpret_cast<float*>(smem + Q_OFF);  // [G][D]
@@ -278,7 +350,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       owner = split == 0 && wave == 0;
     }
   }
-  TileRegs<D, G, BK, BV> cur;
+  std::conditional_t<MXV, MxRegs<D, G, BK, BV>, TileRegs<D, G, BK, BV>> cur;
   int tile = tile_begin + wave;
   auto first_tile_keys = [&]() {
     const int t0 = min(tile, tile_end - 1);
@@ -287,7 +359,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       const int page = ptab[t0];
       idx = page >= 0 && page < a.pg.num_pages ? page : 0;
     }
-    load_tile_keys(cur, base + idx * stride, lane);
+    load_tile_keys<D, BK, BV>(cur, base + idx * stride, lane);
   };
   if (!owner) first_tile_keys();
   if (KT) {
@@ -309,7 +381,7 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   }
   __syncthreads();
   float* ktab = reinterpret_cast<float*>(s_union);
-  if (KT) {
+  if (TAB) {
     // NW*64 threads: each owns one pair (q~ loaded once) and a stride of codes
     constexpr int TPP = NW * 64 / P;  // threads per pair
     const int i = tid / TPP, c0 = tid % TPP;
@@ -391,6 +463,40 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
 #pragma unroll
     for (int j = 0; j < PPL; ++j) acc[g][j] = make_float2(0.f, 0.f);
   }
+  // matrix-core mode: rotated-domain sums (cosine and sine elements; lane = pair, result
+  // register = head), query operands (lane l: head l & 3 of each group of four), and
+  // the wave's LDS rows of softmax weights [HG][4][64] and radius levels [64][16]
+  f32x4 ax[M::HG], ay[M::HG];
+  float qr[MXK && M::QREG ? M::HG : 1][MXK && M::QREG ? D : 1];
+  const float* q_row[M::HG];
+  // the waves' value rows follow the score table, if any
+  float* w_ps = reinterpret_cast<float*>(s_union) + (TAB ? P * NTAB * G : 0) +
+                wave * (M::WAVE_BYTES / 4);
+  float* w_lev = w_ps + M::PS_FLOATS;
+  if constexpr (MX) {
+#pragma unroll
+    for (int hg = 0; hg < M::HG; ++hg) {
+      ax[hg] = ay[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int h = 4 * hg + (lane & 3);
+      q_row[hg] = s_q + min(h, G - 1) * D;
+      if constexpr (MXK && M::QREG) {
+#pragma unroll
+        for (int e = 0; e < D; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(q_row[hg] + e);
+          const bool on = h < G;  // rows past the group's heads stay zero
+          qr[hg][e] = on ? v.x : 0.f;
+          qr[hg][e + 1] = on ? v.y : 0.f;
+          qr[hg][e + 2] = on ? v.z : 0.f;
+          qr[hg][e + 3] = on ? v.w : 0.f;
+        }
+      }
+      // weight rows of heads past G are zero for the whole launch
+      if constexpr (MXV) {
+#pragma unroll
+        for (int g = G; g < 4 * M::HG; ++g) w_ps[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = 0.f;
+      }
+    }
+  }
 
   for (; tile < tile_end; tile += NW) {
     // No register double-buffering: several waves per SIMD cover each other's load
@@ -404,18 +510,46 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       idx = present ? page : 0;
     }
     const uint8_t* tp = base + idx * stride;
-    if (tile != tile_begin + wave) load_tile_keys(cur, tp, lane);
+    if (tile != tile_begin + wave) load_tile_keys<D, BK, BV>(cur, tp, lane);
     // opaque to the compiler, which otherwise specialises the whole tile body on an
     // absent tile and runs out of registers
     int nvalid = present ? min(seq_len - tile * kTile, kTile) : 0;
     asm volatile("" : "+s"(nvalid));
     const bool valid = lane < nvalid;
 
-    // ---- keys: lane = token slot
+    // ---- keys: lane = token slot; sc[g] = the score of head g before the key scale
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
-    if (KT) {
+    if constexpr (MXK) {
+      // matrix cores: two chains, the cosine and the sine elements of each pair
+      f32x4 sx[M::HG], sy[M::HG];
+#pragma unroll
+      for (int hg = 0; hg < M::HG; ++hg) sx[hg] = sy[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const uint32_t c = field<BK>(cur.ka, i);
+        const float2 cs = lut_k[c];
+        const float rho = (float)((cur.kr[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        const float bx = rho * cs.x, by = rho * cs.y;
+#pragma unroll
+        for (int hg = 0; hg < M::HG; ++hg) {
+          float qa, qb;
+          if constexpr (M::QREG) {
+            qa = qr[hg][2 * i];
+            qb = qr[hg][2 * i + 1];
+          } else {
+            const float2 qv = reinterpret_cast<const float2*>(q_row[hg])[i];
+            qa = qv.x;
+            qb = qv.y;
+          }
+          sx[hg] = mfma4x4(qa, bx, sx[hg]);
+          sy[hg] = mfma4x4(qb, by, sy[hg]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[g] = sx[g >> 2][g & 3] + sy[g >> 2][g & 3];
+    } else if constexpr (TAB) {
       // Software pipeline over blocks of KB pairs: the table reads of block b + 1 are
       // issued before the FMAs of block b, so the LDS latency overlaps arithmetic
       // (the scheduling fences keep the compiler from re-serialising them).
@@ -468,12 +602,16 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
         }
       }
     }
-    load_tile_values(cur, tp, lane, row, col);
+    if constexpr (MXV)
+      load_tile_values_mx(cur, tp, lane);
+    else
+      load_tile_values(cur, tp, lane, row, col);
     const float kscale = __half2float(__ushort_as_half((uint16_t)cur.ks));
 
-    // ---- softmax weights; pr = p * r0 with the value vector's base radius r0 (s_min,
-    // or s_max when s_max <= s_min); slots past the end get 0
-    float pr[G];
+    // ---- this lane's token's value radius: level(rho) = r0 2^(rho beta) with
+    // r0 = s_min and beta = log2(s_max / s_min) / 15, or r0 = s_max and beta = 0 when
+    // s_max <= s_min; r0 = 0 for slots past the end. Matrix-core values tabulate the 16
+    // levels in the wave's LDS rows; the vector path folds r0 into the weights.
     float beta = 0.f, r0 = 0.f;
     {
       const float smin = __half2float(__ushort_as_half((uint16_t)(cur.vp & 0xFFFFu)));
@@ -488,73 +626,120 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
         beta = 0.f;
       }
     }
+    if constexpr (MXV) {
+      float4* dst = reinterpret_cast<float4*>(w_lev + lane * 16);
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        dst[r / 4] = make_float4(r0 * fast_exp2((float)r * beta), r0 * fast_exp2((float)(r + 1) * beta),
+                                 r0 * fast_exp2((float)(r + 2) * beta),
+                                 r0 * fast_exp2((float)(r + 3) * beta));
+    }
+
+    // ---- online softmax per head (lane = token), base 2; slots past the end get 0
+    float pr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float s = valid ? sc[g] * kscale : -INFINITY;
-      {
-        const float mnew = fmaxf(m[g], wave_max(s));
-        // no token seen yet (only tiles of absent pages): nothing to rescale
-        const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[g] - mnew);
-        l[g] *= alpha;
+      const float mnew = fmaxf(m[g], wave_max(s));
+      // no token seen yet (only tiles of absent pages): nothing to rescale
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[g] - mnew);
+      l[g] *= alpha;
+      if constexpr (MXV) {
+        ax[g >> 2][g & 3] *= alpha;
+        ay[g >> 2][g & 3] *= alpha;
+      } else {
 #pragma unroll
         for (int j = 0; j < PPL; ++j) {
           acc[g][j].x *= alpha;
           acc[g][j].y *= alpha;
         }
-        m[g] = mnew;
       }
+      m[g] = mnew;
       const float pv = m[g] == -INFINITY ? 0.f : fast_exp2(s - m[g]);
       l[g] += pv;
       pr[g] = pv * r0;
+      if constexpr (MXV) w_ps[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = pv;
     }
 
-    // ---- values: lane (row, col); step k handles token slot 16 row + k
-    uint32_t va[PPL][C::VAW];
+    if constexpr (MXV) {
+      // The wave's own LDS rows are read back by other lanes of the wave: LDS operations
+      // of a wave complete in order, so only the compiler must keep them in order.
+      asm volatile("" ::: "memory");
+      // ---- values on the matrix cores: lane = pair (and token half for d = 64); one
+      // product per token of the lane's half, weights of four tokens per LDS read
+      const int th = D == 128 ? 0 : lane >> 5;
 #pragma unroll
-    for (int j = 0; j < PPL; ++j) {
+      for (int t4 = 0; t4 < M::VT / 4; ++t4) {
+        float4 pa[M::HG];
 #pragma unroll
-      for (int w = 0; w < C::VAW; ++w) {
-        if (BV & 1)
-          va[j][w] = w + 1 < C::VAW ? __builtin_amdgcn_alignbit(cur.va[j][w + 1], cur.va[j][w], vshift)
-                                    : (cur.va[j][w] >> vshift);
-        else
-          va[j][w] = cur.va[j][w];
+        for (int hg = 0; hg < M::HG; ++hg)
+          pa[hg] = *reinterpret_cast<const float4*>(
+              w_ps + hg * 4 * kTile + (lane & 3) * kTile + th * 32 + 4 * t4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = 4 * t4 + u;
+          const float2 cs = lut_v[field<BV>(cur.va, t)];
+          const uint32_t rho = (cur.vr[t >> 3] >> (4 * (t & 7))) & 0xFu;
+          const float lvl = w_lev[(th * 32 + t) * 16 + rho];
+          const float vx = lvl * cs.x, vy = lvl * cs.y;
+#pragma unroll
+          for (int hg = 0; hg < M::HG; ++hg) {
+            const float pw = u == 0 ? pa[hg].x : u == 1 ? pa[hg].y : u == 2 ? pa[hg].z : pa[hg].w;
+            ax[hg] = mfma4x4(pw, vx, ax[hg]);
+            ay[hg] = mfma4x4(pw, vy, ay[hg]);
+          }
+        }
       }
-    }
-    // Radius levels: at step k the 16 lanes of a row compute the 16 possible radii
-    // 2^(level * beta) of their token (lane col takes level col), and each lane gathers
-    // the levels of its pairs with a lane permute. The gather addresses are bytes
-    // 4 * (16 row + level): low nibbles (even slots) and high nibbles (odd slots).
-    uint32_t alo[PPL][2], ahi[PPL][2];
-    const uint32_t rowb = 0x01010101u * (uint32_t)(64 * row);
-#pragma unroll
-    for (int j = 0; j < PPL; ++j) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        alo[j][w] = ((cur.vr[j][w] & 0x0F0F0F0Fu) << 2) | rowb;
-        ahi[j][w] = ((cur.vr[j][w] >> 2) & 0x3C3C3C3Cu) | rowb;
-      }
-    }
-    const float colf = (float)col;
-#pragma unroll
-    for (int k = 0; k < kStepTokens; ++k) {
-      // token slot 16 row + k: its softmax weights and radius step broadcast along the
-      // row with DPP; the lane's level gathered from the row's 16 computed levels
-      float pj[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) pj[g] = row_bcast(pr[g], k);
-      const float lev = fast_exp2(colf * row_bcast(beta, k));
+      asm volatile("" ::: "memory");  // the next tile's LDS writes stay after these reads
+    } else {
+      // ---- values: lane (row, col); step k handles token slot 16 row + k
+      uint32_t va[PPL][C::VAW];
 #pragma unroll
       for (int j = 0; j < PPL; ++j) {
-        const float2 cs = lut_v[field<BV>(va[j], k)];
-        const uint32_t aw = (k & 1) ? ahi[j][k >> 3] : alo[j][k >> 3];
-        // the permute reads only address bits 2..7, so the byte needs no masking
-        const float r = bperm_f((int)(aw >> (8 * ((k >> 1) & 3))), lev);
-        const float vx = r * cs.x, vy = r * cs.y;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          acc[g][j].x = fmaf(pj[g], vx, acc[g][j].x);
-          acc[g][j].y = fmaf(pj[g], vy, acc[g][j].y);
+        for (int w = 0; w < C::VAW; ++w) {
+          if (BV & 1)
+            va[j][w] = w + 1 < C::VAW ? __builtin_amdgcn_alignbit(cur.va[j][w + 1], cur.va[j][w], vshift)
+                                      : (cur.va[j][w] >> vshift);
+          else
+            va[j][w] = cur.va[j][w];
+        }
+      }
+      // Radius levels: at step k the 16 lanes of a row compute the 16 possible radii
+      // 2^(level * beta) of their token (lane col takes level col), and each lane gathers
+      // the levels of its pairs with a lane permute. The gather addresses are bytes
+      // 4 * (16 row + level): low nibbles (even slots) and high nibbles (odd slots).
+      uint32_t alo[PPL][2], ahi[PPL][2];
+      const uint32_t rowb = 0x01010101u * (uint32_t)(64 * row);
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          alo[j][w] = ((cur.vr[j][w] & 0x0F0F0F0Fu) << 2) | rowb;
+          ahi[j][w] = ((cur.vr[j][w] >> 2) & 0x3C3C3C3Cu) | rowb;
+        }
+      }
+      const float colf = (float)col;
+#pragma unroll
+      for (int k = 0; k < kStepTokens; ++k) {
+        // token slot 16 row + k: its softmax weights and radius step broadcast along the
+        // row with DPP; the lane's level gathered from the row's 16 computed levels
+        float pj[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pj[g] = row_bcast(pr[g], k);
+        const float lev = fast_exp2(colf * row_bcast(beta, k));
+#pragma unroll
+        for (int j = 0; j < PPL; ++j) {
+          const float2 cs = lut_v[field<BV>(va[j], k)];
+          const uint32_t aw = (k & 1) ? ahi[j][k >> 3] : alo[j][k >> 3];
+          // the permute reads only address bits 2..7, so the byte needs no masking
+          const float r = bperm_f((int)(aw >> (8 * ((k >> 1) & 3))), lev);
+          const float vx = r * cs.x, vy = r * cs.y;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            acc[g][j].x = fmaf(pj[g], vx, acc[g][j].x);
+            acc[g][j].y = fmaf(pj[g], vy, acc[g][j].y);
+          }
         }
       }
     }
@@ -562,15 +747,28 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
 #pragma unroll
   for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
 
-  // ---- rows hold partial sums for the same pairs: fold them into row 0
+  if constexpr (MXV) {
+    // d = 64: the two token halves hold partial sums of the same pairs
+    if constexpr (D == 64) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+      for (int hg = 0; hg < M::HG; ++hg)
 #pragma unroll
-    for (int j = 0; j < PPL; ++j) {
-      acc[g][j].x += __shfl_xor(acc[g][j].x, 16);
-      acc[g][j].y += __shfl_xor(acc[g][j].y, 16);
-      acc[g][j].x += __shfl_xor(acc[g][j].x, 32);
-      acc[g][j].y += __shfl_xor(acc[g][j].y, 32);
+        for (int r = 0; r < 4; ++r) {
+          ax[hg][r] += __shfl_xor(ax[hg][r], 32);
+          ay[hg][r] += __shfl_xor(ay[hg][r], 32);
+        }
+    }
+  } else {
+    // ---- rows hold partial sums for the same pairs: fold them into row 0
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        acc[g][j].x += __shfl_xor(acc[g][j].x, 16);
+        acc[g][j].y += __shfl_xor(acc[g][j].y, 16);
+        acc[g][j].x += __shfl_xor(acc[g][j].x, 32);
+        acc[g][j].y += __shfl_xor(acc[g][j].y, 32);
+      }
     }
   }
   __syncthreads();  // every wave is done with the key table; reuse it for merging
@@ -583,7 +781,14 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
       s_ml[(wave * G + g) * 2 + 1] = l[g];
     }
   }
-  if (row == 0) {
+  if constexpr (MXV) {
+    if (lane < P) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        *reinterpret_cast<float2*>(s_acc + (wave * G + g) * D + 2 * lane) =
+            make_float2(ax[g >> 2][g & 3], ay[g >> 2][g & 3]);
+    }
+  } else if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -691,28 +896,42 @@ __global__ __launch_bounds__(split_waves(KTM != 0, G) * 64) void attn_decode_ker
   if (tid == 0) __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+template <int D, int G, int BK, int BV, int MODE>
+hipError_t launch_mode(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
+                       hipStream_t s) {
+  if constexpr (attn_lds_bytes(D, G, BK, BV, MODE) <= kLdsBytesMax) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, MODE>), grid,
+                       dim3(split_waves(MODE, G) * 64), 0, s, a, cache, a.qrot, app);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+// Launches the variant the host selected (a.key_table). Only the variants the host can
+// select are compiled: those attn_mode gives for this code width (power-of-two n or
+// not).
 template <int D, int G, int BK, int BV>
 hipError_t decode_launch(const AttnArgs& a, const AppendArgs& app, const uint8_t* cache, dim3 grid,
                     hipStream_t s) {
-  constexpr long full = SplitCfg<D, G, BK, BV>::TAB_BYTES;
-  if constexpr (full <= kKeyTableMaxBytes) {
-    if (a.key_table == 1) {
-      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 1>), grid,
-                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot, app);
-      return hipGetLastError();
-    }
+  constexpr int m_pow2 = attn_mode(D, G, 1 << BK, BK, BV);
+  constexpr int m_other = attn_mode(D, G, (1 << BK) - 1, BK, BV);
+  if (a.key_table == m_pow2) return launch_mode<D, G, BK, BV, m_pow2>(a, app, cache, grid, s);
+  if constexpr (m_other != m_pow2) {
+    if (a.key_table == m_other) return launch_mode<D, G, BK, BV, m_other>(a, app, cache, grid, s);
   }
-  if constexpr (full / 2 <= kKeyTableMaxBytes) {
-    if (a.key_table == 2) {
-      hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 2>), grid,
-                         dim3(split_waves(true, G) * 64), 0, s, a, cache, a.qrot, app);
-      return hipGetLastError();
-    }
+#ifdef KVQ_ATTN_ALL_MODES
+  switch (a.key_table) {
+    case 0: return launch_mode<D, G, BK, BV, 0>(a, app, cache, grid, s);
+    case 1: return launch_mode<D, G, BK, BV, 1>(a, app, cache, grid, s);
+    case 2: return launch_mode<D, G, BK, BV, 2>(a, app, cache, grid, s);
+    case 3: return launch_mode<D, G, BK, BV, 3>(a, app, cache, grid, s);
+    case 5: return launch_mode<D, G, BK, BV, 5>(a, app, cache, grid, s);
+    case 6: return launch_mode<D, G, BK, BV, 6>(a, app, cache, grid, s);
+    case 7: return launch_mode<D, G, BK, BV, 7>(a, app, cache, grid, s);
+    default: break;
   }
-  if (a.key_table) return hipErrorInvalidValue;  // host and kernel disagree on the table
-  hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, 0>), grid,
-                     dim3(split_waves(false, G) * 64), 0, s, a, cache, a.qrot, app);
-  return hipGetLastError();
+#endif
+  return hipErrorInvalidValue;  // host and kernel disagree on the variant
 }
 
 template <int D, int G, int BK>
@@ -754,7 +973,7 @@ hipError_t decode_g(const AttnArgs& a, const AppendArgs& app, const uint8_t* cac
 hipError_t launch_attn_decode(const AttnArgs& a, const AppendArgs& app, int d,
                               const uint8_t* cache, hipStream_t stream) {
   if (d != 64 && d != 128) return hipErrorInvalidValue;
-  if (!a.key_table) {
+  if ((a.key_table & 3) == 0) {  // scores read the rotated query from the workspace
     const dim3 pgrid((unsigned)(a.batch * a.hq));
     if (d == 64)
       hipLaunchKernelGGL(attn_prepare_kernel<64>, pgrid, dim3(64), 0, stream, a);

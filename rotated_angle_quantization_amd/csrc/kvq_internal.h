@@ -121,6 +121,41 @@ struct AttnArgs {
 constexpr int kKeyTableMaxBytes = 128 * 1024;
 inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (1L << bk) * group * 4; }
 
+// Decode-attention kernel variants ("mode"): bits 0-1 choose how scores are formed
+// (0: rotated query through scalar loads, 1: full LDS score table, 2: half score table
+// for power-of-two n, 3: matrix-core products), bit 2 puts the value sum on the matrix
+// cores. The LDS a variant needs mirrors the kernel's own layout (cos/sin tables, the
+// rotated query, a flag word, then the score table and the waves' value rows, or the
+// merge buffers after the tile loop).
+constexpr int kLdsBytesMax = 160 * 1024;
+constexpr int attn_waves(int mode, int group) {
+  return (mode & 3) == 3 ? 8 : ((mode & 3) != 0 && group <= 4 ? 12 : 8);
+}
+constexpr long attn_lds_bytes(int d, int group, int bk, int bv, int mode) {
+  const int p = d / 2, nw = attn_waves(mode, group);
+  const int hg = group > 4 ? group / 4 : 1;
+  const long tab = (mode & 3) == 1 ? (long)p * (1 << bk) * group * 4
+                   : (mode & 3) == 2 ? (long)p * (1 << (bk - 1)) * group * 4 : 0;
+  const long rows = (mode & 4) ? (long)nw * (hg * 4 * 64 + 64 * 16) * 4 : 0;
+  const long merge = (long)nw * group * (d + 2) * 4;
+  const long loop = tab + rows;
+  return (1L << bk) * 8 + (1L << bv) * 8 + (long)group * d * 4 + 16 + (loop > merge ? loop : merge);
+}
+// The variant run for a shape (n_k a power of two admits the half table), as measured
+// fastest on MI355X: for up to four heads per kv head, the score table with the value
+// sum on the matrix cores when both fit in LDS, else the score table with the vector
+// value sum (8-bit key codes at four heads: the 128 KiB half table leaves no room for
+// the value rows); for eight heads, and when no table fits, the matrix cores for both.
+constexpr int attn_mode(int d, int group, int n_k, int bk, int bv) {
+  const bool pow2 = n_k == (1 << bk);
+  if (group <= 4) {
+    const int tabmode = pow2 ? 2 : 1;
+    if (attn_lds_bytes(d, group, bk, bv, tabmode | 4) <= kLdsBytesMax) return tabmode | 4;
+    if (attn_lds_bytes(d, group, bk, bv, tabmode) <= kLdsBytesMax) return tabmode;
+  }
+  return 3 | 4;
+}
+
 // Fused append of decode attention: the new token of sequence b (K/V rows at
 // k / v + b * sb + h * sh elements, d contiguous) is coded into slot positions[b] before
 // that slot's tile is read; the sequence attends to min(positions[b] + 1, seq_len)

@@ -24,20 +24,26 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_cpu_baseline_is_the_oracle_on_a_bounded_sample():
-    out = bench.cpu_baseline(get("mistral7b"), 0.2)
-    assert out["kind"] == "oracle" and out["unit"] == "GB/s" and out["cores"] == 1
-    assert out["value"] > 0 and "4096 tokens" in out["sample"]
+    out = bench.cpu_baseline(get("tinyllama"), 0.01)
+    assert out["kind"] == "oracle" and out["unit"] == "GB/s"
+    assert out["cores"] == len(os.sched_getaffinity(0))
+    assert out["value"] > 0 and out["decode_token_heads_per_s"] > 0
+    assert out["encode_token_heads_per_s"] > 0 and out["cpu_model"]
+    assert "layers [0, 21]" in out["sample"] and "first 64 tokens" in out["sample"]
     json.dumps(out)
 
 
 @pytest.mark.parametrize("d,g,nk,nv,name", [
-    (128, 4, 128, 64, "attn_decode_kernel<128, 4, 7, 6, 2>"),     # half table
-    (128, 4, 256, 256, "attn_decode_kernel<128, 4, 8, 8, 2>"),
-    (128, 4, 100, 40, "attn_decode_kernel<128, 4, 7, 6, 1>"),     # full table
-    (128, 8, 200, 256, "attn_decode_kernel<128, 8, 8, 8, 0>"),    # no table
-    (64, 8, 128, 64, "attn_decode_kernel<64, 8, 7, 6, 2>"),
+    (128, 4, 128, 64, "attn_decode_kernel<128, 4, 7, 6, 6>"),     # half table + MFMA values
+    (128, 4, 256, 256, "attn_decode_kernel<128, 4, 8, 8, 2>"),    # half table, vector values
+    (128, 4, 100, 40, "attn_decode_kernel<128, 4, 7, 6, 1>"),     # full table, vector values
+    (128, 4, 200, 40, "attn_decode_kernel<128, 4, 8, 6, 7>"),     # no table fits: MFMA
+    (128, 2, 100, 40, "attn_decode_kernel<128, 2, 7, 6, 5>"),     # full table + MFMA values
+    (128, 8, 200, 256, "attn_decode_kernel<128, 8, 8, 8, 7>"),
+    (64, 8, 128, 64, "attn_decode_kernel<64, 8, 7, 6, 7>"),
+    (64, 4, 128, 64, "attn_decode_kernel<64, 4, 7, 6, 6>"),
 ])
-def test_kernel_name_follows_the_key_table_rule(d, g, nk, nv, name):
+def test_kernel_name_follows_the_variant_rule(d, g, nk, nv, name):
     assert bench.attn_kernel_name(d, g, nk, nv) == name
 
 
