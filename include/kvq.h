@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 7
+#define KVQ_ABI_VERSION 8
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -362,6 +362,27 @@ kvq_status kvq_attn_multi_paged(const kvq_layer_desc* desc, const void* pool,
                                 const uint32_t* seq_lens, uint32_t max_seq_len,
                                 float softmax_scale, void* out, kvq_dtype out_dtype,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Allocation-free decode attention, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): kvq_attn_decode with its workspace taken from a fixed device
+ * array inside this library, kvq_attn_static_scratch_bytes() = 8 MiB on each GPU the
+ * library runs on (held until the process ends; its address is looked up once per
+ * device). Arguments, results and errors are those of kvq_attn_decode, except that a
+ * shape whose kvq_attn_workspace_bytes exceeds the array returns KVQ_ERR_WORKSPACE
+ * before any device work. The call enqueues a small fill kernel that zeroes the split
+ * counters, then the attention kernel; it allocates nothing. All calls on one GPU share
+ * its array, which keeps the last call's contents: calls that may overlap on one GPU
+ * (different streams, or concurrent host threads) race and must be serialised by the
+ * caller.
+ */
+size_t kvq_attn_static_scratch_bytes(void);
+
+kvq_status kvq_attn_decode_static(const kvq_layer_desc* desc, const void* cache, const void* q,
+                                  kvq_dtype q_dtype, uint32_t num_q_heads, uint32_t seq_len,
+                                  float softmax_scale, void* out, kvq_dtype out_dtype,
+                                  void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
  * this shape (host only; 0 if the arguments are invalid). Each split covers a whole

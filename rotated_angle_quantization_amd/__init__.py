@@ -9,7 +9,8 @@ from ._lib import (  # noqa: F401
     EXPORTS, KVQ_F16, KVQ_F32, KvqError, LayerDesc, Paging, abi_version, alloc_cache, append,
     append_paged, attn_decode_append, attn_decode_paged, decode_paged, encode_paged, make_paging,
     paged_pool_bytes,
-    alloc_workspace, attn_decode, attn_decode_varlen, attn_multi, attn_multi_workspace_bytes,
+    alloc_workspace, attn_decode, attn_decode_static, attn_decode_varlen, attn_multi,
+    attn_multi_workspace_bytes, attn_static_scratch_bytes,
     attn_num_splits,
     attn_workspace_bytes, cache_bytes, decode, default_scale, encode, layer_signs, lib,
     make_desc, tile_bytes)

@@ -95,6 +95,9 @@ _SIGS = {
                                              _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
                                       ctypes.c_int, _v, _sz, _v]),
+    "kvq_attn_static_scratch_bytes": (_sz, []),
+    "kvq_attn_decode_static": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
+                                              ctypes.c_int, _v]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -326,6 +329,27 @@ def attn_decode(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: 
                                out.data_ptr(), _dtype_code(out), workspace.data_ptr(),
                                workspace.numel(), _stream(q.device)), "kvq_attn_decode")
     return out
+
+
+def attn_decode_static(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor, seq_len: int,
+                       softmax_scale: float = 0.0, out_dtype=None, out=None):
+    """attn_decode without a workspace (kvq_attn_decode_static): the library's own fixed
+    device scratch array serves as the workspace; nothing is allocated when out is
+    given. Calls that may overlap on one GPU must be serialised by the caller."""
+    _query(desc, q)
+    _layer_cache(desc, cache)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("q", q), ("out", out))
+    out = _attn_out(out, q.shape, out_dtype, q)
+    _check(lib.kvq_attn_decode_static(ctypes.byref(desc), cache.data_ptr(), q.data_ptr(),
+                                      _dtype_code(q), q.shape[1], seq_len, float(softmax_scale),
+                                      out.data_ptr(), _dtype_code(out), _stream(q.device)),
+           "kvq_attn_decode_static")
+    return out
+
+
+def attn_static_scratch_bytes() -> int:
+    return lib.kvq_attn_static_scratch_bytes()
 
 
 def attn_decode_varlen(desc: LayerDesc, cache: torch.Tensor, q: torch.Tensor,

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -615,3 +617,73 @@ kvq_status kvq_attn_multi_paged(const kvq_layer_desc* d, const void* pool,
 
 }  // extern "C"
 
+// ------------------------------------------------------------ allocation-free variant
+//
+// For callers that cannot allocate device memory (code under graph capture, tight
+// serving loops, harnesses that forbid allocation): kvq_attn_decode with the workspace
+// taken from a fixed-size device array of this library, one copy per GPU (each device
+// holds its own copy at its own address, looked up once per device with
+// hipGetSymbolAddress and kept). Every call on a GPU shares that GPU's array.
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+constexpr int kScratchDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Zero-fills the split counters at the start of the workspace (a kernel rather than a
+// memset, so the call can also be recorded into a graph).
+__global__ void zero_words_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch array (looked up on first use per
+// device; relaxed atomics: threads that race on the first call store the same value).
+hipError_t scratch_address(void** out) {
+  static std::atomic<void*> addr[kScratchDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_relaxed);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_attn_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+kvq_status kvq_attn_decode_static(const kvq_layer_desc* d, const void* cache, const void* q,
+                                  kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len,
+                                  float scale, void* out, kvq_dtype out_dtype, void* stream) {
+  // every argument is checked before the first HIP call
+  kvq_status st = attn_check(d, hq, seq_len);
+  if (st != KVQ_OK) return st;
+  st = attn_io_check(cache, q, q_dtype, out, out_dtype);
+  if (st != KVQ_OK) return st;
+  const size_t need = kvq_attn_workspace_bytes(d, hq, seq_len);
+  if (need == 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (need > kStaticScratchBytes) return KVQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return KVQ_ERR_HIP;
+  // the split counters must read zero; the array keeps the last call's contents
+  const int words = (int)(d->batch * d->num_kv_heads);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, static_cast<unsigned*>(ws), words);
+  if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  return attn_run(d, cache, kNoPaging, q, q_dtype, hq, seq_len, nullptr, scale, out, out_dtype,
+                  ws, need, stream);
+}
+
+}  // extern "C"

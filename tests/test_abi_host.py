@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 7
+    assert kvq.abi_version() == 8
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -282,3 +282,20 @@ def test_fused_append_attention_validation():
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(None, 4, 10))) == INVALID
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
     assert _fused(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
+
+
+def test_static_scratch_entry_point_rejects_before_any_device_work():
+    """kvq_attn_decode_static: argument errors and shapes whose workspace exceeds the
+    fixed scratch array are rejected on the host (no HIP call is reached)."""
+    assert kvq.attn_static_scratch_bytes() == 8 << 20
+    f = lib.kvq_attn_decode_static
+    small = kvq.make_desc(128, 2, 1, 256, 128, 64)
+    assert f(ctypes.byref(small), FAKE, None, 0, 8, 256, 0.0, FAKE, 0, None) == INVALID
+    assert f(ctypes.byref(small), FAKE + 8, FAKE, 0, 8, 256, 0.0, FAKE, 0, None) == INVALID
+    assert f(ctypes.byref(small), FAKE, FAKE, 0, 8, 300, 0.0, FAKE, 0, None) == CAPACITY
+    assert f(ctypes.byref(small), FAKE, FAKE, 0, 48, 256, 0.0, FAKE, 0, None) == UNSUPPORTED
+    # 256 sequences x 8 kv heads x 64 query heads: partials of 16 MiB > 8 MiB
+    big = kvq.make_desc(128, 8, 256, 8192, 128, 64)
+    need = kvq.attn_workspace_bytes(big, 64, 8192)
+    assert need > kvq.attn_static_scratch_bytes()
+    assert f(ctypes.byref(big), FAKE, FAKE, 0, 64, 8192, 0.0, FAKE, 0, None) == WORKSPACE
