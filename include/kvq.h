@@ -166,7 +166,9 @@ kvq_status kvq_append(const kvq_layer_desc* desc, void* cache, const void* k, co
                       const uint32_t* positions, void* hip_stream);
 
 /*
- * Dequantise tokens [t0, t0 + ntok) back to vectors: x_hat = sign * H_d y_hat / sqrt(d)
+ * Dequantise tokens [t0, t0 + ntok) back to vectors, inverting the encoding of
+ * "TurboAngle: Near-Lossless KV Cache Compression via Uniform Angle Quantization"
+ * (arXiv 2603.27467), Abstract: x_hat = sign * H_d y_hat / sqrt(d)
  * with y_hat[2i] = r_hat cos(2 pi c / n), y_hat[2i+1] = r_hat sin(2 pi c / n);
  * key r_hat = code * s / 255; value r_hat = s_min * exp(code * L / 15) (s_max when
  * s_max <= s_min). Arithmetic in fp32.
@@ -179,7 +181,11 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
                       void* hip_stream);
 
 /*
- * Decode attention for one new query token per sequence, straight from the codes:
+ * Decode attention for one new query token per sequence, straight from the codes of
+ * "TurboAngle: Near-Lossless KV Cache Compression via Uniform Angle Quantization"
+ * (arXiv 2603.27467), Abstract, reconstructing keys and values on the fly without
+ * writing a dequantised cache ("OCTOPUS: Joint Triplet Quantization for KV Cache via
+ * Octahedral Parametrization", Why it matters):
  *   o[b, h] = sum_j softmax_j(scale <q[b, h], k_hat[b, j, h/G]>) v_hat[b, j, h/G]
  * over j < seq_len, G = Hq / Hkv (grouped-query attention: query head h reads kv
  * head floor(h / G)). Scores are formed in the rotated domain (the query is rotated
@@ -199,7 +205,8 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  *   counters back at zero). It holds the rotated queries and split partials. Calls
  *   that share one workspace must not run concurrently (one stream).
  * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; angle codes of 6 to 8 bits
- *   (n in [33, 256]) for K and V; 1 <= seq_len <= capacity.
+ *   (n in [33, 256]) for K and V; 1 <= seq_len <= capacity. kvq_attn_workspace_bytes
+ *   returns 0 for shapes outside this set (and for invalid arguments).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
  */
 size_t kvq_attn_workspace_bytes(const kvq_layer_desc* desc, uint32_t num_q_heads,
@@ -385,8 +392,8 @@ kvq_status kvq_attn_decode_static(const kvq_layer_desc* desc, const void* cache,
                                   void* hip_stream);
 
 /* Number of sequence splits (workgroups per (batch, kv head)) kvq_attn_decode uses for
- * this shape (host only; 0 if the arguments are invalid). Each split covers a whole
- * number of 64-token tiles. */
+ * this shape (host only; 0 if the arguments are invalid or the shape is one decode
+ * attention does not serve). Each split covers a whole number of 64-token tiles. */
 uint32_t kvq_attn_num_splits(const kvq_layer_desc* desc, uint32_t num_q_heads,
                              uint32_t seq_len);
 

@@ -294,7 +294,11 @@ def alloc_workspace(desc: LayerDesc, num_q_heads: int, seq_len: int, device="cud
     between calls, so it can be reused for any later call that fits)."""
     n = attn_workspace_bytes(desc, num_q_heads, seq_len)
     if n == 0:
-        raise KvqError(1, "kvq_attn_workspace_bytes")
+        # the shape's own status (INVALID_ARGUMENT, UNSUPPORTED or CAPACITY): the library
+        # checks the shape before any pointer, so null pointers reach no device work
+        st = lib.kvq_attn_decode(ctypes.byref(desc), None, None, KVQ_F16, num_q_heads, seq_len,
+                                 0.0, None, KVQ_F16, None, 0, None)
+        raise KvqError(st if st else 1, "kvq_attn_workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 

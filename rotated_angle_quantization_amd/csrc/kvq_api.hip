@@ -422,8 +422,7 @@ kvq_status kvq_decode_paged(const kvq_layer_desc* d, const void* pool, const kvq
 }
 
 uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
-  if (!desc_ok(d) || hq == 0 || hq % d->num_kv_heads || seq_len == 0 || seq_len > d->capacity)
-    return 0;
+  if (attn_check(d, hq, seq_len) != KVQ_OK) return 0;  // invalid or not served
   int nsplit, tps;
   split_plan(d->batch * d->num_kv_heads, seq_len, key_table_mode(d, hq) != 0, &nsplit, &tps);
   return (uint32_t)nsplit;

@@ -299,3 +299,25 @@ def test_static_scratch_entry_point_rejects_before_any_device_work():
     need = kvq.attn_workspace_bytes(big, 64, 8192)
     assert need > kvq.attn_static_scratch_bytes()
     assert f(ctypes.byref(big), FAKE, FAKE, 0, 64, 8192, 0.0, FAKE, 0, None) == WORKSPACE
+
+
+def test_sizes_are_zero_for_shapes_attention_does_not_serve():
+    """Workspace and split helpers agree with kvq_attn_decode: 0 where it would return
+    UNSUPPORTED (5-bit codes, G = 16, d = 256) or INVALID."""
+    ok = kvq.make_desc(128, 2, 1, 256, 128, 64)
+    assert kvq.attn_workspace_bytes(ok, 8, 256) > 0
+    for desc, hq in ((kvq.make_desc(128, 2, 1, 256, 32, 64), 8),     # 5-bit key codes
+                     (kvq.make_desc(128, 2, 1, 256, 128, 17), 8),    # 5-bit value codes
+                     (kvq.make_desc(128, 2, 1, 256, 128, 64), 32),   # G = 16
+                     (kvq.make_desc(256, 2, 1, 256, 128, 64), 8),    # d = 256
+                     (kvq.make_desc(128, 2, 1, 256, 128, 64), 7)):   # Hq not a multiple
+        assert kvq.attn_workspace_bytes(desc, hq, 256) == 0
+        assert kvq.attn_num_splits(desc, hq, 256) == 0
+    assert kvq.tile_bytes(32, 128, 64) == 0  # d = 32: key bit strings would split words
+
+
+def test_workspace_helper_reports_the_shape_status():
+    with pytest.raises(kvq.KvqError, match="UNSUPPORTED"):
+        kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 32, 64), 8, 256, "cpu")
+    with pytest.raises(kvq.KvqError, match="CAPACITY"):
+        kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 128, 64), 8, 300, "cpu")
