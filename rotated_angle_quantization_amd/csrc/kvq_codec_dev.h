@@ -36,21 +36,23 @@ __device__ __forceinline__ uint16_t fp16_bits(double exact_fp16_value) {
   return __half_as_ushort(__float2half_rn((float)exact_fp16_value));
 }
 
-// atan(z) on [0, 1]: odd polynomial z * sum_k c_k z^2k, least-squares fitted to atan
-// (measured maximum error 2.5e-7 rad on [0, 1]; 3.5e-7 rad evaluated in fp32).
+// atan(z) on [0, 1]: odd polynomial z * sum_k c_k z^2k, the minimax fit to atan on a
+// dense grid (Lawson's reweighted least squares) rounded to fp32, as printed by
+// fit_atan01.py beside this file: maximum error 2.5e-7 rad in exact arithmetic, 3.3e-7
+// rad evaluated in fp32 as below.
 __device__ __forceinline__ float atan01(float z) {
   const float s = z * z;
-  float p = 0.006806020624935627f;
-  p = fmaf(p, s, -0.03358602523803711f);
-  p = fmaf(p, s, 0.07960157096385956f);
-  p = fmaf(p, s, -0.13232044875621796f);
-  p = fmaf(p, s, 0.19807438552379608f);
-  p = fmaf(p, s, -0.3331731855869293f);
-  p = fmaf(p, s, 0.9999960660934448f);
+  float p = 0.006811870262026787f;
+  p = fmaf(p, s, -0.0336044542491436f);
+  p = fmaf(p, s, 0.07962393760681152f);
+  p = fmaf(p, s, -0.13233356177806854f);
+  p = fmaf(p, s, 0.1980782002210617f);
+  p = fmaf(p, s, -0.3331736922264099f);
+  p = fmaf(p, s, 0.9999961256980896f);
   return p * z;
 }
 
-// Angle of a nonzero pair in fp32, by octant reduction: |error| <= 3.5e-7 (polynomial)
+// Angle of a nonzero pair in fp32, by octant reduction: |error| <= 3.3e-7 (polynomial)
 // + 1.2e-7 (z = min/max through the reciprocal) + 6e-8 (rounding the pair to fp32)
 // + 2.4e-7 (the two reflections about pi/2 and pi) < 8e-7 rad. The reflections and the
 // sign use the fp32 values' sign bits (exact: rounding keeps the sign).
