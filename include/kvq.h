@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 8
+#define KVQ_ABI_VERSION 9
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -396,6 +396,112 @@ kvq_status kvq_attn_decode_static(const kvq_layer_desc* desc, const void* cache,
  * attention does not serve). Each split covers a whole number of 64-token tiles. */
 uint32_t kvq_attn_num_splits(const kvq_layer_desc* desc, uint32_t num_q_heads,
                              uint32_t seq_len);
+
+/* ===================================================================================
+ * Triplet (octahedral) codec: the variant summarised for "OCTOPUS: Joint Triplet
+ * Quantization for KV Cache via Octahedral Parametrization" (TL;DR, What is new). After
+ * the same seeded sign diagonal and normalised Walsh-Hadamard transform, a vector y is
+ * scaled to unit length by its norm N (stored as fp16); its coordinates are taken three
+ * at a time; each triplet's direction goes to the square [-1, 1]^2 through the
+ * octahedral parametrisation, and the two square coordinates and the triplet's norm are
+ * quantised with Lloyd-Max quantisers fitted to the exact marginals these quantities
+ * have for a uniformly random unit vector (the page's "implementation-matched
+ * marginals"); the 1 or 2 coordinates left over (d = 64 or 128) get a Lloyd-Max
+ * quantiser of their own. The bit split between direction and norm is a parameter.
+ * Readings of the open steps:
+ *  - octahedral map: p = w / |w|_1; p3 >= 0 keeps (p1, p2), otherwise the point folds to
+ *    ((1 - |p2|) sgn p1, (1 - |p1|) sgn p2), sgn(0) = +1; a zero triplet maps to (0, 0);
+ *  - marginals: square coordinate f(s) = [2(1-s)/(2s^2+(1-s)^2) + 2s/(s^2+2(1-s)^2)]
+ *    / sqrt(s^2+(1-s)^2) for s = |s| (up to a constant); triplet norm
+ *    r^2 (1 - r^2)^((d-5)/2) on [0, 1]; one coordinate (1 - u^2)^((d-3)/2) on [-1, 1];
+ *  - Lloyd-Max: the fixed point of the centroid conditions (every level the conditional
+ *    mean of its cell, boundaries at midpoints), started at the (i + 1/2) / 2^b
+ *    quantiles and solved to a residual of 1e-15; cell integrals by 40-point
+ *    Gauss-Legendre rules, cells split at 0 for the symmetric densities; a value takes
+ *    the nearest level, the lower one at an exact midpoint;
+ *  - reconstruction: N_hat rho_hat w_hat per triplet (w_hat = the inverse octahedral
+ *    map of the two levels, normalised), N_hat u_hat per leftover coordinate, then the
+ *    inverse rotation; keys and values use the same codec.
+ * =================================================================================== */
+
+/*
+ * One triplet-coded layer.
+ *  head_dim           64 or 128.
+ *  num_kv_heads, batch, capacity   as in kvq_layer_desc.
+ *  bits_dir           bits of each of the two square coordinates, 1..6.
+ *  bits_norm          bits of the triplet norm, 1..6.
+ *  bits_rest          bits of each leftover coordinate, 1..8.
+ *  layer, seed        select the sign diagonal (kvq_layer_signs).
+ */
+typedef struct {
+  uint32_t head_dim;
+  uint32_t num_kv_heads;
+  uint32_t batch;
+  uint32_t capacity;
+  uint32_t bits_dir;
+  uint32_t bits_norm;
+  uint32_t bits_rest;
+  uint32_t layer;
+  uint64_t seed;
+} kvq_tri_desc;
+
+/*
+ * Sizes (host only; 0 for an invalid descriptor). A token-head record is the bit string
+ * (LSB-first in 32-bit words): the fp16 bits of N in [0, 16), then triplet j's fields at
+ * 16 + j * (2 bits_dir + bits_norm): s code, t code, norm code (in that order, each
+ * LSB-first), then the leftover codes of bits_rest bits; padded to whole words. A tile of
+ * 64 slots holds the key plane then the value plane, each word-interleaved by slot (word
+ * w of slot t at 4 (w * 64 + t)); the cache is [batch][kv head][tile][tile bytes].
+ */
+uint32_t kvq_tri_record_words(const kvq_tri_desc* desc);
+size_t kvq_tri_tile_bytes(const kvq_tri_desc* desc);
+size_t kvq_tri_cache_bytes(const kvq_tri_desc* desc);
+
+/*
+ * The layer's quantisers (host only): writes kvq_tri_codebook_doubles(desc) doubles to
+ * out_host: the square-coordinate levels (2^bits_dir), the norm levels (2^bits_norm),
+ * the leftover levels (2^bits_rest), then the three sets of decision boundaries
+ * (2^b - 1 each, the midpoints), all ascending. Computed on the host by Newton's method
+ * on the Lloyd-Max centroid conditions (milliseconds to a few seconds); the caller keeps
+ * the table in device memory and passes it to the calls below. Depends only on
+ * (head_dim, bits).
+ */
+size_t kvq_tri_codebook_doubles(const kvq_tri_desc* desc);
+kvq_status kvq_tri_codebook(const kvq_tri_desc* desc, double* out_host);
+
+/*
+ * Encode K/V tokens [t0, t0 + ntok) (inputs as for kvq_encode: [B, ntok, Hkv, d],
+ * strides in elements, d contiguous, fp16 or fp32). The transform, N, the triplet norms,
+ * the square coordinates and every decision are taken in IEEE binary64. codebook: the
+ * device copy of kvq_tri_codebook's table. Slots outside the range keep their bytes.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (d not 64/128), CAPACITY, HIP.
+ */
+kvq_status kvq_tri_encode(const kvq_tri_desc* desc, void* cache, const double* codebook,
+                          const void* k, const void* v, kvq_dtype in_dtype, int64_t stride_b,
+                          int64_t stride_t, int64_t stride_h, uint32_t t0, uint32_t ntok,
+                          void* hip_stream);
+
+/* Dequantise tokens [t0, t0 + ntok) to contiguous [B, ntok, Hkv, d] outputs (fp32
+ * arithmetic). Errors as kvq_tri_encode. */
+kvq_status kvq_tri_decode(const kvq_tri_desc* desc, const void* cache, const double* codebook,
+                          void* k_out, void* v_out, kvq_dtype out_dtype, uint32_t t0,
+                          uint32_t ntok, void* hip_stream);
+
+/*
+ * Decode attention over a triplet-coded cache: the definition of kvq_attn_decode with
+ * keys and values reconstructed from the triplet codes (rotated domain, one inverse
+ * transform per output). Two launches: the splits write partial (max, sum, vector)
+ * triples to the workspace, then a merge kernel combines them. The workspace
+ * (kvq_tri_attn_workspace_bytes, 256-byte aligned) needs no initialisation. G in
+ * {1, 2, 4, 8}. Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
+ */
+size_t kvq_tri_attn_workspace_bytes(const kvq_tri_desc* desc, uint32_t num_q_heads,
+                                    uint32_t seq_len);
+kvq_status kvq_tri_attn_decode(const kvq_tri_desc* desc, const void* cache,
+                               const double* codebook, const void* q, kvq_dtype q_dtype,
+                               uint32_t num_q_heads, uint32_t seq_len, float softmax_scale,
+                               void* out, kvq_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

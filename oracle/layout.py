@@ -225,3 +225,81 @@ def unpack_cache(cache: np.ndarray, d, n_k, n_v, batch, hkv, capacity, t0, ntok)
         v = v[:, :, t0 - lo * TILE:t0 - lo * TILE + ntok]
         out[k] = np.ascontiguousarray(np.swapaxes(v, 1, 2))
     return out
+
+
+# ----------------------------------------------------------------------------------
+# Triplet codec records (the layout defined at kvq_tri_desc in include/kvq.h): one
+# token-head record is a little-endian bit string of 32-bit words: the fp16 bits of the
+# vector norm in [0, 16), then for triplet j < T = d // 3 the s code, t code and norm
+# code (b_dir, b_dir, b_norm bits) at 16 + j (2 b_dir + b_norm), then the leftover codes
+# (b_rest bits each); padded to whole words. A tile of 64 slots is the key plane then the
+# value plane, each [word][slot] (word w of slot t at 4 (w * 64 + t)).
+# ----------------------------------------------------------------------------------
+
+
+def tri_record_words(d: int, b_dir: int, b_norm: int, b_rest: int) -> int:
+    t = d // 3
+    return -(-(16 + t * (2 * b_dir + b_norm) + (d - 3 * t) * b_rest) // 32)
+
+
+def tri_tile_bytes(d, b_dir, b_norm, b_rest) -> int:
+    return 2 * tri_record_words(d, b_dir, b_norm, b_rest) * TILE * 4
+
+
+def tri_record_bits(codes: dict, d: int, b_dir: int, b_norm: int, b_rest: int) -> int:
+    """One record as a Python integer (bit i = bit i of the record)."""
+    t = d // 3
+    width = 2 * b_dir + b_norm
+    val = int(codes["scale_bits"])
+    for j in range(t):
+        f = int(codes["s_code"][j]) | (int(codes["t_code"][j]) << b_dir) | \
+            (int(codes["norm_code"][j]) << (2 * b_dir))
+        val |= f << (16 + j * width)
+    for r in range(d - 3 * t):
+        val |= int(codes["rest_code"][r]) << (16 + t * width + r * b_rest)
+    return val
+
+
+def tri_unpack_tiles(tiles: np.ndarray, d, b_dir, b_norm, b_rest) -> dict:
+    """tiles: uint8 [..., tile_bytes] -> codes of both planes, arrays [..., 64, ...]:
+    k_/v_ s_code, t_code, norm_code [.., 64, T], rest_code [.., 64, d - 3T],
+    scale (fp16 values, float64) [.., 64]."""
+    words = tri_record_words(d, b_dir, b_norm, b_rest)
+    tb = tri_tile_bytes(d, b_dir, b_norm, b_rest)
+    lead = tiles.shape[:-1]
+    w32 = np.ascontiguousarray(tiles).reshape(-1, tb).view("<u4").reshape(-1, 2, words, TILE)
+    t = d // 3
+    width = 2 * b_dir + b_norm
+    out = {}
+    for p, name in ((0, "k"), (1, "v")):
+        rec = w32[:, p].astype(np.uint64)  # [n, words, 64]
+
+        def field(off, wd):
+            wi, sh = off // 32, off % 32
+            lo = rec[:, wi, :]
+            hi = rec[:, wi + 1, :] if wi + 1 < words else np.zeros_like(lo)
+            return (((hi << np.uint64(32)) | lo) >> np.uint64(sh)) & np.uint64((1 << wd) - 1)
+
+        f = np.stack([field(16 + j * width, width) for j in range(t)], axis=-1).astype(np.int64)
+        rest = [field(16 + t * width + r * b_rest, b_rest) for r in range(d - 3 * t)]
+        out[f"{name}_s_code"] = (f & ((1 << b_dir) - 1)).reshape(lead + (TILE, t))
+        out[f"{name}_t_code"] = ((f >> b_dir) & ((1 << b_dir) - 1)).reshape(lead + (TILE, t))
+        out[f"{name}_norm_code"] = (f >> (2 * b_dir)).reshape(lead + (TILE, t))
+        out[f"{name}_rest_code"] = np.stack(rest, axis=-1).astype(np.int64).reshape(lead + (TILE, d - 3 * t))
+        bits = (rec[:, 0, :] & np.uint64(0xFFFF)).astype(np.uint16)
+        out[f"{name}_scale"] = bits.view(np.float16).astype(np.float64).reshape(lead + (TILE,))
+    return out
+
+
+def tri_unpack_cache(cache, d, b_dir, b_norm, b_rest, batch, hkv, capacity, t0, ntok) -> dict:
+    """Codes of tokens [t0, t0 + ntok) of a triplet-coded cache, arrays
+    [batch, ntok, hkv, ...] (the token-major order of the inputs)."""
+    tb = tri_tile_bytes(d, b_dir, b_norm, b_rest)
+    tiles = -(-capacity // TILE)
+    c = np.asarray(cache, dtype=np.uint8)[: batch * hkv * tiles * tb].reshape(batch, hkv, tiles, tb)
+    u = tri_unpack_tiles(c, d, b_dir, b_norm, b_rest)
+    out = {}
+    for key, val in u.items():
+        val = val.reshape((batch, hkv, tiles * TILE) + val.shape[4:])[:, :, t0:t0 + ntok]
+        out[key] = np.moveaxis(val, 1, 2)
+    return out

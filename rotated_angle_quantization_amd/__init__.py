@@ -13,4 +13,7 @@ from ._lib import (  # noqa: F401
     attn_multi_workspace_bytes, attn_static_scratch_bytes,
     attn_num_splits,
     attn_workspace_bytes, cache_bytes, decode, default_scale, encode, layer_signs, lib,
-    make_desc, tile_bytes)
+    make_desc, tile_bytes,
+    TriDesc, alloc_tri_cache, make_tri_desc, tri_attn_decode, tri_attn_workspace_bytes,
+    tri_cache_bytes, tri_codebook, tri_codebook_device, tri_decode, tri_encode,
+    tri_record_words, tri_tile_bytes)

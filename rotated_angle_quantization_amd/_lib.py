@@ -40,6 +40,22 @@ class LayerDesc(ctypes.Structure):
                 f"layer={self.layer}, seed={self.seed})")
 
 
+class TriDesc(ctypes.Structure):
+    """kvq_tri_desc: one triplet-coded layer (head dim 64/128, bits per square coordinate,
+    per triplet norm and per leftover coordinate)."""
+
+    _fields_ = [("head_dim", ctypes.c_uint32), ("num_kv_heads", ctypes.c_uint32),
+                ("batch", ctypes.c_uint32), ("capacity", ctypes.c_uint32),
+                ("bits_dir", ctypes.c_uint32), ("bits_norm", ctypes.c_uint32),
+                ("bits_rest", ctypes.c_uint32), ("layer", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
+
+    def __repr__(self):
+        return (f"TriDesc(d={self.head_dim}, hkv={self.num_kv_heads}, B={self.batch}, "
+                f"cap={self.capacity}, bits=({self.bits_dir},{self.bits_norm},"
+                f"{self.bits_rest}), layer={self.layer}, seed={self.seed})")
+
+
 class Paging(ctypes.Structure):
     """kvq_paging: page table (device int32 [batch][pages_per_seq]) of a paged cache."""
 
@@ -55,6 +71,7 @@ class KvqError(RuntimeError):
 
 
 _P = ctypes.POINTER(LayerDesc)
+_PT = ctypes.POINTER(TriDesc)
 _v = ctypes.c_void_p
 _u32, _u64, _i64, _f32, _sz = (ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
                                ctypes.c_float, ctypes.c_size_t)
@@ -95,6 +112,17 @@ _SIGS = {
                                              _f32, _v, ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_multi": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _u32, _f32, _v,
                                       ctypes.c_int, _v, _sz, _v]),
+    "kvq_tri_record_words": (_u32, [_PT]),
+    "kvq_tri_tile_bytes": (_sz, [_PT]),
+    "kvq_tri_cache_bytes": (_sz, [_PT]),
+    "kvq_tri_codebook_doubles": (_sz, [_PT]),
+    "kvq_tri_codebook": (ctypes.c_int, [_PT, ctypes.POINTER(ctypes.c_double)]),
+    "kvq_tri_encode": (ctypes.c_int, [_PT, _v, _v, _v, _v, ctypes.c_int, _i64, _i64, _i64, _u32,
+                                      _u32, _v]),
+    "kvq_tri_decode": (ctypes.c_int, [_PT, _v, _v, _v, _v, ctypes.c_int, _u32, _u32, _v]),
+    "kvq_tri_attn_workspace_bytes": (_sz, [_PT, _u32, _u32]),
+    "kvq_tri_attn_decode": (ctypes.c_int, [_PT, _v, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
+                                           ctypes.c_int, _v, _sz, _v]),
     "kvq_attn_static_scratch_bytes": (_sz, []),
     "kvq_attn_decode_static": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
                                               ctypes.c_int, _v]),
@@ -559,3 +587,115 @@ def attn_decode_append(desc: LayerDesc, cache: torch.Tensor, k: torch.Tensor, v:
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# ------------------------------------------------------------------ triplet codec
+
+
+def make_tri_desc(head_dim, num_kv_heads, batch, capacity, bits_dir, bits_norm, bits_rest,
+                  layer=0, seed=0) -> TriDesc:
+    return TriDesc(head_dim, num_kv_heads, batch, capacity, bits_dir, bits_norm, bits_rest,
+                   layer, seed)
+
+
+def tri_cache_bytes(desc: TriDesc) -> int:
+    return lib.kvq_tri_cache_bytes(ctypes.byref(desc))
+
+
+def tri_tile_bytes(desc: TriDesc) -> int:
+    return lib.kvq_tri_tile_bytes(ctypes.byref(desc))
+
+
+def tri_record_words(desc: TriDesc) -> int:
+    return lib.kvq_tri_record_words(ctypes.byref(desc))
+
+
+def tri_codebook(desc: TriDesc):
+    """The layer's Lloyd-Max tables as computed by the library on the host (a float64
+    numpy array; see kvq_tri_codebook for its order)."""
+    import numpy as np
+    n = lib.kvq_tri_codebook_doubles(ctypes.byref(desc))
+    if n == 0:
+        raise KvqError(1, "kvq_tri_codebook_doubles")
+    buf = (ctypes.c_double * n)()
+    _check(lib.kvq_tri_codebook(ctypes.byref(desc), buf), "kvq_tri_codebook")
+    return np.frombuffer(buf, dtype=np.float64).copy()
+
+
+def tri_codebook_device(desc: TriDesc, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(tri_codebook(desc)).to(device)
+
+
+def alloc_tri_cache(desc: TriDesc, device="cuda") -> torch.Tensor:
+    n = tri_cache_bytes(desc)
+    if n == 0:
+        raise KvqError(1, "kvq_tri_cache_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _tri_cache(desc, cache, codebook) -> None:
+    n = tri_cache_bytes(desc)
+    _need(n > 0, f"invalid triplet descriptor {desc!r}")
+    _byte_buffer(cache, "cache", n)
+    nd = lib.kvq_tri_codebook_doubles(ctypes.byref(desc))
+    _need(isinstance(codebook, torch.Tensor) and codebook.dtype == torch.float64
+          and codebook.is_contiguous() and codebook.numel() == nd,
+          f"codebook must be the contiguous float64 table of {nd} values (tri_codebook_device)")
+
+
+def tri_encode(desc: TriDesc, cache: torch.Tensor, codebook: torch.Tensor, k: torch.Tensor,
+               v: torch.Tensor, t0: int = 0) -> None:
+    """Triplet-code K/V tokens [t0, t0 + ntok): k, v [B, ntok, Hkv, d], d contiguous."""
+    _need(isinstance(k, torch.Tensor) and k.dim() == 4, "k/v must be [B, ntok, Hkv, d]")
+    ntok = k.shape[1]
+    _kv_rows(k, v, (desc.batch, ntok, desc.num_kv_heads, desc.head_dim))
+    _tri_cache(desc, cache, codebook)
+    _same_device(("cache", cache), ("codebook", codebook), ("k", k), ("v", v))
+    _check(lib.kvq_tri_encode(ctypes.byref(desc), cache.data_ptr(), codebook.data_ptr(),
+                              k.data_ptr(), v.data_ptr(), _dtype_code(k), k.stride(0),
+                              k.stride(1), k.stride(2), t0, ntok, _stream(cache.device)),
+           "kvq_tri_encode")
+
+
+def tri_decode(desc: TriDesc, cache: torch.Tensor, codebook: torch.Tensor, t0: int, ntok: int,
+               out_dtype=torch.float16):
+    """Dequantise tokens [t0, t0 + ntok) -> (k_hat, v_hat), each [B, ntok, Hkv, d]."""
+    _tri_cache(desc, cache, codebook)
+    _same_device(("cache", cache), ("codebook", codebook))
+    shape = (desc.batch, ntok, desc.num_kv_heads, desc.head_dim)
+    k_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
+    v_out = torch.empty(shape, dtype=out_dtype, device=cache.device)
+    _check(lib.kvq_tri_decode(ctypes.byref(desc), cache.data_ptr(), codebook.data_ptr(),
+                              k_out.data_ptr(), v_out.data_ptr(), _dtype_code(k_out), t0, ntok,
+                              _stream(cache.device)), "kvq_tri_decode")
+    return k_out, v_out
+
+
+def tri_attn_workspace_bytes(desc: TriDesc, num_q_heads: int, seq_len: int) -> int:
+    return lib.kvq_tri_attn_workspace_bytes(ctypes.byref(desc), num_q_heads, seq_len)
+
+
+def tri_attn_decode(desc: TriDesc, cache: torch.Tensor, codebook: torch.Tensor, q: torch.Tensor,
+                    seq_len: int, softmax_scale: float = 0.0, out_dtype=None, workspace=None,
+                    out=None):
+    """Decode attention over a triplet-coded cache: q [B, Hq, d] -> [B, Hq, d]."""
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3, "q must be [B, Hq, d]")
+    hq = q.shape[1]
+    _float_tensor(q, "q", (desc.batch, hq, desc.head_dim))
+    _tri_cache(desc, cache, codebook)
+    _check_out(out, q.shape)
+    _same_device(("cache", cache), ("codebook", codebook), ("q", q), ("out", out),
+                 ("workspace", workspace))
+    out = _attn_out(out, q.shape, out_dtype, q)
+    n = tri_attn_workspace_bytes(desc, hq, seq_len)
+    if n == 0:
+        raise KvqError(2, "kvq_tri_attn_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _byte_buffer(workspace, "workspace", n)
+    _check(lib.kvq_tri_attn_decode(ctypes.byref(desc), cache.data_ptr(), codebook.data_ptr(),
+                                   q.data_ptr(), _dtype_code(q), hq, seq_len,
+                                   float(softmax_scale), out.data_ptr(), _dtype_code(out),
+                                   workspace.data_ptr(), workspace.numel(), _stream(q.device)),
+           "kvq_tri_attn_decode")
+    return out

@@ -1,0 +1,968 @@
+// Triplet (octahedral) codec: encode, dequantise and decode attention, plus the host
+// side of its C ABI (the Lloyd-Max quantisers are computed here, on the host).
+//
+// Method: "OCTOPUS: Joint Triplet Quantization for KV Cache via Octahedral
+// Parametrization" (TL;DR, What is new): rotated coordinates are quantised three at a
+// time; a triplet's direction goes to the square [-1, 1]^2 through the octahedral
+// parametrisation, and the two square coordinates and the triplet norm are Lloyd-Max
+// quantised against the marginals these quantities actually have after the rotation.
+// The rotation is the angle codec's (seeded sign diagonal, normalised Walsh-Hadamard
+// transform), and the readings of the steps the page leaves open are stated at the
+// declarations in kvq.h.
+//
+// Kernels (one wave per token-head for the codec; the lane maps follow the data):
+//   encode     lane i holds elements 2i, 2i+1 through the binary64 transform; lane j then
+//              gathers triplet j (or leftover coordinate j - T) with lane permutes, takes
+//              its decisions in binary64 against the boundaries in LDS, and lane w packs
+//              record word w from the fields of the lanes that overlap it.
+//   decode     lane j rebuilds its triplet (or leftover) in fp32 from the levels, the
+//              elements are permuted back to two per lane for the inverse transform.
+//   attention  split kernel (grid: splits x batch * kv heads, four waves, a wave per
+//              64-token tile): scores with one lane per token, the key plane staged in
+//              LDS and a table of the 2^(2 bits_dir) reconstructed directions; online
+//              softmax per wave; values with one lane per triplet, summing
+//              p * N * rho * w over the tile's tokens; waves merge in LDS and each split
+//              writes (max, sum, rotated vector) per query head. A merge kernel (a wave
+//              per output row) combines the splits with a log-sum-exp and applies the
+//              inverse transform. Far more arithmetic per byte than the angle codec (a
+//              few bits per element): this path is bound by VALU and LDS work.
+#include <math.h>
+#include <string.h>
+
+#include <cmath>
+#include <vector>
+
+#include "kvq_attn_common.h"
+#include "kvq_codec_dev.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kTriMaxLevelsDir = 64, kTriMaxLevelsNorm = 64, kTriMaxLevelsRest = 256;
+
+// Geometry of one configuration (device and host).
+struct TriGeom {
+  int d, T, R;           // head dim, triplets, leftover coordinates
+  int bd, bn, br, B;     // field widths; B = 2 bd + bn
+  int words;             // record words per token-head
+  int nd, nn, nr;        // levels per quantiser
+};
+
+__host__ __device__ inline TriGeom tri_geom(int d, int bd, int bn, int br) {
+  TriGeom g;
+  g.d = d;
+  g.T = d / 3;
+  g.R = d - 3 * g.T;
+  g.bd = bd;
+  g.bn = bn;
+  g.br = br;
+  g.B = 2 * bd + bn;
+  g.words = (16 + g.T * g.B + g.R * br + 31) / 32;
+  g.nd = 1 << bd;
+  g.nn = 1 << bn;
+  g.nr = 1 << br;
+  return g;
+}
+
+// Bit offset and width of field f (f < T: triplet f; f >= T: leftover f - T).
+__host__ __device__ inline int field_off(const TriGeom& g, int f) {
+  return f < g.T ? 16 + f * g.B : 16 + g.T * g.B + (f - g.T) * g.br;
+}
+__host__ __device__ inline int field_width(const TriGeom& g, int f) { return f < g.T ? g.B : g.br; }
+
+struct TriArgs {
+  TriGeom g;
+  int batch, hkv, tiles_per_seq;
+  int t0, ntok;
+  double inv_sqrt_d;
+  SignMask sign;
+  const double* cb;  // codebook: levels dir, norm, rest; then bounds dir, norm, rest
+};
+
+__device__ inline int cb_bounds_off(const TriGeom& g) { return g.nd + g.nn + g.nr; }
+
+// Number of boundaries below x (the nearest level; the lower one at an exact midpoint).
+__device__ __forceinline__ int nearest(const double* bounds, int n_levels, double x) {
+  int lo = 0, hi = n_levels - 1;  // count in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (bounds[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ double sgn64(double x) { return x < 0.0 ? -1.0 : 1.0; }
+__device__ __forceinline__ float sgn32(float x) { return x < 0.f ? -1.f : 1.f; }
+
+template <class Tv>
+__device__ __forceinline__ Tv shfl_t(Tv v, int src) { return __shfl(v, src, 64); }
+
+// ------------------------------------------------------------------------------ encode
+
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cache, const void* k,
+                                                         const void* v, int64_t sb, int64_t st,
+                                                         int64_t sh) {
+  constexpr int P = D / 2;
+  const TriGeom& g = a.g;
+  __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
+  const int bo = cb_bounds_off(g);
+  for (int i = threadIdx.x; i < g.nd - 1; i += 256) s_bd[i] = a.cb[bo + i];
+  for (int i = threadIdx.x; i < g.nn - 1; i += 256) s_bn[i] = a.cb[bo + g.nd - 1 + i];
+  for (int i = threadIdx.x; i < g.nr - 1; i += 256) s_br[i] = a.cb[bo + g.nd - 1 + g.nn - 1 + i];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long total = (long long)a.batch * a.ntok * a.hkv;
+  if (item >= total) return;
+  const int h = (int)(item % a.hkv);
+  const long long bj = item / a.hkv;
+  const int j = (int)(bj % a.ntok), b = (int)(bj / a.ntok);
+  const int slot = a.t0 + j, tile = slot / kTile, t = slot % kTile;
+  const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
+  uint32_t* tp = reinterpret_cast<uint32_t*>(
+      cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * tile_bytes);
+  const int i = lane & (P - 1);  // pair held by this lane
+  const int e0 = 2 * i;
+  const int nf = g.T + g.R;
+
+#pragma unroll 1
+  for (int kv = 0; kv < 2; ++kv) {
+    const char* src = static_cast<const char*>(kv == 0 ? k : v) +
+                      ((size_t)b * sb + (size_t)j * st + (size_t)h * sh) * (F32 ? 4 : 2);
+    double y0, y1;
+    if (F32) {
+      const float2 x = reinterpret_cast<const float2*>(src)[i];
+      y0 = x.x;
+      y1 = x.y;
+    } else {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(src)[i];
+      y0 = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
+      y1 = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
+    }
+    if (sign_neg(a.sign, e0)) y0 = -y0;
+    if (sign_neg(a.sign, e0 + 1)) y1 = -y1;
+    {
+      const double u = y0, w = y1;
+      y0 = u + w;
+      y1 = u - w;
+    }
+#pragma unroll
+    for (int m = 1; m < P; m <<= 1) lane_stage(y0, y1, lane, m);
+    y0 *= a.inv_sqrt_d;
+    y1 *= a.inv_sqrt_d;
+    // vector norm (lanes of one half hold every pair once)
+    double n2 = fma(y1, y1, y0 * y0);
+#pragma unroll
+    for (int m = 1; m < P; m <<= 1) n2 += shfl_xor_f64(n2, m);
+    const double nrm = sqrt(n2);
+    const double u0 = nrm > 0.0 ? y0 / nrm : 0.0, u1 = nrm > 0.0 ? y1 / nrm : 0.0;
+    // lane f < T gathers triplet f, lane T + r the leftover coordinate 3T + r
+    const int f = lane < nf ? lane : 0;
+    const int base = f < g.T ? 3 * f : 3 * g.T + (f - g.T);
+    double c[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int e = min(base + m, D - 1);
+      const double lo_v = shfl_t(u0, e >> 1), hi_v = shfl_t(u1, e >> 1);
+      c[m] = (e & 1) ? hi_v : lo_v;
+    }
+    uint32_t field = 0;
+    if (f < g.T) {
+      const double rho = sqrt(fma(c[2], c[2], fma(c[1], c[1], c[0] * c[0])));
+      const double l1 = fabs(c[0]) + fabs(c[1]) + fabs(c[2]);
+      const double dv = l1 > 0.0 ? l1 : 1.0;
+      const double p1 = c[0] / dv, p2 = c[1] / dv, p3 = c[2] / dv;
+      const double s = p3 >= 0.0 ? p1 : (1.0 - fabs(p2)) * sgn64(p1);
+      const double tt = p3 >= 0.0 ? p2 : (1.0 - fabs(p1)) * sgn64(p2);
+      const uint32_t cs = (uint32_t)nearest(s_bd, g.nd, s);
+      const uint32_t ct = (uint32_t)nearest(s_bd, g.nd, tt);
+      const uint32_t cr = (uint32_t)nearest(s_bn, g.nn, rho);
+      field = cs | (ct << g.bd) | (cr << (2 * g.bd));
+    } else {
+      field = (uint32_t)nearest(s_br, g.nr, c[0]);
+    }
+    // record words: lane w gathers the fields overlapping bits [32 w, 32 w + 32)
+    uint32_t acc = 0u;
+    if (lane == 0) acc = (uint32_t)fp16_bits(fp16_round_pos(fmin(nrm, kFp16Max)));
+    const int wlo = 32 * lane;
+    // first field ending past bit wlo
+    int ff = 0;
+    {
+      const int rel = wlo - 16;
+      if (rel > 0) {
+        ff = rel < g.T * g.B ? rel / g.B : g.T + (rel - g.T * g.B) / g.br;
+        if (ff > 0) --ff;
+      }
+    }
+    const int span = 32 / min(g.B, g.br) + 3;
+    for (int u = 0; u < span; ++u) {
+      const int fi = min(ff + u, nf - 1);
+      const uint32_t val = (uint32_t)__shfl((int)field, fi, 64);
+      if (ff + u >= nf) continue;
+      const int off = field_off(g, fi), wd = field_width(g, fi);
+      const int sh2 = off - wlo;
+      if (sh2 >= 32 || sh2 + wd <= 0) continue;
+      acc |= sh2 >= 0 ? val << sh2 : val >> -sh2;
+    }
+    if (lane < g.words) tp[(size_t)(kv * g.words + lane) * kTile + t] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------------ decode
+
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(256) void tri_decode_kernel(TriArgs a, const uint8_t* cache,
+                                                         void* k_out, void* v_out) {
+  constexpr int P = D / 2;
+  const TriGeom& g = a.g;
+  __shared__ float s_ld[kTriMaxLevelsDir], s_ln[kTriMaxLevelsNorm], s_lr[kTriMaxLevelsRest];
+  for (int i = threadIdx.x; i < g.nd; i += 256) s_ld[i] = (float)a.cb[i];
+  for (int i = threadIdx.x; i < g.nn; i += 256) s_ln[i] = (float)a.cb[g.nd + i];
+  for (int i = threadIdx.x; i < g.nr; i += 256) s_lr[i] = (float)a.cb[g.nd + g.nn + i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long total = (long long)a.batch * a.ntok * a.hkv;
+  if (item >= total) return;
+  const int h = (int)(item % a.hkv);
+  const long long bj = item / a.hkv;
+  const int j = (int)(bj % a.ntok), b = (int)(bj / a.ntok);
+  const int slot = a.t0 + j, tile = slot / kTile, t = slot % kTile;
+  const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
+  const uint32_t* tp = reinterpret_cast<const uint32_t*>(
+      cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * tile_bytes);
+  const int nf = g.T + g.R;
+  const int f = lane < nf ? lane : 0;
+  const int off = field_off(g, f), wd = field_width(g, f);
+  const int i = lane & (P - 1);
+  const float isd = (float)a.inv_sqrt_d;
+
+#pragma unroll 1
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint32_t* rec = tp + (size_t)kv * g.words * kTile + t;
+    const float nu = __half2float(__ushort_as_half((uint16_t)(rec[0] & 0xFFFFu)));
+    const int wi = off >> 5;
+    const uint32_t lo = rec[(size_t)wi * kTile];
+    const uint32_t hi = wi + 1 < g.words ? rec[(size_t)(wi + 1) * kTile] : 0u;
+    const uint64_t win = ((uint64_t)hi << 32) | lo;
+    const uint32_t val = (uint32_t)(win >> (off & 31)) & ((1u << wd) - 1u);
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    if (f < g.T) {
+      const float s = s_ld[val & (g.nd - 1)], tt = s_ld[(val >> g.bd) & (g.nd - 1)];
+      const float rho = s_ln[val >> (2 * g.bd)];
+      const float z = 1.f - fabsf(s) - fabsf(tt);
+      const float x = z >= 0.f ? s : (1.f - fabsf(tt)) * sgn32(s);
+      const float y = z >= 0.f ? tt : (1.f - fabsf(s)) * sgn32(tt);
+      const float sc = nu * rho * rsqrtf(x * x + y * y + z * z);
+      c0 = x * sc;
+      c1 = y * sc;
+      c2 = z * sc;
+    } else {
+      c0 = nu * s_lr[val];
+    }
+    // elements 2i, 2i+1 back to lane i
+    float e[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int el = 2 * i + m;
+      const int srcl = el < 3 * g.T ? el / 3 : g.T + (el - 3 * g.T);
+      const int comp = el < 3 * g.T ? el % 3 : 0;
+      const float v0 = __shfl(c0, srcl, 64), v1 = __shfl(c1, srcl, 64), v2 = __shfl(c2, srcl, 64);
+      e[m] = comp == 0 ? v0 : (comp == 1 ? v1 : v2);
+    }
+    float a0 = e[0], a1 = e[1];
+    fwht_pairs_f32<P>(a0, a1, i);
+    a0 *= isd;
+    a1 *= isd;
+    if (sign_neg(a.sign, 2 * i)) a0 = -a0;
+    if (sign_neg(a.sign, 2 * i + 1)) a1 = -a1;
+    if (lane < P) {
+      const size_t row = ((size_t)(b * a.ntok + j) * a.hkv + h) * D;
+      void* out = kv == 0 ? k_out : v_out;
+      if (F32OUT)
+        reinterpret_cast<float2*>(out)[(row >> 1) + i] = make_float2(a0, a1);
+      else
+        reinterpret_cast<__half2*>(out)[(row >> 1) + i] = __floats2half2_rn(a0, a1);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------- attention
+
+struct TriAttnArgs {
+  TriGeom g;
+  int batch, hkv, hq, group, tiles_per_seq;
+  int seq_len, ntiles, nsplit, tiles_per_split;
+  int q_f32, out_f32;
+  float q_scale;      // softmax scale * log2(e), folded into the rotated query
+  float inv_sqrt_d;
+  SignMask sign;
+  const double* cb;
+  const void* q;      // [B, Hq, d]
+  void* out;          // [B, Hq, d]
+  float* part_ml;     // [B * Hq][nsplit][2]
+  float* part_acc;    // [B * Hq][nsplit][d] (rotated domain, element order of the codec)
+};
+
+constexpr int kTriWaves = 4;
+
+// Field f of the record of slot `lane` in a plane staged in LDS as [words][64].
+__device__ __forceinline__ uint32_t staged_field(const uint32_t* plane, int off, int wd, int words,
+                                                 int slot) {
+  const int wi = off >> 5;
+  const uint32_t lo = plane[wi * kTile + slot];
+  const uint32_t hi = wi + 1 < words ? plane[(wi + 1) * kTile + slot] : 0u;
+  const uint64_t win = ((uint64_t)hi << 32) | lo;
+  return (uint32_t)(win >> (off & 31)) & ((1u << wd) - 1u);
+}
+
+template <int D, int G, int DIRB>
+__global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnArgs a,
+                                                                         const uint8_t* cache) {
+  constexpr int P = D / 2, T = D / 3, R = D - 3 * T;
+  const TriGeom& g = a.g;
+  // LDS: direction table (2^(2 bd) unit vectors, sized for bd <= DIRB), norm and
+  // leftover levels, the rotated query as padded triplets, then per wave: the staged
+  // plane and the token weights
+  __shared__ float4 s_dir[(1 << DIRB) * (1 << DIRB)];
+  __shared__ float s_ln[kTriMaxLevelsNorm], s_lr[kTriMaxLevelsRest];
+  __shared__ float4 s_q3[G][T + 1];        // (q~[3j], q~[3j+1], q~[3j+2], 0); row T: leftovers
+  __shared__ uint32_t s_plane[kTriWaves][32 * kTile];  // up to 32 record words
+  __shared__ float s_w[kTriWaves][G][kTile];           // p * N per token
+  __shared__ float s_ml[kTriWaves][G][2];
+  __shared__ float s_acc[kTriWaves][G][D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x, bk = blockIdx.y, b = bk / a.hkv;
+  const int nd = g.nd;
+  for (int idx = tid; idx < nd * nd; idx += kTriWaves * 64) {
+    const float s = (float)a.cb[idx / nd], tt = (float)a.cb[idx % nd];
+    const float z = 1.f - fabsf(s) - fabsf(tt);
+    const float x = z >= 0.f ? s : (1.f - fabsf(tt)) * sgn32(s);
+    const float y = z >= 0.f ? tt : (1.f - fabsf(s)) * sgn32(tt);
+    const float r = rsqrtf(x * x + y * y + z * z);
+    s_dir[idx] = make_float4(x * r, y * r, z * r, 0.f);
+  }
+  for (int idx = tid; idx < g.nn; idx += kTriWaves * 64) s_ln[idx] = (float)a.cb[nd + idx];
+  for (int idx = tid; idx < g.nr; idx += kTriWaves * 64) s_lr[idx] = (float)a.cb[nd + g.nn + idx];
+  // rotated query: wave w < G rotates head w (lane p < P holds elements 2p, 2p+1)
+  for (int hh = wave; hh < G; hh += kTriWaves) {
+    const size_t qoff = ((size_t)bk * G + hh) * D;
+    float x0, x1;
+    const int p = lane & (P - 1);
+    if (a.q_f32) {
+      const float2 v = reinterpret_cast<const float2*>(a.q)[(qoff >> 1) + p];
+      x0 = v.x;
+      x1 = v.y;
+    } else {
+      const __half2 v = reinterpret_cast<const __half2*>(a.q)[(qoff >> 1) + p];
+      x0 = __low2float(v);
+      x1 = __high2float(v);
+    }
+    if (sign_neg(a.sign, 2 * p)) x0 = -x0;
+    if (sign_neg(a.sign, 2 * p + 1)) x1 = -x1;
+    fwht_pairs_f32<P>(x0, x1, p);
+    const float sc = a.inv_sqrt_d * a.q_scale;
+    x0 *= sc;
+    x1 *= sc;
+    float* row = reinterpret_cast<float*>(&s_q3[hh][0]);
+    if (lane < P) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int el = 2 * p + m;
+        const float val = m ? x1 : x0;
+        const int slotq = el < 3 * T ? (el / 3) * 4 + el % 3 : T * 4 + (el - 3 * T);
+        row[slotq] = val;
+      }
+      if (lane < T + 1) row[lane * 4 + 3] = 0.f;
+      if (lane == 0 && R < 3) {
+        for (int r = R; r < 3; ++r) row[T * 4 + r] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int tile_begin = split * a.tiles_per_split;
+  const int tile_end = min(tile_begin + a.tiles_per_split, a.ntiles);
+  const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
+  const uint8_t* base = cache + (size_t)bk * a.tiles_per_seq * tile_bytes;
+  const int nf = T + R;
+  const int f = lane < nf ? lane : 0;
+  const int foff = field_off(g, f), fwd = field_width(g, f);
+
+  float m[G], l[G], acc[G][3];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+    acc[hh][0] = acc[hh][1] = acc[hh][2] = 0.f;
+  }
+  uint32_t* plane = s_plane[wave];
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kTriWaves) {
+    const uint32_t* tw = reinterpret_cast<const uint32_t*>(base + (size_t)tile * tile_bytes);
+    const int nvalid = min(a.seq_len - tile * kTile, kTile);
+    const bool valid = lane < nvalid;
+    // ---- keys: stage the key plane, one lane per token
+    for (int w = 0; w < g.words; ++w) plane[w * kTile + lane] = tw[w * kTile + lane];
+    asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+    const float nu_k = __half2float(__ushort_as_half((uint16_t)(plane[lane] & 0xFFFFu)));
+    float sc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+    for (int jt = 0; jt < T; ++jt) {
+      const uint32_t val = staged_field(plane, 16 + jt * g.B, g.B, g.words, lane);
+      const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+      const float rho = s_ln[val >> (2 * g.bd)];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float4 q4 = s_q3[hh][jt];
+        sc[hh] = fmaf(rho, fmaf(q4.x, w4.x, fmaf(q4.y, w4.y, q4.z * w4.z)), sc[hh]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t val = staged_field(plane, 16 + T * g.B + r * g.br, g.br, g.words, lane);
+      const float u = s_lr[val];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float4 q4 = s_q3[hh][T];
+        sc[hh] = fmaf(u, r == 0 ? q4.x : (r == 1 ? q4.y : q4.z), sc[hh]);
+      }
+    }
+    // ---- value plane staged, then the softmax weights p * N per token
+    const float nu_v = __half2float(__ushort_as_half((uint16_t)(tw[g.words * kTile + lane] & 0xFFFFu)));
+    asm volatile("" ::: "memory");
+    for (int w = 0; w < g.words; ++w) plane[w * kTile + lane] = tw[(g.words + w) * kTile + lane];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float s = valid ? sc[hh] * nu_k : -INFINITY;
+      const float mnew = fmaxf(m[hh], wave_max(s));
+      const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[hh] - mnew);
+      l[hh] *= alpha;
+      acc[hh][0] *= alpha;
+      acc[hh][1] *= alpha;
+      acc[hh][2] *= alpha;
+      m[hh] = mnew;
+      const float pv = m[hh] == -INFINITY ? 0.f : fast_exp2(s - m[hh]);
+      l[hh] += pv;
+      s_w[wave][hh][lane] = valid ? pv * nu_v : 0.f;
+    }
+    asm volatile("" ::: "memory");
+    // ---- values: lane f rebuilds its triplet (or leftover) of every token
+    if (lane < nf) {
+      for (int tk = 0; tk < kTile; ++tk) {
+        const uint32_t val = staged_field(plane, foff, fwd, g.words, tk);
+        float c0, c1, c2;
+        if (f < T) {
+          const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+          const float rho = s_ln[val >> (2 * g.bd)];
+          c0 = rho * w4.x;
+          c1 = rho * w4.y;
+          c2 = rho * w4.z;
+        } else {
+          c0 = s_lr[val];
+          c1 = c2 = 0.f;
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float wgt = s_w[wave][hh][tk];
+          acc[hh][0] = fmaf(wgt, c0, acc[hh][0]);
+          acc[hh][1] = fmaf(wgt, c1, acc[hh][1]);
+          acc[hh][2] = fmaf(wgt, c2, acc[hh][2]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) l[hh] = wave_sum(l[hh]);
+  // ---- waves merge in LDS (rotated-domain element order of the codec)
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      s_ml[wave][hh][0] = m[hh];
+      s_ml[wave][hh][1] = l[hh];
+    }
+  }
+  if (lane < nf) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      if (f < T) {
+        s_acc[wave][hh][3 * f] = acc[hh][0];
+        s_acc[wave][hh][3 * f + 1] = acc[hh][1];
+        s_acc[wave][hh][3 * f + 2] = acc[hh][2];
+      } else {
+        s_acc[wave][hh][3 * T + (f - T)] = acc[hh][0];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kTriWaves * 64) {
+    const int hh = idx / D, e = idx % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kTriWaves; ++w) mm = fmaxf(mm, s_ml[w][hh][0]);
+    float ll = 0.f, aa = 0.f;
+#pragma unroll
+    for (int w = 0; w < kTriWaves; ++w) {
+      const float fct = mm == -INFINITY ? 0.f : fast_exp2(s_ml[w][hh][0] - mm);
+      ll += s_ml[w][hh][1] * fct;
+      aa += s_acc[w][hh][e] * fct;
+    }
+    const size_t rowi = ((size_t)bk * G + hh) * a.nsplit + split;
+    a.part_acc[rowi * D + e] = aa;
+    if (e == 0) {
+      a.part_ml[2 * rowi] = mm;
+      a.part_ml[2 * rowi + 1] = ll;
+    }
+  }
+}
+
+// One wave per output row (batch, query head): log-sum-exp over the splits, then the
+// inverse transform of acc / l (lane p holds elements 2p, 2p+1).
+template <int D>
+__global__ __launch_bounds__(64) void tri_attn_merge_kernel(TriAttnArgs a) {
+  constexpr int P = D / 2;
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const float* ml = a.part_ml + 2 * row * a.nsplit;
+  const float* pa = a.part_acc + row * a.nsplit * D;
+  const int p = lane & (P - 1);
+  float mm = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, ml[2 * s]);
+  float ll = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float fct = mm == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - mm);
+    ll += ml[2 * s + 1] * fct;
+    a0 += pa[(size_t)s * D + 2 * p] * fct;
+    a1 += pa[(size_t)s * D + 2 * p + 1] * fct;
+  }
+  const float inv = ll > 0.f ? 1.f / ll : 0.f;
+  a0 *= inv;
+  a1 *= inv;
+  fwht_pairs_f32<P>(a0, a1, p);
+  a0 *= a.inv_sqrt_d;
+  a1 *= a.inv_sqrt_d;
+  if (sign_neg(a.sign, 2 * p)) a0 = -a0;
+  if (sign_neg(a.sign, 2 * p + 1)) a1 = -a1;
+  if (lane < P) {
+    const size_t o = row * D;
+    if (a.out_f32)
+      reinterpret_cast<float2*>(a.out)[(o >> 1) + p] = make_float2(a0, a1);
+    else
+      reinterpret_cast<__half2*>(a.out)[(o >> 1) + p] = __floats2half2_rn(a0, a1);
+  }
+}
+
+// ------------------------------------------------------------------- host: quantisers
+
+// 40-point Gauss-Legendre rule on [-1, 1]: nodes are the roots of P_40 (Newton's method
+// on the three-term recurrence from the standard initial guesses), weights
+// 2 / ((1 - x^2) P_40'(x)^2).
+struct GaussRule {
+  double x[40], w[40];
+};
+
+GaussRule gauss_legendre40() {
+  constexpr int n = 40;
+  GaussRule r;
+  for (int i = 0; i < n; ++i) {
+    double x = cos(M_PI * (i + 0.75) / (n + 0.5));
+    double dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = x;
+      for (int k = 1; k < n; ++k) {
+        const double p2 = ((2.0 * k + 1.0) * x * p1 - k * p0) / (k + 1.0);
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (x * p1 - p0) / (x * x - 1.0);
+      const double dx = p1 / dp;
+      x -= dx;
+      if (fabs(dx) < 1e-16) break;
+    }
+    double p0 = 1.0, p1 = x;
+    for (int k = 1; k < n; ++k) {
+      const double p2 = ((2.0 * k + 1.0) * x * p1 - k * p0) / (k + 1.0);
+      p0 = p1;
+      p1 = p2;
+    }
+    dp = n * (x * p1 - p0) / (x * x - 1.0);
+    r.x[n - 1 - i] = x;  // ascending
+    r.w[n - 1 - i] = 2.0 / ((1.0 - x * x) * dp * dp);
+  }
+  return r;
+}
+
+enum Marginal { kOct = 0, kNorm = 1, kCoord = 2 };
+
+// The marginals (up to constants, which cancel in the means and quantiles).
+double marginal(int kind, int d, double x) {
+  if (kind == kOct) {
+    const double s = fabs(x), c = s * s + (1.0 - s) * (1.0 - s);
+    return (2.0 * (1.0 - s) / (2.0 * s * s + (1.0 - s) * (1.0 - s)) +
+            2.0 * s / (s * s + 2.0 * (1.0 - s) * (1.0 - s))) / sqrt(c);
+  }
+  const double q = 1.0 - x * x;
+  if (q <= 0.0) return 0.0;
+  if (kind == kNorm) return x * x * pow(q, (d - 5) / 2.0);
+  return pow(q, (d - 3) / 2.0);
+}
+
+struct LloydMax {
+  const GaussRule& gl;
+  int kind, d;
+  double lo, hi;
+  bool split0;  // cells are split at 0
+
+  void cell(double a, double b, double* mass, double* mom) const {
+    double ms = 0.0, mo = 0.0;
+    double edges[3] = {a, b, b};
+    int ne = 2;
+    if (split0) {
+      edges[1] = fmin(fmax(0.0, a), b);
+      edges[2] = b;
+      ne = 3;
+    }
+    for (int p = 0; p + 1 < ne; ++p) {
+      const double x0 = edges[p], x1 = edges[p + 1];
+      const double half = 0.5 * (x1 - x0), mid = 0.5 * (x1 + x0);
+      double sm = 0.0, sx = 0.0;
+      for (int i = 0; i < 40; ++i) {
+        const double x = mid + half * gl.x[i];
+        const double fx = marginal(kind, d, x);
+        sm += gl.w[i] * fx;
+        sx += gl.w[i] * fx * x;
+      }
+      ms += half * sm;
+      mo += half * sx;
+    }
+    *mass = ms;
+    *mom = mo;
+  }
+  double cdf(double x) const {
+    double m, mu;
+    cell(lo, x, &m, &mu);
+    return m;
+  }
+  void fit(int bits, double* levels) const {
+    const int n = 1 << bits;
+    const double total = cdf(hi);
+    for (int i = 0; i < n; ++i) {
+      const double q = (i + 0.5) / n;
+      double a = lo, b = hi;
+      for (int it = 0; it < 200; ++it) {
+        const double mid = 0.5 * (a + b);
+        if (mid <= a || mid >= b) break;
+        if (cdf(mid) < q * total) a = mid;
+        else b = mid;
+      }
+      levels[i] = 0.5 * (a + b);
+    }
+    // Lloyd's iteration (each level to the centroid of its cell) converges linearly
+    // with a rate near 1 - O(1/n^2), too slowly for 7-8 bit quantisers; its fixed point
+    // F(l) = l - centroid(l) = 0 is solved by Newton's method instead. Cell i's centroid
+    // c_i = M1_i / M0_i over [a_i, b_i] moves with its edges as
+    //   dc_i/da_i = f(a_i) (c_i - a_i) / M0_i,   dc_i/db_i = f(b_i) (b_i - c_i) / M0_i,
+    // and the inner edges are midpoints of adjacent levels, so the Jacobian of F is
+    // tridiagonal. Steps are halved until the levels stay ascending inside the support;
+    // Lloyd steps finish the job should Newton stall.
+    std::vector<double> a(n), b(n), c(n), m0(n), F(n), lo_d(n), di(n), up_d(n), step(n), nl(n);
+    const auto residual = [&](const double* l) {
+      double r = 0.0;
+      for (int i = 0; i < n; ++i) {
+        a[i] = i == 0 ? lo : 0.5 * (l[i - 1] + l[i]);
+        b[i] = i == n - 1 ? hi : 0.5 * (l[i] + l[i + 1]);
+        double mass, mom;
+        cell(a[i], b[i], &mass, &mom);
+        m0[i] = mass;
+        c[i] = mass > 0.0 ? mom / mass : l[i];
+        F[i] = l[i] - c[i];
+        r = fmax(r, fabs(F[i]));
+      }
+      return r;
+    };
+    double r = residual(levels);
+    for (int it = 0; it < 100 && r > 1e-15; ++it) {
+      for (int i = 0; i < n; ++i) {
+        const double dca = (i == 0 || m0[i] <= 0.0) ? 0.0 : marginal(kind, d, a[i]) * (c[i] - a[i]) / m0[i];
+        const double dcb = (i == n - 1 || m0[i] <= 0.0) ? 0.0 : marginal(kind, d, b[i]) * (b[i] - c[i]) / m0[i];
+        lo_d[i] = -0.5 * dca;
+        di[i] = 1.0 - 0.5 * (dca + dcb);
+        up_d[i] = -0.5 * dcb;
+      }
+      // Thomas algorithm on (lo_d, di, up_d) step = F
+      for (int i = 0; i < n; ++i) step[i] = F[i];
+      for (int i = 1; i < n; ++i) {
+        const double w = lo_d[i] / di[i - 1];
+        di[i] -= w * up_d[i - 1];
+        step[i] -= w * step[i - 1];
+      }
+      step[n - 1] /= di[n - 1];
+      for (int i = n - 2; i >= 0; --i) step[i] = (step[i] - up_d[i] * step[i + 1]) / di[i];
+      bool moved = false;
+      for (double t = 1.0; t > 1e-6; t *= 0.5) {
+        bool ok = true;
+        for (int i = 0; i < n; ++i) {
+          nl[i] = levels[i] - t * step[i];
+          ok = ok && std::isfinite(nl[i]) && nl[i] > lo && nl[i] < hi && (i == 0 || nl[i] > nl[i - 1]);
+        }
+        if (!ok) continue;
+        for (int i = 0; i < n; ++i) levels[i] = nl[i];
+        moved = true;
+        break;
+      }
+      if (!moved) break;
+      r = residual(levels);
+    }
+    for (int it = 0; it < 200000 && r > 1e-14; ++it) {
+      for (int i = 0; i < n; ++i) levels[i] = c[i];
+      r = residual(levels);
+    }
+  }
+};
+
+bool tri_desc_ok(const kvq_tri_desc* d) {
+  if (!d) return false;
+  if (d->head_dim != 64 && d->head_dim != 128) return false;
+  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0) return false;
+  if (d->bits_dir < 1 || d->bits_dir > 6 || d->bits_norm < 1 || d->bits_norm > 6) return false;
+  if (d->bits_rest < 1 || d->bits_rest > 8) return false;
+  return true;
+}
+
+TriGeom geom_of_tri(const kvq_tri_desc* d) {
+  return tri_geom((int)d->head_dim, (int)d->bits_dir, (int)d->bits_norm, (int)d->bits_rest);
+}
+
+SignMask tri_sign_mask(const kvq_tri_desc* d) {
+  // the angle codec's generator, through its public entry point
+  int8_t s[128];
+  SignMask m;
+  memset(&m, 0, sizeof(m));
+  kvq_layer_signs(d->seed, d->layer, d->head_dim, s);
+  for (uint32_t i = 0; i < d->head_dim; ++i)
+    if (s[i] < 0) m.w[i >> 6] |= 1ull << (i & 63);
+  return m;
+}
+
+int tri_tiles(const kvq_tri_desc* d) { return (int)((d->capacity + kTile - 1) / kTile); }
+
+kvq_status tri_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+TriArgs tri_args(const kvq_tri_desc* d, const double* cb, uint32_t t0, uint32_t ntok) {
+  TriArgs a;
+  a.g = geom_of_tri(d);
+  a.batch = (int)d->batch;
+  a.hkv = (int)d->num_kv_heads;
+  a.tiles_per_seq = tri_tiles(d);
+  a.t0 = (int)t0;
+  a.ntok = (int)ntok;
+  a.inv_sqrt_d = 1.0 / sqrt((double)d->head_dim);
+  a.sign = tri_sign_mask(d);
+  a.cb = cb;
+  return a;
+}
+
+void tri_split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tps) {
+  const int ntiles = (int)((seq_len + kTile - 1) / kTile);
+  int s = (int)((1024 + units - 1) / units);
+  int max_s = (ntiles + 3) / 4;
+  if (max_s < 1) max_s = 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  *tps = (ntiles + s - 1) / s;
+  *nsplit = (ntiles + *tps - 1) / *tps;
+}
+
+size_t tri_align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+template <int D, int DIRB>
+hipError_t tri_attn_split(const TriAttnArgs& a, const uint8_t* cache, hipStream_t s) {
+  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv));
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL((tri_attn_split_kernel<D, 1, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
+    case 2: hipLaunchKernelGGL((tri_attn_split_kernel<D, 2, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
+    case 4: hipLaunchKernelGGL((tri_attn_split_kernel<D, 4, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
+    case 8: hipLaunchKernelGGL((tri_attn_split_kernel<D, 8, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t tri_attn_launch(const TriAttnArgs& a, const uint8_t* cache, hipStream_t s) {
+  // direction tables of up to 4 bits per coordinate take 4 KiB of LDS, 6 bits 64 KiB
+  const hipError_t e0 = a.g.bd <= 4 ? tri_attn_split<D, 4>(a, cache, s) : tri_attn_split<D, 6>(a, cache, s);
+  if (e0 != hipSuccess) return e0;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tri_attn_merge_kernel<D>), dim3((unsigned)(a.batch * a.hq)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+uint32_t kvq_tri_record_words(const kvq_tri_desc* d) {
+  if (!tri_desc_ok(d)) return 0;
+  return (uint32_t)geom_of_tri(d).words;
+}
+
+size_t kvq_tri_tile_bytes(const kvq_tri_desc* d) {
+  if (!tri_desc_ok(d)) return 0;
+  return (size_t)2 * geom_of_tri(d).words * kTile * 4;
+}
+
+size_t kvq_tri_cache_bytes(const kvq_tri_desc* d) {
+  if (!tri_desc_ok(d)) return 0;
+  return (size_t)d->batch * d->num_kv_heads * tri_tiles(d) * kvq_tri_tile_bytes(d);
+}
+
+size_t kvq_tri_codebook_doubles(const kvq_tri_desc* d) {
+  if (!tri_desc_ok(d)) return 0;
+  const TriGeom g = geom_of_tri(d);
+  return (size_t)2 * (g.nd + g.nn + g.nr) - 3;
+}
+
+kvq_status kvq_tri_codebook(const kvq_tri_desc* d, double* out) {
+  if (!tri_desc_ok(d) || !out) return KVQ_ERR_INVALID_ARGUMENT;
+  const TriGeom g = geom_of_tri(d);
+  const GaussRule gl = gauss_legendre40();
+  const LloydMax dir{gl, kOct, g.d, -1.0, 1.0, true};
+  const LloydMax nrm{gl, kNorm, g.d, 0.0, 1.0, false};
+  const LloydMax rst{gl, kCoord, g.d, -1.0, 1.0, true};
+  double* ld = out;
+  double* ln = ld + g.nd;
+  double* lr = ln + g.nn;
+  dir.fit(g.bd, ld);
+  nrm.fit(g.bn, ln);
+  rst.fit(g.br, lr);
+  double* b = lr + g.nr;
+  for (int i = 0; i + 1 < g.nd; ++i) *b++ = 0.5 * (ld[i] + ld[i + 1]);
+  for (int i = 0; i + 1 < g.nn; ++i) *b++ = 0.5 * (ln[i] + ln[i + 1]);
+  for (int i = 0; i + 1 < g.nr; ++i) *b++ = 0.5 * (lr[i] + lr[i + 1]);
+  return KVQ_OK;
+}
+
+kvq_status kvq_tri_encode(const kvq_tri_desc* d, void* cache, const double* cb, const void* k,
+                          const void* v, kvq_dtype in_dtype, int64_t sb, int64_t st, int64_t sh,
+                          uint32_t t0, uint32_t ntok, void* stream) {
+  if (!tri_desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (in_dtype != KVQ_F16 && in_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !cb || !k || !v || ((uintptr_t)cache % 16) || ((uintptr_t)cb % 8))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  const size_t esz = in_dtype == KVQ_F32 ? 4 : 2;
+  if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  const TriArgs a = tri_args(d, cb, t0, ntok);
+  const long long items = (long long)d->batch * ntok * d->num_kv_heads;
+  if ((items + 3) / 4 > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  const bool f32 = in_dtype == KVQ_F32;
+  if (d->head_dim == 64) {
+    if (f32) hipLaunchKernelGGL((tri_encode_kernel<64, true>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    else hipLaunchKernelGGL((tri_encode_kernel<64, false>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+  } else {
+    if (f32) hipLaunchKernelGGL((tri_encode_kernel<128, true>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    else hipLaunchKernelGGL((tri_encode_kernel<128, false>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+  }
+  return tri_hip(hipGetLastError());
+}
+
+kvq_status kvq_tri_decode(const kvq_tri_desc* d, const void* cache, const double* cb, void* k_out,
+                          void* v_out, kvq_dtype out_dtype, uint32_t t0, uint32_t ntok,
+                          void* stream) {
+  if (!tri_desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != KVQ_F16 && out_dtype != KVQ_F32) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uint64_t)t0 + ntok > d->capacity) return KVQ_ERR_CAPACITY;
+  if (ntok == 0) return KVQ_OK;
+  if (!cache || !cb || !k_out || !v_out || ((uintptr_t)cache % 16) || ((uintptr_t)cb % 8))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)k_out % 8) || ((uintptr_t)v_out % 8)) return KVQ_ERR_INVALID_ARGUMENT;
+  const TriArgs a = tri_args(d, cb, t0, ntok);
+  const long long items = (long long)d->batch * ntok * d->num_kv_heads;
+  if ((items + 3) / 4 > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* c = (const uint8_t*)cache;
+  const bool f32 = out_dtype == KVQ_F32;
+  if (d->head_dim == 64) {
+    if (f32) hipLaunchKernelGGL((tri_decode_kernel<64, true>), grid, block, 0, s, a, c, k_out, v_out);
+    else hipLaunchKernelGGL((tri_decode_kernel<64, false>), grid, block, 0, s, a, c, k_out, v_out);
+  } else {
+    if (f32) hipLaunchKernelGGL((tri_decode_kernel<128, true>), grid, block, 0, s, a, c, k_out, v_out);
+    else hipLaunchKernelGGL((tri_decode_kernel<128, false>), grid, block, 0, s, a, c, k_out, v_out);
+  }
+  return tri_hip(hipGetLastError());
+}
+
+size_t kvq_tri_attn_workspace_bytes(const kvq_tri_desc* d, uint32_t hq, uint32_t seq_len) {
+  if (!tri_desc_ok(d) || hq == 0 || hq % d->num_kv_heads || seq_len == 0 || seq_len > d->capacity)
+    return 0;
+  const uint32_t g = hq / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return 0;
+  if (geom_of_tri(d).words > 32) return 0;
+  int nsplit, tps;
+  tri_split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
+  const size_t rows = (size_t)d->batch * hq * nsplit;
+  return tri_align256(rows * 2 * sizeof(float)) + tri_align256(rows * d->head_dim * sizeof(float));
+}
+
+kvq_status kvq_tri_attn_decode(const kvq_tri_desc* d, const void* cache, const double* cb,
+                               const void* q, kvq_dtype q_dtype, uint32_t hq, uint32_t seq_len,
+                               float scale, void* out, kvq_dtype out_dtype, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!tri_desc_ok(d)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (hq == 0 || hq % d->num_kv_heads || seq_len == 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (seq_len > d->capacity) return KVQ_ERR_CAPACITY;
+  const uint32_t g = hq / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
+  if (geom_of_tri(d).words > 32) return KVQ_ERR_UNSUPPORTED;
+  const size_t need = kvq_tri_attn_workspace_bytes(d, hq, seq_len);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!cache || !cb || !q || !out || ((uintptr_t)cache % 16) || ((uintptr_t)cb % 8))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)q % (q_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)out % (out_dtype == KVQ_F32 ? 8 : 4)) return KVQ_ERR_INVALID_ARGUMENT;
+  TriAttnArgs a;
+  a.g = geom_of_tri(d);
+  a.batch = (int)d->batch;
+  a.hkv = (int)d->num_kv_heads;
+  a.hq = (int)hq;
+  a.group = (int)g;
+  a.tiles_per_seq = tri_tiles(d);
+  a.seq_len = (int)seq_len;
+  a.ntiles = (int)((seq_len + kTile - 1) / kTile);
+  tri_split_plan(d->batch * d->num_kv_heads, seq_len, &a.nsplit, &a.tiles_per_split);
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.out_f32 = out_dtype == KVQ_F32;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
+  a.q_scale = (float)(sc * 1.4426950408889634);
+  a.inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
+  a.sign = tri_sign_mask(d);
+  a.cb = cb;
+  a.q = q;
+  a.out = out;
+  const size_t rows = (size_t)d->batch * hq * a.nsplit;
+  a.part_ml = (float*)ws;
+  a.part_acc = (float*)((char*)ws + tri_align256(rows * 2 * sizeof(float)));
+  const hipError_t e = d->head_dim == 64 ? tri_attn_launch<64>(a, (const uint8_t*)cache, (hipStream_t)stream)
+                                          : tri_attn_launch<128>(a, (const uint8_t*)cache, (hipStream_t)stream);
+  return tri_hip(e);
+}
+
+}  // extern "C"

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 8
+    assert kvq.abi_version() == 9
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
