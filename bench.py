@@ -8,7 +8,10 @@ One step = the whole path over one batch of synthetic input, all layers:
 After the timed steps, a ragged-batch decode loop is timed on the same caches (append one
 token per sequence at its own slot, attend with per-sequence lengths) and reported under
 `decode_loop`; multi-query attention (kvq_attn_multi, several query tokens per sequence
-on the matrix cores) is timed on them last and reported under `multi_query`. Inputs and
+on the matrix cores) is timed on them and reported under `multi_query`; a read-only
+streaming probe over the same buffers gives the achievable read bandwidth
+(`roofline.stream_probe`); last, the triplet codec is run on the same K/V and queries
+(`triplet`). Inputs and
 caches are resident in HBM before timing starts. `value` is decode-attention
 throughput in GB/s of compressed cache read per second over the attention phase of a
 step (all layers, every launch and gap included). Phase times come from HIP events on
@@ -47,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate oracle CPU time (all cores together) of the baseline "
                          "sample")
+    ap.add_argument("--no-triplet", action="store_true",
+                    help="skip the triplet-codec sub-record")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (used to "
                          "scale rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -355,6 +360,94 @@ def multi_query(kvq, cfg, descs, caches, dev, nqs=(4, 8), reps=5):
     return res
 
 
+def stream_probe(kvq, caches, dev, reps=3):
+    """Read-only streaming probe (kvq_probe_read) over the same cache buffers the
+    attention sweep reads, one launch per layer, HIP events around the sweep: the
+    bandwidth a plain read of this memory reaches on this GPU (context for the
+    roofline, no codec work)."""
+    import torch
+
+    sink = torch.zeros(256, dtype=torch.uint8, device=dev)
+    nbytes = sum(c.numel() for c in caches)
+
+    def sweep():
+        for c in caches:
+            kvq.probe_read(c, sink)
+
+    sweep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sweep()
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    return {"GBps": round(nbytes / s / 1e9, 2), "bytes_per_sweep": nbytes,
+            "launches_per_sweep": len(caches), "frac_of_peak": round(nbytes / s / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+TRIPLET_BITS = (4, 2, 3)  # (bits per square coordinate, per triplet norm, per leftover)
+
+
+def triplet_sub(kvq, cfg, ks, vs, qs, dev, reps=3):
+    """The triplet (octahedral) codec on the same K/V and queries, every layer: encode
+    all tokens, then one decode attention launch pair (splits + merge) per layer; HIP
+    events around each sweep. Cache bytes per attention launch are the records read
+    (both planes, whole 32-bit words)."""
+    import torch
+
+    L, B, T, Hkv, Hq, d = cfg.layers, cfg.batch, cfg.seq, cfg.hkv, cfg.hq, cfg.d
+    descs = [kvq.make_tri_desc(d, Hkv, B, T, *TRIPLET_BITS, layer, 0) for layer in range(L)]
+    table = kvq.tri_codebook_device(descs[0], dev)  # depends on (d, bits) only
+    caches = [kvq.alloc_tri_cache(dd, dev) for dd in descs]
+    ws = torch.empty(kvq.tri_attn_workspace_bytes(descs[0], Hq, T), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def enc():
+        for layer in range(L):
+            kvq.tri_encode(descs[layer], caches[layer], table, ks[layer], vs[layer], 0)
+
+    def att():
+        for layer in range(L):
+            kvq.tri_attn_decode(descs[layer], caches[layer], table, qs[layer], T, workspace=ws,
+                                out=out)
+
+    enc()
+    att()
+    torch.cuda.synchronize()
+    e = [Ev() for _ in range(3)]
+    e[0].record()
+    for _ in range(reps):
+        enc()
+    e[1].record()
+    for _ in range(reps):
+        att()
+    e[2].record()
+    torch.cuda.synchronize()
+    enc_ms = e[0].elapsed_time(e[1]) / reps
+    att_ms = e[1].elapsed_time(e[2]) / reps
+    words = kvq.tri_record_words(descs[0])
+    rec_bytes = B * Hkv * T * words * 4 * 2
+    del caches
+    torch.cuda.empty_cache()
+    return {
+        "what": "triplet codec (octahedral directions + Lloyd-Max norms): encode every "
+                "layer, then decode attention every layer (split + merge launches)",
+        "bits": {"dir": TRIPLET_BITS[0], "norm": TRIPLET_BITS[1], "rest": TRIPLET_BITS[2],
+                 "record_words": words, "bits_per_element": words * 32 / d},
+        "encode_tokens_per_s": round(B * T / (enc_ms * 1e-3), 1),
+        "encode_ms_all_layers": round(enc_ms, 4),
+        "attn_ms_all_layers": round(att_ms, 4),
+        "attn_us_per_layer": round(att_ms * 1e3 / L, 2),
+        "attn_cache_GBps": round(rec_bytes * L / (att_ms * 1e-3) / 1e9, 2),
+        "attn_hbm_frac": round(rec_bytes * L / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_per_launch": rec_bytes,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -457,6 +550,8 @@ def main():
 
     loop = decode_loop(kvq, cfg, descs, caches, ws, dev)
     mq = multi_query(kvq, cfg, descs, caches, dev)
+    probe = stream_probe(kvq, caches, dev)
+    tri = None if args.no_triplet else triplet_sub(kvq, cfg, ks, vs, qs, dev)
 
     enc_ms = sum(e[0].elapsed_time(e[1]) for e, _ in recs) / args.steps
     att_ms = sum(e[1].elapsed_time(e[2]) for e, _ in recs) / args.steps
@@ -509,6 +604,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "decode_loop": loop,
         "multi_query": mq,
+        "triplet": tri,
         "roofline": {
             "kernel": "attn_decode_kernel (kvq_attn_decode)",
             "bound": "hbm",
@@ -521,6 +617,8 @@ def main():
             "timing": ("HIP events around each launch" if graph[0] is None else
                        f"HIP events around the replayed graph of the {L} launches, / {L}"),
             "bytes_per_launch": launch_bytes_avg,
+            "stream_probe": probe,
+            "achieved_over_probe": round(achieved / probe["GBps"], 4),
         },
     }
     if not args.no_cpu_baseline:

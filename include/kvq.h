@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 9
+#define KVQ_ABI_VERSION 10
 #define KVQ_TILE_TOKENS 64
 
 typedef enum {
@@ -502,6 +502,16 @@ kvq_status kvq_tri_attn_decode(const kvq_tri_desc* desc, const void* cache,
                                uint32_t num_q_heads, uint32_t seq_len, float softmax_scale,
                                void* out, kvq_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
+
+/* ===================================================================================
+ * Read-only streaming probe (context for the roofline of the cache-reading kernels; no
+ * codec work): reads `bytes` of device memory at `buf` once with 16-byte loads, as a
+ * plain streaming kernel would, and returns. `sink` is a device buffer of at least 256
+ * bytes that the kernel may write to (in practice it never does: a store happens only
+ * when the XOR of everything read equals one fixed 32-bit constant). buf 16-byte
+ * aligned, bytes a multiple of 16 (0 enqueues nothing). Errors: INVALID_ARGUMENT, HIP.
+ * =================================================================================== */
+kvq_status kvq_probe_read(const void* buf, size_t bytes, void* sink, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -16,4 +16,4 @@ from ._lib import (  # noqa: F401
     make_desc, tile_bytes,
     TriDesc, alloc_tri_cache, make_tri_desc, tri_attn_decode, tri_attn_workspace_bytes,
     tri_cache_bytes, tri_codebook, tri_codebook_device, tri_decode, tri_encode,
-    tri_record_words, tri_tile_bytes)
+    tri_record_words, tri_tile_bytes, probe_read)

@@ -123,6 +123,7 @@ _SIGS = {
     "kvq_tri_attn_workspace_bytes": (_sz, [_PT, _u32, _u32]),
     "kvq_tri_attn_decode": (ctypes.c_int, [_PT, _v, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
                                            ctypes.c_int, _v, _sz, _v]),
+    "kvq_probe_read": (ctypes.c_int, [_v, _sz, _v, _v]),
     "kvq_attn_static_scratch_bytes": (_sz, []),
     "kvq_attn_decode_static": (ctypes.c_int, [_P, _v, _v, ctypes.c_int, _u32, _u32, _f32, _v,
                                               ctypes.c_int, _v]),
@@ -699,3 +700,18 @@ def tri_attn_decode(desc: TriDesc, cache: torch.Tensor, codebook: torch.Tensor, 
                                    workspace.data_ptr(), workspace.numel(), _stream(q.device)),
            "kvq_tri_attn_decode")
     return out
+
+
+# ------------------------------------------------------------------ streaming probe
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of `buf` once on the device (kvq_probe_read); sink: a device
+    tensor of at least 256 bytes on the same device."""
+    _need(isinstance(buf, torch.Tensor) and buf.is_contiguous(), "buf must be a contiguous tensor")
+    _need(isinstance(sink, torch.Tensor) and sink.is_contiguous()
+          and sink.numel() * sink.element_size() >= 256, "sink must hold at least 256 bytes")
+    _same_device(("buf", buf), ("sink", sink))
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.kvq_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf.device)),
+           "kvq_probe_read")

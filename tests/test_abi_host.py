@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert kvq.abi_version() == 9
+    assert kvq.abi_version() == 10
     for s in range(6):
         assert lib.kvq_status_string(s)
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -321,3 +321,13 @@ def test_workspace_helper_reports_the_shape_status():
         kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 32, 64), 8, 256, "cpu")
     with pytest.raises(kvq.KvqError, match="CAPACITY"):
         kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 128, 64), 8, 300, "cpu")
+
+
+def test_probe_read_validation():
+    lib = kvq.lib
+    p = ctypes.c_void_p(4096)     # never dereferenced: each call fails its checks first
+    assert lib.kvq_probe_read(None, 16, p, None) == 1
+    assert lib.kvq_probe_read(p, 16, None, None) == 1
+    assert lib.kvq_probe_read(ctypes.c_void_p(4104), 16, p, None) == 1   # not 16-aligned
+    assert lib.kvq_probe_read(p, 24, p, None) == 1                       # not a multiple of 16
+    assert lib.kvq_probe_read(p, 0, p, None) == 0                        # nothing to read
