@@ -562,10 +562,9 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   a.part_acc = (float*)(base + l.acc);
   a.seq_lens = seq_lens;
   a.pg = pg;
-  // launches of at most 16 query rows each (consecutive query tokens), one after the
-  // other on the stream and sharing the workspace: the 16-row kernel keeps two waves
-  // per SIMD, which outweighs reading the cache once per launch
-  const uint32_t per = 16 / g;
+  // one launch for up to 32 query rows: the 16-row kernel, or the 32-row one, which
+  // reads the cache once for all of them
+  const uint32_t per = 32 / g;
   for (uint32_t q0 = 0; q0 < nq; q0 += per) {
     a.q0 = (int)q0;
     a.nqc = (int)(nq - q0 < per ? nq - q0 : per);

@@ -25,10 +25,14 @@ namespace {
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Waves per workgroup: 8 for 16 rows (two waves per SIMD fit its registers, so one
-// wave's LDS round trips overlap another's work), 4 for 32 rows (one per SIMD). The
-// library launches 16-row kernels only, splitting more rows over launches.
-constexpr int mq_waves(int rb) { return rb == 1 ? 8 : 4; }
+// Waves per workgroup: 8 for 16 rows and 6 for 32 rows (LDS holds six waves' tiles at
+// 32 rows); both keep two waves per SIMD, so one wave's LDS round trips overlap another's
+// work. The 32-row kernel holds one tile's code planes in registers at a time (key planes
+// loaded at the tile's start, value planes once the keys are rebuilt), reads the query
+// operands from LDS and scores one 16-row block at a time. At d = 128 it still spills
+// some 60-70 registers to scratch, and measured faster so (151 us per Mistral-7B-shaped
+// layer at 32 rows) than as four waves with no spill (167 us).
+constexpr int mq_waves(int rb) { return rb == 1 ? 8 : 6; }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __floats2half2_rn(lo, hi));
@@ -69,7 +73,11 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   constexpr int WAVEW = TILEW > MERGEW ? TILEW : MERGEW;
   constexpr int NKT = 1 << BK, NVT = 1 << BV;
   static_assert(M * D <= WAVEW, "rotated queries are staged in the first wave's space");
+  // 16 rows: the query operands live in registers; 32 rows: in LDS as fp16 rows
+  constexpr bool QREG = RB == 1;
+  constexpr int QROW = D / 2 + 1;  // dwords per fp16 query row (odd: fewer conflicts)
   __shared__ float2 lut_k[NKT], lut_v[NVT];
+  __shared__ uint32_t s_qh[QREG ? 1 : M * QROW];
   __shared__ __align__(16) uint32_t s_wave[kMqWaves][WAVEW];
   __shared__ uint32_t s_p[kMqWaves][M * PROW];
   __shared__ int s_flag;
@@ -105,31 +113,44 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
 
   const int vi = min(lane, P - 1);  // value pair of this lane (lanes past P repeat the last)
 
-  // The planes of this wave's next tile are loaded while the current one is processed,
-  // and the first tile's are requested before the set-up below, whose work then covers
-  // their latency. A tile the page table maps to no page reads page 0 and counts as
-  // holding no token.
+  // 16 rows: the planes of this wave's next tile are loaded while the current one is
+  // processed, and the first tile's are requested before the set-up below, whose work
+  // then covers their latency. 32 rows (no room for two tiles' planes in registers):
+  // a tile's key planes are loaded at its start and its value planes once the keys are
+  // rebuilt, their latency covered by the scores and the other wave of the SIMD. A tile
+  // the page table maps to no page reads page 0 and counts as holding no token.
   struct Planes {
     uint32_t ka[GE::WKA], kr[GE::WKR], va[2 * BV], vr[8], ks, vp;
     bool present;
   };
-  auto load_planes = [&](Planes& t, int tile) {
+  auto tile_words = [&](int tile, bool* present) {
     const long long off = tile_offset(a.pg, b, kvh, a.hkv, a.tiles_per_seq, tile, GE::BYTES);
-    t.present = off >= 0;
-    const uint32_t* w32 = reinterpret_cast<const uint32_t*>(cache + (off >= 0 ? off : 0));
+    *present = off >= 0;
+    return reinterpret_cast<const uint32_t*>(cache + (off >= 0 ? off : 0));
+  };
+  auto load_key_planes = [&](Planes& t, int tile) {
+    const uint32_t* w32 = tile_words(tile, &t.present);
 #pragma unroll
     for (int w = 0; w < GE::WKA; ++w) t.ka[w] = w32[w * kTile + lane];
 #pragma unroll
     for (int w = 0; w < GE::WKR; ++w) t.kr[w] = w32[GE::OFF_KR / 4 + w * kTile + lane];
     t.ks = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(w32) + GE::OFF_KS)[lane];
+  };
+  auto load_value_planes = [&](Planes& t, int tile) {
+    bool present;
+    const uint32_t* w32 = tile_words(tile, &present);
     t.vp = w32[GE::OFF_VP / 4 + lane];
 #pragma unroll
     for (int w = 0; w < 2 * BV; ++w) t.va[w] = w32[GE::OFF_VA / 4 + w * P + vi];
 #pragma unroll
     for (int w = 0; w < 8; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + w * P + vi];
   };
+  constexpr bool DB = RB == 1;  // next tile's planes loaded during the current one
   Planes nxt;
-  if (tile_begin + wave < tile_end) load_planes(nxt, tile_begin + wave);
+  if (DB && tile_begin + wave < tile_end) {
+    load_key_planes(nxt, tile_begin + wave);
+    load_value_planes(nxt, tile_begin + wave);
+  }
 
   for (int c = tid; c < NKT; c += kMqWaves * 64) {
     float sn = 0.f, co = 0.f;
@@ -152,14 +173,21 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
     if (lane < P) reinterpret_cast<float2*>(s_q)[row * P + lane] = v;
   }
   __syncthreads();
-  h4 qa[RB][NS];
+  h4 qa[QREG ? RB : 1][QREG ? NS : 1];
+  if constexpr (QREG) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float4 f = *reinterpret_cast<const float4*>(s_q + (16 * rb + l16) * D + 16 * s + 4 * g4);
-      qa[rb][s] = h4{(_Float16)f.x, (_Float16)f.y, (_Float16)f.z, (_Float16)f.w};
+      for (int s = 0; s < NS; ++s) {
+        const float4 f = *reinterpret_cast<const float4*>(s_q + (16 * rb + l16) * D + 16 * s + 4 * g4);
+        qa[rb][s] = h4{(_Float16)f.x, (_Float16)f.y, (_Float16)f.z, (_Float16)f.w};
+      }
+  } else {
+    for (int idx = tid; idx < M * P; idx += kMqWaves * 64) {
+      const float2 f = reinterpret_cast<const float2*>(s_q)[idx];
+      s_qh[(idx / P) * QROW + idx % P] = pack_h2(f.x, f.y);
     }
+  }
   // tokens visible to each accumulator row of this lane (0 for padding rows)
   int lim[RB][4];
 #pragma unroll
@@ -187,14 +215,22 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   uint32_t* pb = s_p[wave];
 
   for (int tile = tile_begin + wave; tile < tile_end; tile += kMqWaves) {
-    const Planes cur = nxt;
-    if (tile + kMqWaves < tile_end) load_planes(nxt, tile + kMqWaves);
+    Planes cur;
+    if constexpr (DB) {
+      cur = nxt;
+      if (tile + kMqWaves < tile_end) {
+        load_key_planes(nxt, tile + kMqWaves);
+        load_value_planes(nxt, tile + kMqWaves);
+      }
+    } else {
+      load_key_planes(cur, tile);
+    }
+    const bool present = cur.present;
     const uint32_t(&ka)[GE::WKA] = cur.ka;
     const uint32_t(&kr)[GE::WKR] = cur.kr;
     const uint32_t(&va)[2 * BV] = cur.va;
     const uint32_t(&vr)[8] = cur.vr;
     const uint16_t ks = (uint16_t)cur.ks;
-    const uint32_t vp = cur.vp;
     const bool tvalid = cur.present && tile * kTile + lane < seq_len;
 
     // ---- key tile K^[token][feature] (fp16, rotated domain, radius s / 255 * code)
@@ -205,38 +241,52 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
         const float2 cs = lut_k[field<BK>(ka, i)];
         const float r = (float)((kr[i >> 2] >> (8 * (i & 3))) & 0xFFu) * ksc;
         kb[lane * KROW + i] = pack_h2(r * cs.x, r * cs.y);
+        if (!DB && (i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (!DB) load_value_planes(cur, tile);
+    const uint32_t vp = cur.vp;
     __builtin_amdgcn_wave_barrier();
 
-    // ---- scores S = q~ K^T: fragment [rb][blk] holds rows 16 rb + 4 g4 + r, token
-    // 16 blk + l16
-    f4 sc[RB][4];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      h4 kv[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) kv[s] = h4_from(kb + (16 * blk + l16) * KROW + 8 * s + 2 * g4);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[rb][s], kv[s], acc, 0, 0, 0);
-        sc[rb][blk] = acc;
-      }
-    }
-
-    // ---- online softmax per row (base 2); probabilities to LDS as fp16 [row][token]
+    // ---- per 16-row block: scores S = q~ K^T (fragment [blk] holds rows
+    // 16 rb + 4 g4 + r, token 16 blk + l16), then the online softmax per row (base 2),
+    // probabilities to LDS as fp16 [row][token]
     _Float16* ph = reinterpret_cast<_Float16*>(pb);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+      f4 sc[4];
+      if constexpr (QREG) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          h4 kv[NS];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) kv[s] = h4_from(kb + (16 * blk + l16) * KROW + 8 * s + 2 * g4);
+          f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[rb][s], kv[s], acc, 0, 0, 0);
+          sc[blk] = acc;
+        }
+      } else {
+        // one query fragment per feature block, read from LDS, serves the four token blocks
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) sc[blk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const h4 qv = h4_from(s_qh + (16 * rb + l16) * QROW + 8 * s + 2 * g4);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            const h4 kv = h4_from(kb + (16 * blk + l16) * KROW + 8 * s + 2 * g4);
+            sc[blk] = __builtin_amdgcn_mfma_f32_16x16x16f16(qv, kv, sc[blk], 0, 0, 0);
+          }
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v[4], mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
           const int t = tile * kTile + 16 * blk + l16;
-          v[blk] = cur.present && t < lim[rb][r] ? sc[rb][blk][r] : -INFINITY;
+          v[blk] = present && t < lim[rb][r] ? sc[blk][r] : -INFINITY;
           mx = fmaxf(mx, v[blk]);
         }
         mx = row16_max(mx);
@@ -256,6 +306,7 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
 #pragma unroll
         for (int s = 0; s < NS; ++s) o[rb][s][r] *= alpha;
       }
+    }
     __builtin_amdgcn_wave_barrier();
 
     // ---- value tile V^[feature][token] in the key tile's space (its reads are done):
@@ -293,6 +344,8 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
           x0 = x;
           y0 = y;
         }
+        // 32 rows: the scheduler may not gather all of the loop's table reads up front
+        if (!DB && (t & 15) == 15) __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -439,6 +492,8 @@ hipError_t launch_attn_multi(const AttnArgs& a, int d, int rows, const uint8_t* 
 #define KVQ_MQ_BK(D_, RB_) KVQ_MQ_BV(D_, 6, RB_) KVQ_MQ_BV(D_, 7, RB_) KVQ_MQ_BV(D_, 8, RB_)
   KVQ_MQ_BK(64, 1)
   KVQ_MQ_BK(128, 1)
+  KVQ_MQ_BK(64, 2)
+  KVQ_MQ_BK(128, 2)
 #undef KVQ_MQ_BK
 #undef KVQ_MQ_BV
 #undef KVQ_MQ
