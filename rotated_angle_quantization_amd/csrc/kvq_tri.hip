@@ -19,13 +19,15 @@
 //              elements are permuted back to two per lane for the inverse transform.
 //   attention  split kernel (grid: splits x batch * kv heads, four waves, a wave per
 //              64-token tile): scores with one lane per token, the key plane staged in
-//              LDS and a table of the 2^(2 bits_dir) reconstructed directions; online
-//              softmax per wave; values with one lane per triplet, summing
-//              p * N * rho * w over the tile's tokens; waves merge in LDS and each split
-//              writes (max, sum, rotated vector) per query head. A merge kernel (a wave
-//              per output row) combines the splits with a log-sum-exp and applies the
-//              inverse transform. Far more arithmetic per byte than the angle codec (a
-//              few bits per element): this path is bound by VALU and LDS work.
+//              LDS (rows padded by a word) and a table of the 2^(2 bits_dir)
+//              reconstructed directions; online softmax per wave; values with one lane
+//              per triplet, summing p * N * rho * w over the tile's tokens; both products
+//              on the matrix cores in fp32 (four query heads per instruction); waves
+//              merge in LDS and each split writes (max, sum, rotated vector) per query
+//              head. A merge kernel (a wave per output row) combines the splits with a
+//              log-sum-exp and applies the inverse transform. Far more arithmetic per
+//              byte than the angle codec (a few bits per element): this path is bound by
+//              the rebuild of the operands (VALU and LDS).
 #include <math.h>
 #include <string.h>
 
@@ -308,13 +310,24 @@ struct TriAttnArgs {
 };
 
 constexpr int kTriWaves = 4;
+constexpr int kTriMaxWords = 32;  // record words the attention kernel serves
 
-// Field f of the record of slot `lane` in a plane staged in LDS as [words][64].
+typedef float mf4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ mf4 tri_mfma(float a, float b, mf4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+// A plane staged in LDS as [words][kPlaneRow]: a row of 64 slots plus one pad word, so
+// the words of one slot (read together when a lane owns a field and loops over slots)
+// fall in different banks.
+constexpr int kPlaneRow = kTile + 1;
+
+// Field f of the record of slot `slot` in a staged plane.
 __device__ __forceinline__ uint32_t staged_field(const uint32_t* plane, int off, int wd, int words,
                                                  int slot) {
   const int wi = off >> 5;
-  const uint32_t lo = plane[wi * kTile + slot];
-  const uint32_t hi = wi + 1 < words ? plane[(wi + 1) * kTile + slot] : 0u;
+  const uint32_t lo = plane[wi * kPlaneRow + slot];
+  const uint32_t hi = wi + 1 < words ? plane[(wi + 1) * kPlaneRow + slot] : 0u;
   const uint64_t win = ((uint64_t)hi << 32) | lo;
   return (uint32_t)(win >> (off & 31)) & ((1u << wd) - 1u);
 }
@@ -330,8 +343,8 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   __shared__ float4 s_dir[(1 << DIRB) * (1 << DIRB)];
   __shared__ float s_ln[kTriMaxLevelsNorm], s_lr[kTriMaxLevelsRest];
   __shared__ float4 s_q3[G][T + 1];        // (q~[3j], q~[3j+1], q~[3j+2], 0); row T: leftovers
-  __shared__ uint32_t s_plane[kTriWaves][32 * kTile];  // up to 32 record words
-  __shared__ float s_w[kTriWaves][G][kTile];           // p * N per token
+  __shared__ uint32_t s_plane[kTriWaves][32 * kPlaneRow];  // up to 32 record words
+  __shared__ __align__(16) float s_w[kTriWaves][kTile][G];  // p * N per token and head
   __shared__ float s_ml[kTriWaves][G][2];
   __shared__ float s_acc[kTriWaves][G][D];
 
@@ -394,33 +407,63 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   const int f = lane < nf ? lane : 0;
   const int foff = field_off(g, f), fwd = field_width(g, f);
 
-  float m[G], l[G], acc[G][3];
+  // Both products run on the matrix cores in fp32 (v_mfma_f32_4x4x1f32: lane 4b + i
+  // supplies row i of block b's A operand, lane l column l of B, and lane l accumulates
+  // D[l][i] += A[4 (l / 4) + i] * B[l]); with the query heads as the rows, A in lane l is
+  // head 4 hg + (l & 3)'s operand. Scores: lane = token, B = the token's rebuilt key
+  // element rho * w[c]; values: lane = triplet (or leftover), B = its element of the
+  // token's rebuilt value, A = the token's weight. One instruction does the 64 x 4
+  // products that take four FMAs per lane and head on the vector units.
+  constexpr int HG = G > 4 ? G / 4 : 1;
+  const int hl = lane & 3;
+  float m[G], l[G];
+  mf4 ax[HG], ay[HG], az[HG];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m[hh] = -INFINITY;
     l[hh] = 0.f;
-    acc[hh][0] = acc[hh][1] = acc[hh][2] = 0.f;
   }
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) ax[hg] = ay[hg] = az[hg] = mf4{0.f, 0.f, 0.f, 0.f};
   uint32_t* plane = s_plane[wave];
-  for (int tile = tile_begin + wave; tile < tile_end; tile += kTriWaves) {
+  // Both planes of a tile are loaded into registers at once (all loads in flight), the
+  // next tile's as soon as the current value plane is staged, so their latency overlaps
+  // the value sum.
+  uint32_t kw[kTriMaxWords], vw[kTriMaxWords];
+  const int words = g.words;
+  auto load_tile = [&](int tile) {
     const uint32_t* tw = reinterpret_cast<const uint32_t*>(base + (size_t)tile * tile_bytes);
+#pragma unroll
+    for (int w = 0; w < kTriMaxWords; ++w)
+      if (w < words) {
+        kw[w] = tw[w * kTile + lane];
+        vw[w] = tw[(words + w) * kTile + lane];
+      }
+  };
+  if (tile_begin + wave < tile_end) load_tile(tile_begin + wave);
+  for (int tile = tile_begin + wave; tile < tile_end; tile += kTriWaves) {
     const int nvalid = min(a.seq_len - tile * kTile, kTile);
     const bool valid = lane < nvalid;
     // ---- keys: stage the key plane, one lane per token
-    for (int w = 0; w < g.words; ++w) plane[w * kTile + lane] = tw[w * kTile + lane];
+#pragma unroll
+    for (int w = 0; w < kTriMaxWords; ++w)
+      if (w < words) plane[w * kPlaneRow + lane] = kw[w];
     asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
     const float nu_k = __half2float(__ushort_as_half((uint16_t)(plane[lane] & 0xFFFFu)));
-    float sc[G];
+    mf4 kx[HG], ky[HG], kz[HG];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) sc[hh] = 0.f;
+    for (int hg = 0; hg < HG; ++hg) kx[hg] = ky[hg] = kz[hg] = mf4{0.f, 0.f, 0.f, 0.f};
     for (int jt = 0; jt < T; ++jt) {
       const uint32_t val = staged_field(plane, 16 + jt * g.B, g.B, g.words, lane);
       const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
       const float rho = s_ln[val >> (2 * g.bd)];
+      const float bx = rho * w4.x, by = rho * w4.y, bz = rho * w4.z;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float4 q4 = s_q3[hh][jt];
-        sc[hh] = fmaf(rho, fmaf(q4.x, w4.x, fmaf(q4.y, w4.y, q4.z * w4.z)), sc[hh]);
+      for (int hg = 0; hg < HG; ++hg) {
+        const float4 q4 = s_q3[min(4 * hg + hl, G - 1)][jt];  // rows past G: unused sums
+        kx[hg] = tri_mfma(q4.x, bx, kx[hg]);
+        ky[hg] = tri_mfma(q4.y, by, ky[hg]);
+        kz[hg] = tri_mfma(q4.z, bz, kz[hg]);
       }
     }
 #pragma unroll
@@ -428,52 +471,56 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
       const uint32_t val = staged_field(plane, 16 + T * g.B + r * g.br, g.br, g.words, lane);
       const float u = s_lr[val];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float4 q4 = s_q3[hh][T];
-        sc[hh] = fmaf(u, r == 0 ? q4.x : (r == 1 ? q4.y : q4.z), sc[hh]);
+      for (int hg = 0; hg < HG; ++hg) {
+        const float4 q4 = s_q3[min(4 * hg + hl, G - 1)][T];
+        kx[hg] = tri_mfma(r == 0 ? q4.x : (r == 1 ? q4.y : q4.z), u, kx[hg]);
       }
     }
-    // ---- value plane staged, then the softmax weights p * N per token
-    const float nu_v = __half2float(__ushort_as_half((uint16_t)(tw[g.words * kTile + lane] & 0xFFFFu)));
+    // ---- value plane staged (the next tile's planes are requested), then the softmax
+    // weights p * N per token
+    const float nu_v = __half2float(__ushort_as_half((uint16_t)(vw[0] & 0xFFFFu)));
     asm volatile("" ::: "memory");
-    for (int w = 0; w < g.words; ++w) plane[w * kTile + lane] = tw[(g.words + w) * kTile + lane];
+#pragma unroll
+    for (int w = 0; w < kTriMaxWords; ++w)
+      if (w < words) plane[w * kPlaneRow + lane] = vw[w];
+    if (tile + kTriWaves < tile_end) load_tile(tile + kTriWaves);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float s = valid ? sc[hh] * nu_k : -INFINITY;
+      const float sc = kx[hh >> 2][hh & 3] + ky[hh >> 2][hh & 3] + kz[hh >> 2][hh & 3];
+      const float s = valid ? sc * nu_k : -INFINITY;
       const float mnew = fmaxf(m[hh], wave_max(s));
       const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[hh] - mnew);
       l[hh] *= alpha;
-      acc[hh][0] *= alpha;
-      acc[hh][1] *= alpha;
-      acc[hh][2] *= alpha;
+      ax[hh >> 2][hh & 3] *= alpha;
+      ay[hh >> 2][hh & 3] *= alpha;
+      az[hh >> 2][hh & 3] *= alpha;
       m[hh] = mnew;
       const float pv = m[hh] == -INFINITY ? 0.f : fast_exp2(s - m[hh]);
       l[hh] += pv;
-      s_w[wave][hh][lane] = valid ? pv * nu_v : 0.f;
+      s_w[wave][lane][hh] = valid ? pv * nu_v : 0.f;
     }
     asm volatile("" ::: "memory");
-    // ---- values: lane f rebuilds its triplet (or leftover) of every token
-    if (lane < nf) {
-      for (int tk = 0; tk < kTile; ++tk) {
-        const uint32_t val = staged_field(plane, foff, fwd, g.words, tk);
-        float c0, c1, c2;
-        if (f < T) {
-          const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
-          const float rho = s_ln[val >> (2 * g.bd)];
-          c0 = rho * w4.x;
-          c1 = rho * w4.y;
-          c2 = rho * w4.z;
-        } else {
-          c0 = s_lr[val];
-          c1 = c2 = 0.f;
-        }
+    // ---- values: lane f rebuilds its triplet (or leftover) of every token; the matrix
+    // instructions run on the whole wave, lanes past the fields contributing zero
+    for (int tk = 0; tk < kTile; ++tk) {
+      const uint32_t val = staged_field(plane, foff, fwd, g.words, tk);
+      float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+      if (f < T) {
+        const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+        const float rho = s_ln[val >> (2 * g.bd)];
+        c0 = rho * w4.x;
+        c1 = rho * w4.y;
+        c2 = rho * w4.z;
+      } else {
+        c0 = s_lr[val];
+      }
+      if (lane >= nf) c0 = c1 = c2 = 0.f;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float wgt = s_w[wave][hh][tk];
-          acc[hh][0] = fmaf(wgt, c0, acc[hh][0]);
-          acc[hh][1] = fmaf(wgt, c1, acc[hh][1]);
-          acc[hh][2] = fmaf(wgt, c2, acc[hh][2]);
-        }
+      for (int hg = 0; hg < HG; ++hg) {
+        const float wgt = s_w[wave][tk][min(4 * hg + hl, G - 1)];
+        ax[hg] = tri_mfma(wgt, c0, ax[hg]);
+        ay[hg] = tri_mfma(wgt, c1, ay[hg]);
+        az[hg] = tri_mfma(wgt, c2, az[hg]);
       }
     }
     asm volatile("" ::: "memory");
@@ -491,12 +538,13 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   if (lane < nf) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
+      const float v0 = ax[hh >> 2][hh & 3], v1 = ay[hh >> 2][hh & 3], v2 = az[hh >> 2][hh & 3];
       if (f < T) {
-        s_acc[wave][hh][3 * f] = acc[hh][0];
-        s_acc[wave][hh][3 * f + 1] = acc[hh][1];
-        s_acc[wave][hh][3 * f + 2] = acc[hh][2];
+        s_acc[wave][hh][3 * f] = v0;
+        s_acc[wave][hh][3 * f + 1] = v1;
+        s_acc[wave][hh][3 * f + 2] = v2;
       } else {
-        s_acc[wave][hh][3 * T + (f - T)] = acc[hh][0];
+        s_acc[wave][hh][3 * T + (f - T)] = v0;
       }
     }
   }
