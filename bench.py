@@ -592,7 +592,9 @@ def main():
                          f"{Hq} query heads, d={d}, fp16 K/V, per-layer (n_K, n_V) = "
                          f"{sorted(set(cfg.bins(x) for x in range(L)))}"),
             "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
-            "encode_decisions": "f64", "attention_arithmetic": "f32",
+            "encode_decisions": "f64",
+            "attention_arithmetic": "f32 (value products on the matrix cores: fp16 operands, "
+                                    "fp32 sums)",
         },
         "hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "encode_tokens_per_s": round(tokens / (enc_ms * 1e-3), 1),

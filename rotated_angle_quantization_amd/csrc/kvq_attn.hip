@@ -177,22 +177,27 @@ __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
 
 // ---------------------------------------------------------------- matrix-core mode
 //
-// KTM 3: both products of a tile run on the matrix cores in fp32
-// (v_mfma_f32_4x4x1f32: sixteen independent 4x4 blocks, k = 1). Lane 4b + i supplies
-// row i of block b's A operand, lane 4b + j column j of its B operand, and lane 4b + j
-// receives D[b][0..3][j] in its four result registers (checked on the GPU against a host
+// KTM 3 (scores) and bit 2 of KTM (values) run a tile's products on the matrix cores:
+// sixteen independent 4x4 blocks per instruction. Lane 4b + i supplies row i of block
+// b's A operand, lane 4b + j column j of its B operand, and lane 4b + j receives
+// D[b][0..3][j] in its four result registers (checked on the GPU against a host
 // product). With the query heads of a kv head as the four rows:
-//   scores  lane = token: A = q~[head][e] (lane l holds head l & 3), B = the token's
-//           reconstructed rotated key element rho * (cos, sin)[code]; one product per
-//           element e leaves the four heads' scores in the token's lane.
-//   values  lane = pair (d = 128) or pair and token half (d = 64): A = the softmax weight
-//           of token t for head l & 3, B = level(rho) * (cos, sin)[code] of token t in
-//           the lane's pair; the rotated-domain sums of the four heads accumulate in
-//           the pair's lane.
-// Each product is one instruction for 64 (token or pair, head) terms, where the vector
-// path spends one FMA per 16: the VALU keeps only code unpacking, table lookups and the
-// two multiplies per element. Rows past G are zero.
+//   scores  v_mfma_f32_4x4x1f32 (fp32, k = 1), lane = token: A = q~[head][e] (lane l
+//           holds head l & 3), B = the token's reconstructed rotated key element
+//           rho * (cos, sin)[code]; one product per element e leaves the four heads'
+//           scores in the token's lane. Kept in fp32: with fp16 keys and queries a CPU
+//           emulation over real codes puts the attention error at up to 2e-3 on inputs
+//           with outlier channels (large logits).
+//   values  v_mfma_f32_4x4x4f16 (fp16 operands, fp32 sums, k = 4 tokens), lane = pair
+//           (d = 128) or pair and token half (d = 64): A = the softmax weights of four
+//           tokens for head l & 3, B = level(rho) * (cos, sin)[code] of those tokens in
+//           the lane's pair (formed in fp32, rounded once to fp16); the rotated-domain
+//           sums of the four heads accumulate in the pair's lane. Rounding the operands
+//           adds about 2^-11 relative per term, well inside the attention bound.
+// The VALU keeps only code unpacking, table lookups and the multiplies per element.
+// Rows past G are zero.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4x __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma4x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
@@ -675,19 +680,24 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
         for (int hg = 0; hg < M::HG; ++hg)
           pa[hg] = *reinterpret_cast<const float4*>(
               w_ps + hg * 4 * kTile + (lane & 3) * kTile + th * 32 + 4 * t4);
+        float vx[4], vy[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int t = 4 * t4 + u;
           const float2 cs = lut_v[field<BV>(cur.va, t)];
           const uint32_t rho = (cur.vr[t >> 3] >> (4 * (t & 7))) & 0xFu;
           const float lvl = w_lev[(th * 32 + t) * 16 + rho];
-          const float vx = lvl * cs.x, vy = lvl * cs.y;
+          vx[u] = lvl * cs.x;
+          vy[u] = lvl * cs.y;
+        }
+        // four tokens per product: fp16 operands, fp32 sums
+        const h4x bx = h4x{(_Float16)vx[0], (_Float16)vx[1], (_Float16)vx[2], (_Float16)vx[3]};
+        const h4x by = h4x{(_Float16)vy[0], (_Float16)vy[1], (_Float16)vy[2], (_Float16)vy[3]};
 #pragma unroll
-          for (int hg = 0; hg < M::HG; ++hg) {
-            const float pw = u == 0 ? pa[hg].x : u == 1 ? pa[hg].y : u == 2 ? pa[hg].z : pa[hg].w;
-            ax[hg] = mfma4x4(pw, vx, ax[hg]);
-            ay[hg] = mfma4x4(pw, vy, ay[hg]);
-          }
+        for (int hg = 0; hg < M::HG; ++hg) {
+          const h4x pw = h4x{(_Float16)pa[hg].x, (_Float16)pa[hg].y, (_Float16)pa[hg].z, (_Float16)pa[hg].w};
+          ax[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pw, bx, ax[hg], 0, 0, 0);
+          ay[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pw, by, ay[hg], 0, 0, 0);
         }
       }
       asm volatile("" ::: "memory");  // the next tile's LDS writes stay after these reads
