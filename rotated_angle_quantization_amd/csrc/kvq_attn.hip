@@ -847,9 +847,18 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
   // ---- cross-split merge by the last workgroup of this (batch, kv head) to finish:
   // once its partial results are complete in memory it takes a ticket; the holder of
   // the last ticket combines the splits (log-sum-exp), applies the inverse transform
-  // and resets the counter. The partials are written and read with device-coherent
-  // accesses, so completion of the stores (waitcnt) is all the ordering needed, and no
-  // agent-wide cache write-back or invalidate is issued.
+  // and resets the counter. The ordering rests on three properties of gfx950 rather
+  // than on release/acquire fences (which here write back or invalidate the whole L2 of
+  // an XCD and made the kernel 2-3x slower):
+  //  1. the partials are stored and later loaded as agent-scope atomics, which the
+  //     compiler emits with the device-coherence cache policy: they are performed past
+  //     the per-XCD L2, so no stale copy of them can be read on another XCD;
+  //  2. s_waitcnt vmcnt(0) returns only once those stores are acknowledged, i.e.
+  //     performed at that coherence point, and it precedes the barrier after which one
+  //     thread takes the ticket, so every store of the workgroup is performed first;
+  //  3. the ticket is a system-scope atomic add, performed at memory in a single total
+  //     order, so the workgroup that draws the last ticket does so after all others
+  //     have performed their stores, and its coherent loads (1) then observe them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {

@@ -421,8 +421,10 @@ __global__ __launch_bounds__(mq_waves(RB) * 64) void attn_multi_kernel(AttnArgs 
   }
   if (!single) {
     // the last workgroup of this (batch, kv head) to finish combines the splits; the
-    // partials are written and read with device-coherent accesses, so completion of the
-    // stores is all the ordering needed
+    // partials are written and read as agent-scope atomics (device-coherent cache
+    // policy), the stores are performed before the ticket is taken (waitcnt, then the
+    // barrier) and the ticket is a system-scope atomic: the same ordering argument as
+    // the decode-attention kernel's merge
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
