@@ -474,7 +474,8 @@ kvq_status kvq_tri_codebook(const kvq_tri_desc* desc, double* out_host);
  * strides in elements, d contiguous, fp16 or fp32). The transform, N, the triplet norms,
  * the square coordinates and every decision are taken in IEEE binary64. codebook: the
  * device copy of kvq_tri_codebook's table. Slots outside the range keep their bytes.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (d not 64/128), CAPACITY, HIP.
+ * Errors: INVALID_ARGUMENT (also for batch * ntok * num_kv_heads above 2^32 - 256),
+ * UNSUPPORTED (d not 64/128), CAPACITY, HIP.
  */
 kvq_status kvq_tri_encode(const kvq_tri_desc* desc, void* cache, const double* codebook,
                           const void* k, const void* v, kvq_dtype in_dtype, int64_t stride_b,

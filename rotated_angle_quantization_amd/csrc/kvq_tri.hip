@@ -116,12 +116,13 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long long total = (long long)a.batch * a.ntok * a.hkv;
+  // token-head index in 32 bits (the host keeps B * ntok * Hkv below 2^32)
+  const unsigned item = blockIdx.x * 4u + (unsigned)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned total = (unsigned)a.batch * (unsigned)a.ntok * (unsigned)a.hkv;
   if (item >= total) return;
-  const int h = (int)(item % a.hkv);
-  const long long bj = item / a.hkv;
-  const int j = (int)(bj % a.ntok), b = (int)(bj / a.ntok);
+  const int h = (int)(item % (unsigned)a.hkv);
+  const unsigned bj = item / (unsigned)a.hkv;
+  const int j = (int)(bj % (unsigned)a.ntok), b = (int)(bj / (unsigned)a.ntok);
   const int slot = a.t0 + j, tile = slot / kTile, t = slot % kTile;
   const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
   uint32_t* tp = reinterpret_cast<uint32_t*>(
@@ -226,12 +227,13 @@ __global__ __launch_bounds__(256) void tri_decode_kernel(TriArgs a, const uint8_
   for (int i = threadIdx.x; i < g.nr; i += 256) s_lr[i] = (float)a.cb[g.nd + g.nn + i];
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long long total = (long long)a.batch * a.ntok * a.hkv;
+  // token-head index in 32 bits (the host keeps B * ntok * Hkv below 2^32)
+  const unsigned item = blockIdx.x * 4u + (unsigned)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned total = (unsigned)a.batch * (unsigned)a.ntok * (unsigned)a.hkv;
   if (item >= total) return;
-  const int h = (int)(item % a.hkv);
-  const long long bj = item / a.hkv;
-  const int j = (int)(bj % a.ntok), b = (int)(bj / a.ntok);
+  const int h = (int)(item % (unsigned)a.hkv);
+  const unsigned bj = item / (unsigned)a.hkv;
+  const int j = (int)(bj % (unsigned)a.ntok), b = (int)(bj / (unsigned)a.ntok);
   const int slot = a.t0 + j, tile = slot / kTile, t = slot % kTile;
   const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
   const uint32_t* tp = reinterpret_cast<const uint32_t*>(
@@ -915,7 +917,7 @@ kvq_status kvq_tri_encode(const kvq_tri_desc* d, void* cache, const double* cb, 
   if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
   const TriArgs a = tri_args(d, cb, t0, ntok);
   const long long items = (long long)d->batch * ntok * d->num_kv_heads;
-  if ((items + 3) / 4 > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+  if (items > 0xFFFFFF00LL) return KVQ_ERR_INVALID_ARGUMENT;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
   const bool f32 = in_dtype == KVQ_F32;
@@ -941,7 +943,7 @@ kvq_status kvq_tri_decode(const kvq_tri_desc* d, const void* cache, const double
   if (((uintptr_t)k_out % 8) || ((uintptr_t)v_out % 8)) return KVQ_ERR_INVALID_ARGUMENT;
   const TriArgs a = tri_args(d, cb, t0, ntok);
   const long long items = (long long)d->batch * ntok * d->num_kv_heads;
-  if ((items + 3) / 4 > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+  if (items > 0xFFFFFF00LL) return KVQ_ERR_INVALID_ARGUMENT;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
   const uint8_t* c = (const uint8_t*)cache;
