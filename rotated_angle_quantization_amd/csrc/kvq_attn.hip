@@ -198,6 +198,7 @@ __device__ __forceinline__ float bperm_f(int byte_addr, float v) {
 // Rows past G are zero.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h4x __attribute__((ext_vector_type(4)));
+typedef _Float16 h2x __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma4x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
@@ -382,7 +383,10 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
   for (int c = tid; c < (1 << BV); c += NW * 64) {
     float sn = 0.f, co = 0.f;
     if (c < a.n_v) sincospif(2.0f * (float)c / (float)a.n_v, &sn, &co);
-    lut_v[c] = make_float2(co, sn);
+    if constexpr (MXV)  // matrix-core values: fp16 pairs, the operand type
+      reinterpret_cast<h2x*>(lut_v)[c] = h2x{(_Float16)co, (_Float16)sn};
+    else
+      lut_v[c] = make_float2(co, sn);
   }
   __syncthreads();
   float* ktab = reinterpret_cast<float*>(s_union);
@@ -478,6 +482,9 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
   float* w_ps = reinterpret_cast<float*>(s_union) + (TAB ? P * NTAB * G : 0) +
                 wave * (M::WAVE_BYTES / 4);
   float* w_lev = w_ps + M::PS_FLOATS;
+  // the weights are kept as fp16, the matrix instructions' operand type (rows of 64
+  // halves in the first half of the space reserved for them)
+  _Float16* w_ph = reinterpret_cast<_Float16*>(w_ps);
   if constexpr (MX) {
 #pragma unroll
     for (int hg = 0; hg < M::HG; ++hg) {
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
       // weight rows of heads past G are zero for the whole launch
       if constexpr (MXV) {
 #pragma unroll
-        for (int g = G; g < 4 * M::HG; ++g) w_ps[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = 0.f;
+        for (int g = G; g < 4 * M::HG; ++g) w_ph[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = (_Float16)0.f;
       }
     }
   }
@@ -632,12 +639,14 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
       }
     }
     if constexpr (MXV) {
-      float4* dst = reinterpret_cast<float4*>(w_lev + lane * 16);
+      // fp16 levels (in [2^-14, 65504] or 0), the operand type of the value products
+      h4x* dst = reinterpret_cast<h4x*>(reinterpret_cast<_Float16*>(w_lev) + lane * 16);
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
-        dst[r / 4] = make_float4(r0 * fast_exp2((float)r * beta), r0 * fast_exp2((float)(r + 1) * beta),
-                                 r0 * fast_exp2((float)(r + 2) * beta),
-                                 r0 * fast_exp2((float)(r + 3) * beta));
+        dst[r / 4] = h4x{(_Float16)(r0 * fast_exp2((float)r * beta)),
+                         (_Float16)(r0 * fast_exp2((float)(r + 1) * beta)),
+                         (_Float16)(r0 * fast_exp2((float)(r + 2) * beta)),
+                         (_Float16)(r0 * fast_exp2((float)(r + 3) * beta))};
     }
 
     // ---- online softmax per head (lane = token), base 2; slots past the end get 0
@@ -663,7 +672,7 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
       const float pv = m[g] == -INFINITY ? 0.f : fast_exp2(s - m[g]);
       l[g] += pv;
       pr[g] = pv * r0;
-      if constexpr (MXV) w_ps[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = pv;
+      if constexpr (MXV) w_ph[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = (_Float16)pv;
     }
 
     if constexpr (MXV) {
@@ -675,29 +684,28 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
       const int th = D == 128 ? 0 : lane >> 5;
 #pragma unroll
       for (int t4 = 0; t4 < M::VT / 4; ++t4) {
-        float4 pa[M::HG];
+        h4x pa[M::HG];
 #pragma unroll
         for (int hg = 0; hg < M::HG; ++hg)
-          pa[hg] = *reinterpret_cast<const float4*>(
-              w_ps + hg * 4 * kTile + (lane & 3) * kTile + th * 32 + 4 * t4);
-        float vx[4], vy[4];
+          pa[hg] = *reinterpret_cast<const h4x*>(
+              w_ph + hg * 4 * kTile + (lane & 3) * kTile + th * 32 + 4 * t4);
+        // the four tokens' rebuilt elements level * (cos, sin), one packed fp16 product
+        // each; four tokens per matrix instruction, fp32 sums
+        h2x v2[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int t = 4 * t4 + u;
-          const float2 cs = lut_v[field<BV>(cur.va, t)];
+          const h2x cs = reinterpret_cast<const h2x*>(lut_v)[field<BV>(cur.va, t)];
           const uint32_t rho = (cur.vr[t >> 3] >> (4 * (t & 7))) & 0xFu;
-          const float lvl = w_lev[(th * 32 + t) * 16 + rho];
-          vx[u] = lvl * cs.x;
-          vy[u] = lvl * cs.y;
+          const _Float16 lvl = reinterpret_cast<const _Float16*>(w_lev)[(th * 32 + t) * 16 + rho];
+          v2[u] = h2x{lvl, lvl} * cs;
         }
-        // four tokens per product: fp16 operands, fp32 sums
-        const h4x bx = h4x{(_Float16)vx[0], (_Float16)vx[1], (_Float16)vx[2], (_Float16)vx[3]};
-        const h4x by = h4x{(_Float16)vy[0], (_Float16)vy[1], (_Float16)vy[2], (_Float16)vy[3]};
+        const h4x bx = h4x{v2[0].x, v2[1].x, v2[2].x, v2[3].x};
+        const h4x by = h4x{v2[0].y, v2[1].y, v2[2].y, v2[3].y};
 #pragma unroll
         for (int hg = 0; hg < M::HG; ++hg) {
-          const h4x pw = h4x{(_Float16)pa[hg].x, (_Float16)pa[hg].y, (_Float16)pa[hg].z, (_Float16)pa[hg].w};
-          ax[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pw, bx, ax[hg], 0, 0, 0);
-          ay[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pw, by, ay[hg], 0, 0, 0);
+          ax[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[hg], bx, ax[hg], 0, 0, 0);
+          ay[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa[hg], by, ay[hg], 0, 0, 0);
         }
       }
       asm volatile("" ::: "memory");  // the next tile's LDS writes stay after these reads
