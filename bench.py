@@ -75,7 +75,7 @@ def attn_lds_bytes(d, group, bk, bv, mode):
     tables, rotated query, flag word, then the score table and the waves' value rows,
     or the merge buffers)."""
     p = d // 2
-    nw = 8 if mode & 3 == 3 else (12 if mode & 3 and group <= 4 else 8)
+    nw = (12 if mode == 7 and d == 128 else 8) if mode & 3 == 3 else (12 if mode & 3 and group <= 4 else 8)
     hg = group // 4 if group > 4 else 1
     tab = {1: p * (1 << bk) * group * 4, 2: p * (1 << (bk - 1)) * group * 4}.get(mode & 3, 0)
     rows = nw * (hg * 4 * 64 + 64 * 16) * 4 if mode & 4 else 0

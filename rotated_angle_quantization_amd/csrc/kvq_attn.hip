@@ -244,10 +244,10 @@ __device__ __forceinline__ void load_tile_values_mx(MxRegs<D, G, BK, BV>& t, con
   for (int w = 0; w < M::VRW; ++w) t.vr[w] = w32[GE::OFF_VR / 4 + (th * M::VRW + w) * P + pr];
 }
 
-// Waves per split workgroup: 12 (three per SIMD) when the key table is used with up to
-// four heads per kv head, which leaves the kernel under 168 VGPRs; 8 in matrix-core mode
-// (two per SIMD: the query operands take 128 VGPRs) and otherwise.
-constexpr int split_waves(int ktm, int group) { return attn_waves(ktm, group); }
+// Waves per split workgroup (attn_waves): 12 (three per SIMD) with the key table at up to
+// four heads per kv head, and with both products on the matrix cores at d = 128 (both stay
+// under 168 VGPRs); 8 otherwise (KTM 3 keeps the query operands in 128 VGPRs).
+constexpr int split_waves(int ktm, int group, int d) { return attn_waves(ktm, group, d); }
 
 // One workgroup per (split, batch * kv head). KTM (key-table mode) 1: scores read a
 // per-workgroup table T[i][c][h] = q~_h,2i cos(2 pi c / n) + q~_h,2i+1 sin(2 pi c / n)
@@ -257,7 +257,7 @@ constexpr int split_waves(int ktm, int group) { return attn_waves(ktm, group); }
 // pair, and it admits n = 256 at four heads. KTM 0: scores use the cos/sin table and the
 // rotated query from scalar registers.
 template <int D, int G, int BK, int BV, int KTM>
-__global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
+__global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot,
     AppendArgs app) {
   using C = SplitCfg<D, G, BK, BV>;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(split_waves(KTM, G) * 64) void attn_decode_kernel(
   constexpr int KMODE = KTM & 3;
   constexpr bool KT = KMODE != 0, HALF = KMODE == 2, MXK = KMODE == 3, TAB = KT && !MXK;
   constexpr bool MXV = (KTM & 4) != 0, MX = MXK || MXV;
-  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KTM, G);
+  constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KTM, G, D);
   constexpr int NTAB = HALF ? NKT / 2 : NKT;  // table rows per pair
   // LDS used during the tile loop: the score table, then the waves' value rows
   constexpr int TAB_BYTES = (TAB ? P * NTAB * G * 4 : 0) + (MXV ? NW * M::WAVE_BYTES : 0);
@@ -928,7 +928,7 @@ hipError_t launch_mode(const AttnArgs& a, const AppendArgs& app, const uint8_t* 
                        hipStream_t s) {
   if constexpr (attn_lds_bytes(D, G, BK, BV, MODE) <= kLdsBytesMax) {
     hipLaunchKernelGGL((attn_decode_kernel<D, G, BK, BV, MODE>), grid,
-                       dim3(split_waves(MODE, G) * 64), 0, s, a, cache, a.qrot, app);
+                       dim3(split_waves(MODE, G, D) * 64), 0, s, a, cache, a.qrot, app);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

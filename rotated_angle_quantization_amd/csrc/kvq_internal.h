@@ -128,11 +128,15 @@ inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (
 // rotated query, a flag word, then the score table and the waves' value rows, or the
 // merge buffers after the tile loop).
 constexpr int kLdsBytesMax = 160 * 1024;
-constexpr int attn_waves(int mode, int group) {
-  return (mode & 3) == 3 ? 8 : ((mode & 3) != 0 && group <= 4 ? 12 : 8);
+// Waves per workgroup: 12 (three per SIMD) with the key table at up to four heads per
+// kv head and for both products on the matrix cores at d = 128 (within 168 VGPRs; 4%
+// faster than 8 on the 70B-shaped layers, while d = 64 would spill at 12), else 8.
+constexpr int attn_waves(int mode, int group, int d) {
+  return (mode & 3) == 3 ? (mode == 7 && d == 128 ? 12 : 8)
+                         : ((mode & 3) != 0 && group <= 4 ? 12 : 8);
 }
 constexpr long attn_lds_bytes(int d, int group, int bk, int bv, int mode) {
-  const int p = d / 2, nw = attn_waves(mode, group);
+  const int p = d / 2, nw = attn_waves(mode, group, d);
   const int hg = group > 4 ? group / 4 : 1;
   const long tab = (mode & 3) == 1 ? (long)p * (1 << bk) * group * 4
                    : (mode & 3) == 2 ? (long)p * (1 << (bk - 1)) * group * 4 : 0;
