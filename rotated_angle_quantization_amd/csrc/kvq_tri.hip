@@ -315,6 +315,7 @@ constexpr int kTriWaves = 4;
 constexpr int kTriMaxWords = 32;  // record words the attention kernel serves
 
 typedef float mf4 __attribute__((ext_vector_type(4)));
+typedef _Float16 th4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ mf4 tri_mfma(float a, float b, mf4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
@@ -346,7 +347,8 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   __shared__ float s_ln[kTriMaxLevelsNorm], s_lr[kTriMaxLevelsRest];
   __shared__ float4 s_q3[G][T + 1];        // (q~[3j], q~[3j+1], q~[3j+2], 0); row T: leftovers
   __shared__ uint32_t s_plane[kTriWaves][32 * kPlaneRow];  // up to 32 record words
-  __shared__ __align__(16) float s_w[kTriWaves][kTile][G];  // p * N per token and head
+  // p * N per head and token, fp16 (the value products' operand type), rows of 64
+  __shared__ __align__(16) _Float16 s_w[kTriWaves][G][kTile];
   __shared__ float s_ml[kTriWaves][G][2];
   __shared__ float s_acc[kTriWaves][G][D];
 
@@ -409,13 +411,14 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   const int f = lane < nf ? lane : 0;
   const int foff = field_off(g, f), fwd = field_width(g, f);
 
-  // Both products run on the matrix cores in fp32 (v_mfma_f32_4x4x1f32: lane 4b + i
-  // supplies row i of block b's A operand, lane l column l of B, and lane l accumulates
-  // D[l][i] += A[4 (l / 4) + i] * B[l]); with the query heads as the rows, A in lane l is
-  // head 4 hg + (l & 3)'s operand. Scores: lane = token, B = the token's rebuilt key
-  // element rho * w[c]; values: lane = triplet (or leftover), B = its element of the
-  // token's rebuilt value, A = the token's weight. One instruction does the 64 x 4
-  // products that take four FMAs per lane and head on the vector units.
+  // Both products run on the matrix cores (sixteen 4 x 4 blocks: lane 4b + i supplies
+  // row i of block b's A operand, lane 4b + j column j of B, and lane 4b + j accumulates
+  // D[b][i][j]); with the query heads as the rows, A in lane l is head 4 hg + (l & 3)'s
+  // operand. Scores, v_mfma_f32_4x4x1f32 in fp32: lane = token, B = the token's rebuilt
+  // key element rho * w[c]. Values, v_mfma_f32_4x4x4f16 (fp16 operands, fp32 sums,
+  // four tokens per instruction): lane = triplet (or leftover), B = its element of four
+  // tokens' rebuilt values, A = those tokens' weights. The scores stay fp32, as in the
+  // angle codec's kernel (large logits); fp16 operands add about 2^-11 per value term.
   constexpr int HG = G > 4 ? G / 4 : 1;
   const int hl = lane & 3;
   float m[G], l[G];
@@ -499,30 +502,41 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
       m[hh] = mnew;
       const float pv = m[hh] == -INFINITY ? 0.f : fast_exp2(s - m[hh]);
       l[hh] += pv;
-      s_w[wave][lane][hh] = valid ? pv * nu_v : 0.f;
+      s_w[wave][hh][lane] = (_Float16)(valid ? pv * nu_v : 0.f);
     }
     asm volatile("" ::: "memory");
     // ---- values: lane f rebuilds its triplet (or leftover) of every token; the matrix
-    // instructions run on the whole wave, lanes past the fields contributing zero
-    for (int tk = 0; tk < kTile; ++tk) {
-      const uint32_t val = staged_field(plane, foff, fwd, g.words, tk);
-      float c0 = 0.f, c1 = 0.f, c2 = 0.f;
-      if (f < T) {
-        const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
-        const float rho = s_ln[val >> (2 * g.bd)];
-        c0 = rho * w4.x;
-        c1 = rho * w4.y;
-        c2 = rho * w4.z;
-      } else {
-        c0 = s_lr[val];
+    // instructions (fp16 operands, fp32 sums, four tokens each) run on the whole wave,
+    // lanes past the fields contributing zero
+    for (int t4 = 0; t4 < kTile; t4 += 4) {
+      float c[3][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t val = staged_field(plane, foff, fwd, g.words, t4 + u);
+        float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+        if (f < T) {
+          const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+          const float rho = s_ln[val >> (2 * g.bd)];
+          c0 = rho * w4.x;
+          c1 = rho * w4.y;
+          c2 = rho * w4.z;
+        } else {
+          c0 = s_lr[val];
+        }
+        if (lane >= nf) c0 = c1 = c2 = 0.f;
+        c[0][u] = c0;
+        c[1][u] = c1;
+        c[2][u] = c2;
       }
-      if (lane >= nf) c0 = c1 = c2 = 0.f;
+      const th4 bx = th4{(_Float16)c[0][0], (_Float16)c[0][1], (_Float16)c[0][2], (_Float16)c[0][3]};
+      const th4 by = th4{(_Float16)c[1][0], (_Float16)c[1][1], (_Float16)c[1][2], (_Float16)c[1][3]};
+      const th4 bz = th4{(_Float16)c[2][0], (_Float16)c[2][1], (_Float16)c[2][2], (_Float16)c[2][3]};
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
-        const float wgt = s_w[wave][tk][min(4 * hg + hl, G - 1)];
-        ax[hg] = tri_mfma(wgt, c0, ax[hg]);
-        ay[hg] = tri_mfma(wgt, c1, ay[hg]);
-        az[hg] = tri_mfma(wgt, c2, az[hg]);
+        const th4 wgt = *reinterpret_cast<const th4*>(&s_w[wave][min(4 * hg + hl, G - 1)][t4]);
+        ax[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(wgt, bx, ax[hg], 0, 0, 0);
+        ay[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(wgt, by, ay[hg], 0, 0, 0);
+        az[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(wgt, bz, az[hg], 0, 0, 0);
       }
     }
     asm volatile("" ::: "memory");
