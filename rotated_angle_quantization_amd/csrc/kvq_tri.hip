@@ -41,6 +41,8 @@ namespace kvq {
 namespace {
 
 constexpr int kTriMaxLevelsDir = 64, kTriMaxLevelsNorm = 64, kTriMaxLevelsRest = 256;
+// longest record: d = 128 at 6/6/8 bits, 16 + 42 * 18 + 2 * 8 = 788 bits
+constexpr int kTriMaxRecordWords = 25;
 
 // Geometry of one configuration (device and host).
 struct TriGeom {
@@ -109,6 +111,7 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
   constexpr int P = D / 2;
   const TriGeom& g = a.g;
   __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
+  __shared__ uint32_t s_rec[4][kTriMaxRecordWords];  // a record being assembled, per wave
   const int bo = cb_bounds_off(g);
   for (int i = threadIdx.x; i < g.nd - 1; i += 256) s_bd[i] = a.cb[bo + i];
   for (int i = threadIdx.x; i < g.nn - 1; i += 256) s_bn[i] = a.cb[bo + g.nd - 1 + i];
@@ -187,30 +190,23 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
     } else {
       field = (uint32_t)nearest(s_br, g.nr, c[0]);
     }
-    // record words: lane w gathers the fields overlapping bits [32 w, 32 w + 32)
-    uint32_t acc = 0u;
-    if (lane == 0) acc = (uint32_t)fp16_bits(fp16_round_pos(fmin(nrm, kFp16Max)));
-    const int wlo = 32 * lane;
-    // first field ending past bit wlo
-    int ff = 0;
-    {
-      const int rel = wlo - 16;
-      if (rel > 0) {
-        ff = rel < g.T * g.B ? rel / g.B : g.T + (rel - g.T * g.B) / g.br;
-        if (ff > 0) --ff;
-      }
+    // record words assembled in the wave's LDS row: lane w < words clears word w (word 0
+    // starts as the fp16 bits of N), then each field ORs itself into the one or two words
+    // it overlaps. A wave's LDS operations complete in order, so only the compiler has
+    // to keep the clear, the ORs and the read-back in order.
+    uint32_t* rec = s_rec[threadIdx.x >> 6];
+    if (lane < g.words)
+      rec[lane] = lane == 0 ? (uint32_t)fp16_bits(fp16_round_pos(fmin(nrm, kFp16Max))) : 0u;
+    asm volatile("" ::: "memory");
+    if (lane < nf) {
+      const int off = field_off(g, f), wd = field_width(g, f);
+      const int wi = off >> 5, sh = off & 31;
+      atomicOr(&rec[wi], field << sh);
+      if (sh + wd > 32) atomicOr(&rec[wi + 1], field >> (32 - sh));
     }
-    const int span = 32 / min(g.B, g.br) + 3;
-    for (int u = 0; u < span; ++u) {
-      const int fi = min(ff + u, nf - 1);
-      const uint32_t val = (uint32_t)__shfl((int)field, fi, 64);
-      if (ff + u >= nf) continue;
-      const int off = field_off(g, fi), wd = field_width(g, fi);
-      const int sh2 = off - wlo;
-      if (sh2 >= 32 || sh2 + wd <= 0) continue;
-      acc |= sh2 >= 0 ? val << sh2 : val >> -sh2;
-    }
-    if (lane < g.words) tp[(size_t)(kv * g.words + lane) * kTile + t] = acc;
+    asm volatile("" ::: "memory");
+    if (lane < g.words) tp[(size_t)(kv * g.words + lane) * kTile + t] = rec[lane];
+    asm volatile("" ::: "memory");  // the next plane's clear stays after this read
   }
 }
 
