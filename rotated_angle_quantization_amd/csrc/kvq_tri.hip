@@ -11,10 +11,10 @@
 // declarations in kvq.h.
 //
 // Kernels (one wave per token-head for the codec; the lane maps follow the data):
-//   encode     lane i holds elements 2i, 2i+1 through the binary64 transform; lane j then
-//              gathers triplet j (or leftover coordinate j - T) with lane permutes, takes
-//              its decisions in binary64 against the boundaries in LDS, and lane w packs
-//              record word w from the fields of the lanes that overlap it.
+//   encode     lane i holds elements 2i, 2i+1 through the binary64 transform; the unit
+//              vector is staged in LDS and lane j reads triplet j (or leftover coordinate
+//              j - T), takes its decisions in binary64 against the boundaries in LDS and
+//              ORs its field into the record's words in LDS; lane w stores word w.
 //   decode     lane j rebuilds its triplet (or leftover) in fp32 from the levels, the
 //              elements are permuted back to two per lane for the inverse transform.
 //   attention  split kernel (grid: splits x batch * kv heads, four waves, a wave per
@@ -99,8 +99,6 @@ __device__ __forceinline__ int nearest(const double* bounds, int n_levels, doubl
 __device__ __forceinline__ double sgn64(double x) { return x < 0.0 ? -1.0 : 1.0; }
 __device__ __forceinline__ float sgn32(float x) { return x < 0.f ? -1.f : 1.f; }
 
-template <class Tv>
-__device__ __forceinline__ Tv shfl_t(Tv v, int src) { return __shfl(v, src, 64); }
 
 // ------------------------------------------------------------------------------ encode
 
@@ -112,6 +110,7 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
   const TriGeom& g = a.g;
   __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
   __shared__ uint32_t s_rec[4][kTriMaxRecordWords];  // a record being assembled, per wave
+  __shared__ double s_u[4][D];                         // a unit vector being split, per wave
   const int bo = cb_bounds_off(g);
   for (int i = threadIdx.x; i < g.nd - 1; i += 256) s_bd[i] = a.cb[bo + i];
   for (int i = threadIdx.x; i < g.nn - 1; i += 256) s_bn[i] = a.cb[bo + g.nd - 1 + i];
@@ -168,13 +167,15 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
     // lane f < T gathers triplet f, lane T + r the leftover coordinate 3T + r
     const int f = lane < nf ? lane : 0;
     const int base = f < g.T ? 3 * f : 3 * g.T + (f - g.T);
+    // the unit vector staged in the wave's LDS row (lane i writes elements 2i, 2i + 1),
+    // then each lane reads the three elements of its triplet
+    double* su = s_u[threadIdx.x >> 6];
+    if (lane < P) reinterpret_cast<double2*>(su)[i] = make_double2(u0, u1);
+    asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
     double c[3];
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const int e = min(base + m, D - 1);
-      const double lo_v = shfl_t(u0, e >> 1), hi_v = shfl_t(u1, e >> 1);
-      c[m] = (e & 1) ? hi_v : lo_v;
-    }
+    for (int m = 0; m < 3; ++m) c[m] = su[min(base + m, D - 1)];
+    asm volatile("" ::: "memory");  // the next plane's writes stay after these reads
     uint32_t field = 0;
     if (f < g.T) {
       const double rho = sqrt(fma(c[2], c[2], fma(c[1], c[1], c[0] * c[0])));
