@@ -360,6 +360,49 @@ def multi_query(kvq, cfg, descs, caches, dev, nqs=(4, 8), reps=5):
     return res
 
 
+def fixed_and_streaming(kvq, cfg, descs, caches, qs, dev, reps=16):
+    """Per-launch time of decode attention on one 7/6-bit layer at a quarter and at the
+    full sequence length (each launch over the same cache, replayed from a HIP graph of
+    `reps` calls): the difference gives the streaming rate once a launch is under way,
+    and the intercept the fixed cost of a launch (set-up, the split merge, launch and
+    ramp), which no amount of streaming hides."""
+    import torch
+
+    layer = min(cfg.boosted_layers, cfg.layers - 1)
+    desc, cache, q = descs[layer], caches[layer], qs[layer]
+    T = cfg.seq
+    out = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float16, device=dev)
+    times = {}
+    for L in (T // 4, T):
+        ws = kvq.alloc_workspace(desc, cfg.hq, L, dev)
+        kvq.attn_decode(desc, cache, q, L, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(reps):
+                    kvq.attn_decode(desc, cache, q, L, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times[L] = e0.elapsed_time(e1) * 1e3 / reps
+    per_tok = record_bytes(cfg.d, *cfg.bins(layer), cfg.batch * cfg.hkv)  # bytes per token
+    lo, hi = T // 4, T
+    slope_us = (times[hi] - times[lo]) / (hi - lo)
+    return {
+        "layer": layer, "seq_lens": [lo, hi],
+        "us_per_launch": [round(times[lo], 2), round(times[hi], 2)],
+        "streaming_GBps": round(per_tok / (slope_us * 1e-6) / 1e9, 1),
+        "fixed_us_per_launch": round(times[hi] - slope_us * hi, 2),
+    }
+
+
 def stream_probe(kvq, caches, dev, reps=3):
     """Read-only streaming probe (kvq_probe_read) over the same cache buffers the
     attention sweep reads, one launch per layer, HIP events around the sweep: the
@@ -557,6 +600,7 @@ def main():
     loop = decode_loop(kvq, cfg, descs, caches, ws, dev)
     mq = multi_query(kvq, cfg, descs, caches, dev)
     probe = stream_probe(kvq, caches, dev)
+    fixed = fixed_and_streaming(kvq, cfg, descs, caches, qs, dev)
     tri = None if args.no_triplet else triplet_sub(kvq, cfg, ks, vs, qs, dev)
 
     enc_ms = sum(e[0].elapsed_time(e[1]) for e, _ in recs) / args.steps
@@ -628,6 +672,7 @@ def main():
             "bytes_per_launch": launch_bytes_avg,
             "stream_probe": probe,
             "achieved_over_probe": round(achieved / probe["GBps"], 4),
+            "launch_breakdown": fixed,
         },
     }
     if not args.no_cpu_baseline:
