@@ -87,15 +87,15 @@ def attn_kernel_name(d, group, n_k, n_v):
     """Name of the attention-kernel instantiation the library launches for this shape:
     the score table (half for power-of-two n_k, else full) with the value sum on the
     matrix cores (mode 6 / 5) for up to four query heads per kv head when both fit in
-    160 KiB of LDS, else the score table with the vector value sum (mode 2 / 1) when it
-    fits, else matrix-core products for both (mode 7)."""
+    160 KiB of LDS, else for key codes under 8 bits the score table with the vector value
+    sum (mode 2 / 1) when it fits, else matrix-core products for both (mode 7)."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
     mode = 7
     if group <= 4:
         tab = 2 if n_k == 1 << bk else 1
         if attn_lds_bytes(d, group, bk, bv, tab | 4) <= 160 * 1024:
             mode = tab | 4
-        elif attn_lds_bytes(d, group, bk, bv, tab) <= 160 * 1024:
+        elif bk < 8 and attn_lds_bytes(d, group, bk, bv, tab) <= 160 * 1024:
             mode = tab
     return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {mode}>"
 

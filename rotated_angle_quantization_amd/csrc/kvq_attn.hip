@@ -254,8 +254,8 @@ constexpr int split_waves(int ktm, int group, int d) { return attn_waves(ktm, gr
 // from LDS, one FMA per (pair, head). KTM 2 (n a power of two): only rows c < n/2 are
 // stored and T[i][c + n/2] = -T[i][c] (the angle plus pi), the top code bit flipping the
 // sign of the radius; half the LDS and fewer bank conflicts for one extra operation per
-// pair, and it admits n = 256 at four heads. KTM 0: scores use the cos/sin table and the
-// rotated query from scalar registers.
+// pair, and it leaves room for the matrix-core value rows beside 8-bit codes at up to two
+// heads. KTM 0: scores use the cos/sin table and the rotated query from scalar registers.
 template <int D, int G, int BK, int BV, int KTM>
 __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot,

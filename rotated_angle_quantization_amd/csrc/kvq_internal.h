@@ -147,15 +147,19 @@ constexpr long attn_lds_bytes(int d, int group, int bk, int bv, int mode) {
 }
 // The variant run for a shape (n_k a power of two admits the half table), as measured
 // fastest on MI355X: for up to four heads per kv head, the score table with the value
-// sum on the matrix cores when both fit in LDS, else the score table with the vector
-// value sum (8-bit key codes at four heads: the 128 KiB half table leaves no room for
-// the value rows); for eight heads, and when no table fits, the matrix cores for both.
+// sum on the matrix cores when both fit in LDS. Where they do not (four heads with
+// 8-bit key codes, whose 128 KiB half table leaves no room for the value rows, or 7-bit
+// codes short of a power of two, whose full table is as large): 8-bit codes take the
+// matrix cores for both products, which beats the score table with the vector value sum
+// by 3-12% (61 against 63-69 us per Mistral-7B-shaped 8/8-bit layer); narrower codes keep
+// that table (their matrix-core key loop spills registers at four heads). Eight heads,
+// and shapes where no table fits: the matrix cores for both.
 constexpr int attn_mode(int d, int group, int n_k, int bk, int bv) {
   const bool pow2 = n_k == (1 << bk);
   if (group <= 4) {
     const int tabmode = pow2 ? 2 : 1;
     if (attn_lds_bytes(d, group, bk, bv, tabmode | 4) <= kLdsBytesMax) return tabmode | 4;
-    if (attn_lds_bytes(d, group, bk, bv, tabmode) <= kLdsBytesMax) return tabmode;
+    if (bk < 8 && attn_lds_bytes(d, group, bk, bv, tabmode) <= kLdsBytesMax) return tabmode;
   }
   return 3 | 4;
 }

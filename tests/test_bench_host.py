@@ -35,7 +35,7 @@ def test_cpu_baseline_is_the_oracle_on_a_bounded_sample():
 
 @pytest.mark.parametrize("d,g,nk,nv,name", [
     (128, 4, 128, 64, "attn_decode_kernel<128, 4, 7, 6, 6>"),     # half table + MFMA values
-    (128, 4, 256, 256, "attn_decode_kernel<128, 4, 8, 8, 2>"),    # half table, vector values
+    (128, 4, 256, 256, "attn_decode_kernel<128, 4, 8, 8, 7>"),    # 8-bit keys: MFMA both
     (128, 4, 100, 40, "attn_decode_kernel<128, 4, 7, 6, 1>"),     # full table, vector values
     (128, 4, 200, 40, "attn_decode_kernel<128, 4, 8, 6, 7>"),     # no table fits: MFMA
     (128, 2, 100, 40, "attn_decode_kernel<128, 2, 7, 6, 5>"),     # full table + MFMA values
