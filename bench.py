@@ -72,30 +72,40 @@ def copy_calibration(mib):
 
 def attn_lds_bytes(d, group, bk, bv, mode):
     """LDS bytes of one decode-attention variant (the library's own layout: cos/sin
-    tables, rotated query, flag word, then the score table and the waves' value rows,
-    or the merge buffers)."""
+    tables, rotated query, flag word, then the score table and the waves' fp16 value
+    rows, or the merge buffers; with a score table and matrix-core values the query
+    lives in that union instead)."""
     p = d // 2
     nw = (12 if mode == 7 and d == 128 else 8) if mode & 3 == 3 else (12 if mode & 3 and group <= 4 else 8)
     hg = group // 4 if group > 4 else 1
     tab = {1: p * (1 << bk) * group * 4, 2: p * (1 << (bk - 1)) * group * 4}.get(mode & 3, 0)
-    rows = nw * (hg * 4 * 64 + 64 * 16) * 4 if mode & 4 else 0
-    merge = nw * group * (d + 2) * 4
-    return (1 << bk) * 8 + (1 << bv) * 8 + group * d * 4 + 16 + max(tab + rows, merge)
+    rows = nw * (hg * 4 * 64 + 64 * 16) * 2 if mode & 4 else 0
+    qb = group * d * 4
+    qu = tab > 0 and bool(mode & 4)
+    merge = nw * group * (d + 2) * 4 + (qb if qu else 0)
+    return (1 << bk) * 8 + (1 << bv) * 8 + (0 if qu else qb) + 16 + max(tab + rows, merge)
 
 
 def attn_kernel_name(d, group, n_k, n_v):
     """Name of the attention-kernel instantiation the library launches for this shape:
-    the score table (half for power-of-two n_k, else full) with the value sum on the
-    matrix cores (mode 6 / 5) for up to four query heads per kv head when both fit in
-    160 KiB of LDS, else for key codes under 8 bits the score table with the vector value
-    sum (mode 2 / 1) when it fits, else matrix-core products for both (mode 7)."""
+    for up to four query heads per kv head the score table with the value sum on the
+    matrix cores when both fit in 160 KiB of LDS (the half table, mode 6, for
+    power-of-two n_k at three or four heads, else the full table, mode 5), else for key
+    codes under 8 bits the score table with the vector value sum (mode 1 / 2) when it
+    fits; otherwise matrix-core products for both (mode 7)."""
     bk, bv = (n_k - 1).bit_length(), (n_v - 1).bit_length()
+    pow2 = n_k == 1 << bk
+    cap = 160 * 1024
     mode = 7
     if group <= 4:
-        tab = 2 if n_k == 1 << bk else 1
-        if attn_lds_bytes(d, group, bk, bv, tab | 4) <= 160 * 1024:
-            mode = tab | 4
-        elif bk < 8 and attn_lds_bytes(d, group, bk, bv, tab) <= 160 * 1024:
+        tab = 2 if pow2 else 1
+        full = attn_lds_bytes(d, group, bk, bv, 5) <= cap
+        half = pow2 and attn_lds_bytes(d, group, bk, bv, 6) <= cap
+        if full and (group <= 2 or not half):
+            mode = 5
+        elif half:
+            mode = 6
+        elif bk < 8 and attn_lds_bytes(d, group, bk, bv, tab) <= cap:
             mode = tab
     return f"attn_decode_kernel<{d}, {group}, {bk}, {bv}, {mode}>"
 

@@ -214,9 +214,9 @@ struct MxCfg {
   // query operands in registers (128 VGPRs at d = 128), unless the extra words of
   // 8-bit key codes would then spill: then they are read from LDS per pair
   static constexpr bool QREG = HG * D <= 128 && BK < 8;
-  static constexpr int PS_FLOATS = HG * 4 * kTile;     // per wave: weights [HG][4][64]
-  static constexpr int LEV_FLOATS = kTile * 16;        // per wave: levels [64][16]
-  static constexpr int WAVE_BYTES = (PS_FLOATS + LEV_FLOATS) * 4;
+  static constexpr int PS_HALVES = HG * 4 * kTile;     // per wave: fp16 weights [HG][4][64]
+  static constexpr int LEV_HALVES = kTile * 16;        // per wave: fp16 levels [64][16]
+  static constexpr int WAVE_BYTES = (PS_HALVES + LEV_HALVES) * 2;
 };
 
 // Registers of one tile in matrix-core mode: key planes with lane = token, value planes
@@ -272,22 +272,35 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
   constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KTM, G, D);
   constexpr int NTAB = HALF ? NKT / 2 : NKT;  // table rows per pair
   // LDS used during the tile loop: the score table, then the waves' value rows
-  constexpr int TAB_BYTES = (TAB ? P * NTAB * G * 4 : 0) + (MXV ? NW * M::WAVE_BYTES : 0);
+  constexpr int TABLE_BYTES = TAB ? P * NTAB * G * 4 : 0;
+  constexpr int TAB_BYTES = TABLE_BYTES + (MXV ? NW * M::WAVE_BYTES : 0);
   constexpr int MERGE_BYTES = NW * G * (D + 2) * 4;
-  constexpr int UNION_BYTES = TAB_BYTES > MERGE_BYTES ? TAB_BYTES : MERGE_BYTES;
+  // With a score table and matrix-core values the tile loop never reads the rotated
+  // query, so it lives in the union as well: in the space of the value rows while the
+  // table is built (the rows are first written after the barrier that ends the build),
+  // and after the merge buffers once the loop is done (normalised output). That leaves
+  // room for the full table beside the value rows at four heads and 7-bit codes.
+  constexpr bool QU = TAB && MXV;
+  constexpr int QB = G * D * 4;
+  static_assert(!QU || NW * M::WAVE_BYTES >= QB, "query does not fit in the value rows");
+  constexpr int UNION_BYTES =
+      TAB_BYTES > MERGE_BYTES + (QU ? QB : 0) ? TAB_BYTES : MERGE_BYTES + (QU ? QB : 0);
   // small cos/sin tables at the bottom of LDS so their lookups fold the base into the
   // instruction's immediate offset; then the rotated query (later the normalised
-  // output), a flag, and the key table (or the merge buffers)
+  // output) unless it lives in the union, a flag, and the key table (or the merge
+  // buffers)
   constexpr int LUTK_OFF = 0, LUTV_OFF = NKT * 8, Q_OFF = LUTV_OFF + (1 << BV) * 8;
-  constexpr int FLAG_OFF = Q_OFF + G * D * 4, UNION_OFF = FLAG_OFF + 16;
+  constexpr int FLAG_OFF = Q_OFF + (QU ? 0 : QB), UNION_OFF = FLAG_OFF + 16;
   __shared__ __align__(16) char smem[UNION_OFF + UNION_BYTES];
   static_assert(UNION_OFF + UNION_BYTES == attn_lds_bytes(D, G, BK, BV, KTM),
                 "LDS layout and its host-side model disagree");
   float2* lut_k = reinterpret_cast<float2*>(smem + LUTK_OFF);
   float2* lut_v = reinterpret_cast<float2*>(smem + LUTV_OFF);
-  float* s_q = reinterpret_cast<float*>(smem + Q_OFF);  // [G][D]
   int* s_flag = reinterpret_cast<int*>(smem + FLAG_OFF);
   char* s_union = smem + UNION_OFF;
+  // rotated query [G][D] (set-up, and the matrix-core scores), normalised output [G][D]
+  float* s_q = reinterpret_cast<float*>(QU ? s_union + TABLE_BYTES : smem + Q_OFF);
+  float* s_out = reinterpret_cast<float*>(QU ? s_union + MERGE_BYTES : smem + Q_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar tile addresses
@@ -478,13 +491,10 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
   f32x4 ax[M::HG], ay[M::HG];
   float qr[MXK && M::QREG ? M::HG : 1][MXK && M::QREG ? D : 1];
   const float* q_row[M::HG];
-  // the waves' value rows follow the score table, if any
-  float* w_ps = reinterpret_cast<float*>(s_union) + (TAB ? P * NTAB * G : 0) +
-                wave * (M::WAVE_BYTES / 4);
-  float* w_lev = w_ps + M::PS_FLOATS;
-  // the weights are kept as fp16, the matrix instructions' operand type (rows of 64
-  // halves in the first half of the space reserved for them)
-  _Float16* w_ph = reinterpret_cast<_Float16*>(w_ps);
+  // the waves' value rows follow the score table, if any: softmax weights and radius
+  // levels as fp16, the matrix instructions' operand type
+  _Float16* w_ph = reinterpret_cast<_Float16*>(s_union + TABLE_BYTES + wave * M::WAVE_BYTES);
+  _Float16* w_lev = w_ph + M::PS_HALVES;
   if constexpr (MX) {
 #pragma unroll
     for (int hg = 0; hg < M::HG; ++hg) {
@@ -640,7 +650,7 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
     }
     if constexpr (MXV) {
       // fp16 levels (in [2^-14, 65504] or 0), the operand type of the value products
-      h4x* dst = reinterpret_cast<h4x*>(reinterpret_cast<_Float16*>(w_lev) + lane * 16);
+      h4x* dst = reinterpret_cast<h4x*>(w_lev + lane * 16);
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
         dst[r / 4] = h4x{(_Float16)(r0 * fast_exp2((float)r * beta)),
@@ -697,7 +707,7 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
           const int t = 4 * t4 + u;
           const h2x cs = reinterpret_cast<const h2x*>(lut_v)[field<BV>(cur.va, t)];
           const uint32_t rho = (cur.vr[t >> 3] >> (4 * (t & 7))) & 0xFu;
-          const _Float16 lvl = reinterpret_cast<const _Float16*>(w_lev)[(th * 32 + t) * 16 + rho];
+          const _Float16 lvl = w_lev[(th * 32 + t) * 16 + rho];
           v2[u] = h2x{lvl, lvl} * cs;
         }
         const h4x bx = h4x{v2[0].x, v2[1].x, v2[2].x, v2[3].x};
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
       aa += s_acc[(w * G + g) * D + e] * f;
     }
     if (single) {
-      s_q[idx] = ll > 0.f ? aa / ll : 0.f;  // no token at all: zero output
+      s_out[idx] = ll > 0.f ? aa / ll : 0.f;  // no token at all: zero output
     } else {
       // device-coherent stores (they bypass the non-coherent caches, so no cache
       // write-back is needed before another workgroup reads them)
@@ -846,7 +856,7 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
   if (single) {
     __syncthreads();
     if (wave < G && lane < P) {
-      const float2 v = reinterpret_cast<const float2*>(s_q)[wave * P + lane];
+      const float2 v = reinterpret_cast<const float2*>(s_out)[wave * P + lane];
       store_output<D>(a, ((size_t)bk * G + wave) * D, lane, v.x, v.y);
     }
     return;
@@ -913,11 +923,11 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
         }
       }
     }
-    s_q[idx] = ll > 0.f ? aa / ll : 0.f;
+    s_out[idx] = ll > 0.f ? aa / ll : 0.f;
   }
   __syncthreads();
   if (wave < G && lane < P) {
-    const float2 v = reinterpret_cast<const float2*>(s_q)[wave * P + lane];
+    const float2 v = reinterpret_cast<const float2*>(s_out)[wave * P + lane];
     store_output<D>(a, ((size_t)bk * G + wave) * D, lane, v.x, v.y);
   }
   if (tid == 0) __hip_atomic_store(a.tickets + bk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -125,8 +125,9 @@ inline long key_table_bytes(int d, int group, int bk) { return (long)(d / 2) * (
 // (0: rotated query through scalar loads, 1: full LDS score table, 2: half score table
 // for power-of-two n, 3: matrix-core products), bit 2 puts the value sum on the matrix
 // cores. The LDS a variant needs mirrors the kernel's own layout (cos/sin tables, the
-// rotated query, a flag word, then the score table and the waves' value rows, or the
-// merge buffers after the tile loop).
+// rotated query, a flag word, then the score table and the waves' fp16 value rows, or
+// the merge buffers after the tile loop; with a score table and matrix-core values the
+// query moves into that union, beside the merge buffers).
 constexpr int kLdsBytesMax = 160 * 1024;
 // Waves per workgroup: 12 (three per SIMD) with the key table at up to four heads per
 // kv head and for both products on the matrix cores at d = 128 (within 168 VGPRs; 4%
@@ -140,25 +141,33 @@ constexpr long attn_lds_bytes(int d, int group, int bk, int bv, int mode) {
   const int hg = group > 4 ? group / 4 : 1;
   const long tab = (mode & 3) == 1 ? (long)p * (1 << bk) * group * 4
                    : (mode & 3) == 2 ? (long)p * (1 << (bk - 1)) * group * 4 : 0;
-  const long rows = (mode & 4) ? (long)nw * (hg * 4 * 64 + 64 * 16) * 4 : 0;
-  const long merge = (long)nw * group * (d + 2) * 4;
+  const long rows = (mode & 4) ? (long)nw * (hg * 4 * 64 + 64 * 16) * 2 : 0;
+  const long qb = (long)group * d * 4;
+  const bool qu = tab > 0 && (mode & 4);  // the query lives in the union
+  const long merge = (long)nw * group * (d + 2) * 4 + (qu ? qb : 0);
   const long loop = tab + rows;
-  return (1L << bk) * 8 + (1L << bv) * 8 + (long)group * d * 4 + 16 + (loop > merge ? loop : merge);
+  return (1L << bk) * 8 + (1L << bv) * 8 + (qu ? 0 : qb) + 16 + (loop > merge ? loop : merge);
 }
-// The variant run for a shape (n_k a power of two admits the half table), as measured
-// fastest on MI355X: for up to four heads per kv head, the score table with the value
-// sum on the matrix cores when both fit in LDS. Where they do not (four heads with
-// 8-bit key codes, whose 128 KiB half table leaves no room for the value rows, or 7-bit
-// codes short of a power of two, whose full table is as large): 8-bit codes take the
-// matrix cores for both products, which beats the score table with the vector value sum
-// by 3-12% (61 against 63-69 us per Mistral-7B-shaped 8/8-bit layer); narrower codes keep
-// that table (their matrix-core key loop spills registers at four heads). Eight heads,
-// and shapes where no table fits: the matrix cores for both.
+// The variant run for a shape, as measured fastest on MI355X: for up to four heads per
+// kv head, the score table with the value sum on the matrix cores when both fit in LDS.
+// Power-of-two n admits the half table (mode 6: one more sign operation per pair, half
+// the LDS): it is the faster one at four heads (51.4 against 52.5 us per
+// Mistral-7B-shaped 7/6-bit layer), the full table (mode 5) at one and two (41.7
+// against 42.5-42.9 us at two), and the full table is the only one for other n. Where
+// neither fits (four heads with 8-bit key codes, whose 128 KiB half table leaves no room
+// for the value rows): 8-bit codes take the matrix cores for both products, which beats
+// the score table with the vector value sum by 3-12% (61 against 63-69 us per
+// Mistral-7B-shaped 8/8-bit layer); narrower codes keep that table (their matrix-core
+// key loop spills registers at four heads). Eight heads, and shapes where no table
+// fits: the matrix cores for both.
 constexpr int attn_mode(int d, int group, int n_k, int bk, int bv) {
   const bool pow2 = n_k == (1 << bk);
   if (group <= 4) {
+    const bool full = attn_lds_bytes(d, group, bk, bv, 1 | 4) <= kLdsBytesMax;
+    const bool half = pow2 && attn_lds_bytes(d, group, bk, bv, 2 | 4) <= kLdsBytesMax;
+    if (full && (group <= 2 || !half)) return 1 | 4;
+    if (half) return 2 | 4;
     const int tabmode = pow2 ? 2 : 1;
-    if (attn_lds_bytes(d, group, bk, bv, tabmode | 4) <= kLdsBytesMax) return tabmode | 4;
     if (bk < 8 && attn_lds_bytes(d, group, bk, bv, tabmode) <= kLdsBytesMax) return tabmode;
   }
   return 3 | 4;

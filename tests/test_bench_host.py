@@ -36,12 +36,16 @@ def test_cpu_baseline_is_the_oracle_on_a_bounded_sample():
 @pytest.mark.parametrize("d,g,nk,nv,name", [
     (128, 4, 128, 64, "attn_decode_kernel<128, 4, 7, 6, 6>"),     # half table + MFMA values
     (128, 4, 256, 256, "attn_decode_kernel<128, 4, 8, 8, 7>"),    # 8-bit keys: MFMA both
-    (128, 4, 100, 40, "attn_decode_kernel<128, 4, 7, 6, 1>"),     # full table, vector values
+    (128, 4, 100, 40, "attn_decode_kernel<128, 4, 7, 6, 5>"),     # full table + MFMA values
+    (128, 4, 128, 256, "attn_decode_kernel<128, 4, 7, 8, 6>"),    # half table + MFMA values
+    (128, 4, 100, 256, "attn_decode_kernel<128, 4, 7, 8, 1>"),    # full table, vector values
     (128, 4, 200, 40, "attn_decode_kernel<128, 4, 8, 6, 7>"),     # no table fits: MFMA
     (128, 2, 100, 40, "attn_decode_kernel<128, 2, 7, 6, 5>"),     # full table + MFMA values
+    (128, 2, 256, 256, "attn_decode_kernel<128, 2, 8, 8, 6>"),    # half table + MFMA values
     (128, 8, 200, 256, "attn_decode_kernel<128, 8, 8, 8, 7>"),
     (64, 8, 128, 64, "attn_decode_kernel<64, 8, 7, 6, 7>"),
     (64, 4, 128, 64, "attn_decode_kernel<64, 4, 7, 6, 6>"),
+    (128, 2, 128, 64, "attn_decode_kernel<128, 2, 7, 6, 5>"),     # two heads: full table
 ])
 def test_kernel_name_follows_the_variant_rule(d, g, nk, nv, name):
     assert bench.attn_kernel_name(d, g, nk, nv) == name
