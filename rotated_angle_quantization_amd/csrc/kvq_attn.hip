@@ -256,6 +256,10 @@ constexpr int split_waves(int ktm, int group, int d) { return attn_waves(ktm, gr
 // sign of the radius; half the LDS and fewer bank conflicts for one extra operation per
 // pair, and it leaves room for the matrix-core value rows beside 8-bit codes at up to two
 // heads. KTM 0: scores use the cos/sin table and the rotated query from scalar registers.
+// Lazy softmax maximum: a tile's scores may exceed the running maximum by up to this
+// (base-2 units) before it is refreshed, so the weights stay within 2^8.
+constexpr float kLazyLog2 = 8.f;
+
 template <int D, int G, int BK, int BV, int KTM>
 __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kernel(
     AttnArgs a, const uint8_t* __restrict__ cache, const float* __restrict__ qrot,
@@ -269,6 +273,10 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
   constexpr int KMODE = KTM & 3;
   constexpr bool KT = KMODE != 0, HALF = KMODE == 2, MXK = KMODE == 3, TAB = KT && !MXK;
   constexpr bool MXV = (KTM & 4) != 0, MX = MXK || MXV;
+  // lazy softmax maximum where the wave maxima of eight or more heads per tile are a
+  // visible cost (4-5% of the 70B-shaped layers' time); the table kernels keep the
+  // branch-free form, whose score pipeline the compiler otherwise breaks up
+  constexpr bool LAZY = MXK && G > 4;
   constexpr int P = C::P, NKT = C::NKT, PPL = C::PPL, NW = split_waves(KTM, G, D);
   constexpr int NTAB = HALF ? NKT / 2 : NKT;  // table rows per pair
   // LDS used during the tile loop: the score table, then the waves' value rows
@@ -661,11 +669,10 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
 
     // ---- online softmax per head (lane = token), base 2; slots past the end get 0
     float pr[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float s = valid ? sc[g] * kscale : -INFINITY;
-      const float mnew = fmaxf(m[g], wave_max(s));
-      // no token seen yet (only tiles of absent pages): nothing to rescale
+    // new running maximum of head g from this tile's largest score; the sums so far are
+    // rescaled to it (no token seen yet, only tiles of absent pages: nothing to rescale)
+    auto raise_max = [&](int g, float tile_max) {
+      const float mnew = fmaxf(m[g], tile_max);
       const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(m[g] - mnew);
       l[g] *= alpha;
       if constexpr (MXV) {
@@ -679,7 +686,36 @@ __global__ __launch_bounds__(split_waves(KTM, G, D) * 64) void attn_decode_kerne
         }
       }
       m[g] = mnew;
-      const float pv = m[g] == -INFINITY ? 0.f : fast_exp2(s - m[g]);
+    };
+    if constexpr (LAZY) {
+      // Lazy maximum: the tile's weights are taken relative to the m of the tiles
+      // before unless a score exceeds it by more than kLazyLog2 (a wave-wide vote); only
+      // then are the wave maxima formed and the sums rescaled. Weights stay below
+      // 2^kLazyLog2, inside the fp16 operand range, and the result, a ratio of sums
+      // taken relative to the same m, does not depend on m.
+      float s[G];
+      bool up = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s[g] = valid ? sc[g] * kscale : -INFINITY;
+        up = up || s[g] > m[g] + kLazyLog2;
+      }
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) raise_max(g, wave_max(s[g]));
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[g] = s[g];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sc[g] = valid ? sc[g] * kscale : -INFINITY;
+        raise_max(g, wave_max(sc[g]));
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pv = m[g] == -INFINITY ? 0.f : fast_exp2(sc[g] - m[g]);
       l[g] += pv;
       pr[g] = pv * r0;
       if constexpr (MXV) w_ph[(g >> 2) * 4 * kTile + (g & 3) * kTile + lane] = (_Float16)pv;
