@@ -49,13 +49,26 @@ constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirr
 
 // Wave-wide max / sum: four DPP steps make each row of 16 uniform, then the four row
 // results are combined from scalar registers (readlane), so the result is uniform.
+// The maximum runs on integers ordered like the floats (a non-negative float's bits
+// compare like a signed integer; a negative one's magnitude bits are flipped, which
+// reverses their order and keeps them below zero): the DPP moves then fuse into
+// v_max_i32, the row results combine on the scalar unit, and none of the NaN
+// canonicalisation that a float maximum of lane-moved values costs is needed (scores
+// are never NaN).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, 0);
+}
+__device__ __forceinline__ int float_order(int b) { return b ^ ((b >> 31) & 0x7fffffff); }
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kDppXor1>(x));
-  x = fmaxf(x, dpp<kDppXor2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppMirror>(x));
-  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)),
-               fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+  int i = float_order(__float_as_int(x));
+  i = max(i, dpp_i<kDppXor1>(i));
+  i = max(i, dpp_i<kDppXor2>(i));
+  i = max(i, dpp_i<kDppHalfMirror>(i));
+  i = max(i, dpp_i<kDppMirror>(i));
+  const int r = max(max(__builtin_amdgcn_readlane(i, 0), __builtin_amdgcn_readlane(i, 16)),
+                    max(__builtin_amdgcn_readlane(i, 32), __builtin_amdgcn_readlane(i, 48)));
+  return __int_as_float(float_order(r));  // the map is its own inverse
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
