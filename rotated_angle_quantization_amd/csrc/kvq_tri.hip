@@ -584,23 +584,49 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
 }
 
 // One wave per output row (batch, query head): log-sum-exp over the splits, then the
-// inverse transform of acc / l (lane p holds elements 2p, 2p+1).
+// inverse transform of acc / l (lane p holds elements 2p, 2p+1). The partials come from
+// other compute units through memory, so their loads are issued together rather than
+// one split after another: lane s takes the (max, sum) of splits s, s + 64, ..., the
+// per-split factors go through LDS, and the accumulator loads of kMergeUnroll splits are
+// in flight at once (a dependent load per split had made this kernel 12.7 us at 32
+// splits).
+constexpr int kTriMaxSplits = 1024;  // tri_split_plan's ceiling
+constexpr int kMergeUnroll = 16;
 template <int D>
 __global__ __launch_bounds__(64) void tri_attn_merge_kernel(TriAttnArgs a) {
   constexpr int P = D / 2;
+  __shared__ float s_f[kTriMaxSplits];  // exp2(m_s - max) of split s
   const int lane = threadIdx.x;
   const size_t row = blockIdx.x;
-  const float* ml = a.part_ml + 2 * row * a.nsplit;
-  const float* pa = a.part_acc + row * a.nsplit * D;
+  const int ns = a.nsplit;
+  const float* ml = a.part_ml + 2 * row * ns;
+  const float* pa = a.part_acc + row * ns * D;
   const int p = lane & (P - 1);
   float mm = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, ml[2 * s]);
-  float ll = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
+  for (int s = lane; s < ns; s += 64) mm = fmaxf(mm, ml[2 * s]);
+  mm = wave_max(mm);
+  float ll = 0.f;
+  for (int s = lane; s < ns; s += 64) {
     const float fct = mm == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - mm);
+    s_f[s] = fct;
     ll += ml[2 * s + 1] * fct;
-    a0 += pa[(size_t)s * D + 2 * p] * fct;
-    a1 += pa[(size_t)s * D + 2 * p + 1] * fct;
+  }
+  ll = wave_sum(ll);
+  __syncthreads();
+  float a0 = 0.f, a1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMergeUnroll) {
+    float2 v[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u)
+      v[u] = *reinterpret_cast<const float2*>(pa + (size_t)min(s0 + u, ns - 1) * D + 2 * p);
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (s0 + u < ns) {
+        const float fct = s_f[s0 + u];
+        a0 += v[u].x * fct;
+        a1 += v[u].y * fct;
+      }
+    }
   }
   const float inv = ll > 0.f ? 1.f / ll : 0.f;
   a0 *= inv;
@@ -831,7 +857,7 @@ TriArgs tri_args(const kvq_tri_desc* d, const double* cb, uint32_t t0, uint32_t 
 
 void tri_split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tps) {
   const int ntiles = (int)((seq_len + kTile - 1) / kTile);
-  int s = (int)((1024 + units - 1) / units);
+  int s = (int)((kTriMaxSplits + units - 1) / units);  // never more than kTriMaxSplits
   int max_s = (ntiles + 3) / 4;
   if (max_s < 1) max_s = 1;
   if (s > max_s) s = max_s;
@@ -862,6 +888,7 @@ hipError_t tri_attn_launch(const TriAttnArgs& a, const uint8_t* cache, hipStream
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.nsplit > kTriMaxSplits) return hipErrorInvalidValue;  // the merge's LDS table
   hipLaunchKernelGGL((tri_attn_merge_kernel<D>), dim3((unsigned)(a.batch * a.hq)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
