@@ -43,12 +43,15 @@ __device__ __forceinline__ h4 h4_from(const uint32_t* p) {
   return __builtin_bit_cast(h4, u);
 }
 
-// Maximum and sum over the 16 lanes of each DPP row (lanes 16k .. 16k + 15).
+// Maximum and sum over the 16 lanes of each DPP row (lanes 16k .. 16k + 15); the
+// maximum on float-ordered integers, as wave_max, so the DPP moves fuse into v_max_i32.
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<kDppXor1>(x));
-  x = fmaxf(x, dpp<kDppXor2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  return fmaxf(x, dpp<kDppMirror>(x));
+  int i = float_order(__float_as_int(x));
+  i = max(i, dpp_i<kDppXor1>(i));
+  i = max(i, dpp_i<kDppXor2>(i));
+  i = max(i, dpp_i<kDppHalfMirror>(i));
+  i = max(i, dpp_i<kDppMirror>(i));
+  return __int_as_float(float_order(i));
 }
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp<kDppXor1>(x);
