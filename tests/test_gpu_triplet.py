@@ -296,3 +296,37 @@ def test_mistral7b_full_size_sampled(dev):
     note(f"[tri sampled] ok, attention worst rel {worst:.2e} (fp16 out {worst16:.2e})")
     del k, v, cache
     torch.cuda.empty_cache()
+
+
+def test_long_sequence_many_splits(dev):
+    """One 32768-token sequence over eight kv heads: 128 splits per (batch, kv head), so
+    the merge's lane-parallel pass over the splits' (max, sum) runs more than one round
+    of 64 and its accumulator loop several rounds of sixteen. Attention on sampled query
+    heads against the oracle's dequantisation of the same bytes."""
+    cfg = get("llama3_8b_long")
+    bits = (4, 2, 3)
+    layer, t = 2, 32768
+    d, hkv = cfg.d, cfg.hkv
+    k, v = layer_kv(cfg, layer, dev, seq=t, batch=1)
+    q = query(cfg, layer, dev)
+    desc = kvq.make_tri_desc(d, hkv, 1, t, *bits, layer, 0)
+    table = kvq.tri_codebook_device(desc, dev)
+    cache = kvq.alloc_tri_cache(desc, dev)
+    kvq.tri_encode(desc, cache, table, k, v, 0)
+    out = kvq.tri_attn_decode(desc, cache, table, q, t, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cb = codebook(d, bits)
+    sg = oc.layer_signs(0, layer, d)
+    cache3 = cache.view(hkv, t // 64, kvq.tri_tile_bytes(desc))
+    rng = np.random.default_rng(41)
+    worst = 0.0
+    for hq in sorted({0, cfg.hq - 1, int(rng.integers(cfg.hq))}):
+        h = hq // cfg.group
+        got = ol.tri_unpack_cache(cache3[h].cpu().numpy(), d, *bits, 1, 1, t, 0, t)
+        kh = ot.dequant(plane_codes(got, "k"), sg, cb)
+        vh = ot.dequant(plane_codes(got, "v"), sg, cb)
+        ref = oc.attention(np64(q[:, hq:hq + 1]), kh, vh)
+        worst = max(worst, compare_attention(np64(out[:, hq:hq + 1]), ref, f"h{hq}"))
+    note(f"[tri long] ok, attention worst rel {worst:.2e}")
+    del k, v, cache
+    torch.cuda.empty_cache()
