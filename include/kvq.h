@@ -193,8 +193,7 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  * and one inverse transform per output head brings o back. Work is split over the
  * sequence (flash-decoding style); the last workgroup of each (batch, kv head) to
  * finish merges the partial (max, sum, vector) triples with a log-sum-exp combine, so
- * the whole operation is one kernel launch (two when the key codebook is too large for
- * an LDS score table: a small query-rotation kernel runs first). Scores, softmax and
+ * the whole operation is one kernel launch. Scores, softmax and
  * all sums in fp32; where the value sum runs on the matrix cores (the variants chosen
  * for most shapes) its operands, weights and rebuilt value elements, are rounded to
  * fp16 (about 2^-11 relative per term; measured within 5.4e-4 relative L2 of the

@@ -11,19 +11,24 @@
 // and the output is o = R^T (sum_j p_j z^_j) with z^_j the rotated-domain values:
 // one inverse transform per output head instead of one per cached token.
 //
-// One launch (two without a key table): grid (splits, batch * kv heads), each wave
-// streaming whole 64-token tiles (12 waves per workgroup with the key table and up to
-// four heads, else 8).
+// One launch: grid (splits, batch * kv heads), each wave streaming whole 64-token tiles
+// (12 waves per workgroup with the key table at up to four heads and with both products
+// on the matrix cores at d = 128, else 8). The variant (KTM, chosen on the host by attn_mode) sets how scores and the
+// value sum are formed:
 //   set-up   the workgroup rotates its G query heads (q~ = R q times
-//            softmax_scale * log2(e) / 255) and builds cos/sin tables and the score
-//            table T[i][code][head] = q~_2i cos + q~_2i+1 sin in LDS. Without a key
-//            table (codebook too large for LDS) a small prepare kernel writes q~ to
-//            the workspace first and scores read it through scalar loads.
-//   keys     one lane per token; the score of pair i is one FMA per head against T.
+//            softmax_scale * log2(e) / 255) and builds cos/sin tables and, with a key
+//            table, the score table T[i][code][head] = q~_2i cos + q~_2i+1 sin in LDS
+//            (half of it for power-of-two n). The variant with neither (built only
+//            for comparisons) has a small prepare kernel write q~ to the workspace
+//            first, and its scores read it through scalar loads.
+//   keys     one lane per token: one FMA per pair and head against T, or the matrix
+//            cores (fp32 4x4x1 products of q~ and the rebuilt key element).
 //            Online softmax per wave in base 2.
-//   values   lanes are 4 rows x 16 columns; each step takes one token per row, its
-//            weights broadcast along the row with DPP, its 16 radius levels computed
-//            once per row and gathered with a lane permute, cos/sin from LDS.
+//   values   on the matrix cores (the defaults): one lane per pair, fp16 products of
+//            four tokens' softmax weights and rebuilt level * (cos, sin) per
+//            instruction, fp32 sums. Vector variant: lanes are 4 rows x 16 columns,
+//            one token per row and step, weights broadcast along the row with DPP,
+//            radius levels gathered with a lane permute.
 //   append   (the fused decode step) the wave that will read the tile of a sequence's
 //            new slot first codes the new token into it, with the append kernel's code,
 //            while the other waves stream their tiles.
@@ -32,9 +37,9 @@
 //            (max, sum, acc[d]) per head and the last workgroup of the (batch, kv head)
 //            to finish combines them (log-sum-exp), inverse-transforms and stores.
 //
-// The kernel is bound by VALU issue and LDS instruction throughput, not by HBM: every
-// (token, pair) of a tile costs G FMAs for the score and 2G for the value sum, and a
-// wave64 FP32 FMA occupies a SIMD for four cycles on this chip.
+// The tile loop is bound by VALU issue first (code unpacking, table addressing, the
+// score FMAs; a wave64 fp32 instruction occupies a SIMD for four cycles on this chip),
+// then by LDS instruction throughput and load latency, not by HBM traffic.
 #include "kvq_attn_common.h"
 #include "kvq_codec_dev.h"
 
