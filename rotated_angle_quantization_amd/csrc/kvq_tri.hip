@@ -52,8 +52,8 @@ struct TriGeom {
   int nd, nn, nr;        // levels per quantiser
 };
 
-__host__ __device__ inline TriGeom tri_geom(int d, int bd, int bn, int br) {
-  TriGeom g;
+__host__ __device__ constexpr TriGeom tri_geom(int d, int bd, int bn, int br) {
+  TriGeom g{};
   g.d = d;
   g.T = d / 3;
   g.R = d - 3 * g.T;
@@ -332,12 +332,17 @@ __device__ __forceinline__ uint32_t staged_field(const uint32_t* plane, int off,
   return (uint32_t)(win >> (off & 31)) & ((1u << wd) - 1u);
 }
 
-template <int D, int G, int DIRB>
+// BD, BN, BR != 0: the bit allocation fixed at compile time (then every field offset,
+// mask and table index of the key loop is a constant and the record length is known);
+// 0: taken from the descriptor.
+template <int D, int G, int DIRB, int BD = 0, int BN = 0, int BR = 0>
 __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnArgs a,
                                                                          const uint8_t* cache) {
   constexpr int P = D / 2, T = D / 3, R = D - 3 * T;
-  const TriGeom& g = a.g;
-  // LDS: direction table (2^(2 bd) unit vectors, sized for bd <= DIRB), norm and
+  constexpr bool FIXED = BD != 0;
+  const TriGeom g = FIXED ? tri_geom(D, BD, BN, BR) : a.g;
+  // LDS: direction table (2^(2 bd) unit vectors indexed by the t code then the s code,
+  // so a triplet field's low 2 bd bits are the index; sized for bd <= DIRB), norm and
   // leftover levels, the rotated query as padded triplets, then per wave: the staged
   // plane and the token weights
   __shared__ float4 s_dir[(1 << DIRB) * (1 << DIRB)];
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
   const int split = blockIdx.x, bk = blockIdx.y, b = bk / a.hkv;
   const int nd = g.nd;
   for (int idx = tid; idx < nd * nd; idx += kTriWaves * 64) {
-    const float s = (float)a.cb[idx / nd], tt = (float)a.cb[idx % nd];
+    const float s = (float)a.cb[idx % nd], tt = (float)a.cb[idx / nd];
     const float z = 1.f - fabsf(s) - fabsf(tt);
     const float x = z >= 0.f ? s : (1.f - fabsf(tt)) * sgn32(s);
     const float y = z >= 0.f ? tt : (1.f - fabsf(s)) * sgn32(tt);
@@ -455,9 +460,9 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
     mf4 kx[HG], ky[HG], kz[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) kx[hg] = ky[hg] = kz[hg] = mf4{0.f, 0.f, 0.f, 0.f};
-    for (int jt = 0; jt < T; ++jt) {
+    auto key_triplet = [&](int jt) {
       const uint32_t val = staged_field(plane, 16 + jt * g.B, g.B, g.words, lane);
-      const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+      const float4 w4 = s_dir[val & (nd * nd - 1)];
       const float rho = s_ln[val >> (2 * g.bd)];
       const float bx = rho * w4.x, by = rho * w4.y, bz = rho * w4.z;
 #pragma unroll
@@ -467,6 +472,12 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
         ky[hg] = tri_mfma(q4.y, by, ky[hg]);
         kz[hg] = tri_mfma(q4.z, bz, kz[hg]);
       }
+    };
+    if constexpr (FIXED) {
+#pragma unroll
+      for (int jt = 0; jt < T; ++jt) key_triplet(jt);
+    } else {
+      for (int jt = 0; jt < T; ++jt) key_triplet(jt);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -512,7 +523,7 @@ __global__ __launch_bounds__(kTriWaves * 64) void tri_attn_split_kernel(TriAttnA
         const uint32_t val = staged_field(plane, foff, fwd, g.words, t4 + u);
         float c0 = 0.f, c1 = 0.f, c2 = 0.f;
         if (f < T) {
-          const float4 w4 = s_dir[(val & (nd - 1)) * nd + ((val >> g.bd) & (nd - 1))];
+          const float4 w4 = s_dir[val & (nd * nd - 1)];
           const float rho = s_ln[val >> (2 * g.bd)];
           c0 = rho * w4.x;
           c1 = rho * w4.y;
@@ -871,6 +882,19 @@ size_t tri_align256(size_t v) { return (v + 255) & ~(size_t)255; }
 template <int D, int DIRB>
 hipError_t tri_attn_split(const TriAttnArgs& a, const uint8_t* cache, hipStream_t s) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.batch * a.hkv));
+  if constexpr (DIRB == 4) {
+    // 4 + 4 bits of direction, 2 of norm and 3 per leftover (3.5 bits per element at
+    // d = 128) compiled with the allocation fixed
+    if (a.g.bd == 4 && a.g.bn == 2 && a.g.br == 3) {
+      switch (a.group) {
+        case 1: hipLaunchKernelGGL((tri_attn_split_kernel<D, 1, 4, 4, 2, 3>), grid, dim3(kTriWaves * 64), 0, s, a, cache); return hipSuccess;
+        case 2: hipLaunchKernelGGL((tri_attn_split_kernel<D, 2, 4, 4, 2, 3>), grid, dim3(kTriWaves * 64), 0, s, a, cache); return hipSuccess;
+        case 4: hipLaunchKernelGGL((tri_attn_split_kernel<D, 4, 4, 4, 2, 3>), grid, dim3(kTriWaves * 64), 0, s, a, cache); return hipSuccess;
+        case 8: hipLaunchKernelGGL((tri_attn_split_kernel<D, 8, 4, 4, 2, 3>), grid, dim3(kTriWaves * 64), 0, s, a, cache); return hipSuccess;
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (a.group) {
     case 1: hipLaunchKernelGGL((tri_attn_split_kernel<D, 1, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
     case 2: hipLaunchKernelGGL((tri_attn_split_kernel<D, 2, DIRB>), grid, dim3(kTriWaves * 64), 0, s, a, cache); break;
