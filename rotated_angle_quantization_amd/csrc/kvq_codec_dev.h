@@ -78,10 +78,13 @@ __device__ __forceinline__ float angle_f32(float a, float b) {
 // first scaled by a power of two in binary64 (exact, and the angle is unchanged) and
 // estimated again; a non-finite estimate also fails the margin test. The estimate runs
 // for zero pairs too and the zero test only selects the result, so no branch surrounds
-// the common path.
+// the common path. kWide = false states that the pair comes from fp16 inputs: its
+// nonzero components are then sums of multiples of 2^-24 scaled by 1/sqrt(d) <= 1 and
+// bounded by 65504 sqrt(d), inside [2^-60, 2^60] for every d the library serves, so the
+// range test is skipped (the exact branch still scales, which then changes nothing).
 constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
 constexpr float kAngleRangeLo = 0x1p-60f, kAngleRangeHi = 0x1p60f;
-template <class Edge>  // edge(k) = (cos, sin) of (k + 1/2) 2 pi / n in binary64
+template <bool kWide = true, class Edge>  // edge(k) = (cos, sin) of (k + 1/2) 2 pi / n
 __device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
                                           float bins_per_rad_f, float bin_rad_f,
                                           const Edge& edge) {
@@ -91,7 +94,7 @@ __device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
   float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
   int c = (int)cf;  // in [-n/2, n/2]
   const float mxf = fmaxf(fabsf(af), fabsf(bf));
-  const bool in_range = mxf >= kAngleRangeLo && mxf <= kAngleRangeHi;
+  const bool in_range = !kWide || (mxf >= kAngleRangeLo && mxf <= kAngleRangeHi);
   const bool near_edge = !(0.5f * bin_rad_f - fabsf(res) >= kAngleMargin);  // NaN: near
   if (__builtin_expect((near_edge || !in_range) && !zero, 0)) {
     if (!in_range) {
@@ -140,12 +143,17 @@ __device__ __forceinline__ KeyScale key_scale(double max_r2) {
   k.s_255 = k.s * (1.0 / 255.0);
   return k;
 }
+// kWide = false (fp16 inputs): r <= |x| <= 65504 sqrt(d), and s is max r rounded to fp16
+// (or 65504 past that), so r / s <= sqrt(d) and t < 255 sqrt(d) + 1 needs no cap before
+// the conversion.
+template <bool kWide = true>
 __device__ __forceinline__ int key_level(double r2, const KeyScale& k) {
   int rho = 0;
   if (k.s > 0.0) {
     // capped so that a radius past the fp32 range (fp32 inputs near its top) converts
     // to a level above 255 rather than to an undefined integer
-    const float t = fminf(__builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f, 256.f);
+    float t = __builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f;
+    if (kWide) t = fminf(t, 256.f);
     const float m = rintf(t);
     rho = (int)floorf(t);
     if (__builtin_expect(fabsf(t - m) < 5e-4f, 0)) {
@@ -166,6 +174,7 @@ struct ValueScale {
   double smin, smax, smin2;
   bool spread;
   float scale, inv_smin2;
+  float trust;  // |frac(t) - 1/2| above this: the estimate's level is trusted
 };
 __device__ __forceinline__ ValueScale value_scale(double max_r2, double min_r2) {
   ValueScale v;
@@ -179,6 +188,13 @@ __device__ __forceinline__ ValueScale value_scale(double max_r2, double min_r2) 
       v.spread ? __log2f((float)v.smax * __builtin_amdgcn_rcpf((float)v.smin)) : 1.f;
   v.scale = 7.5f * __builtin_amdgcn_rcpf(l2f);
   v.inv_smin2 = __builtin_amdgcn_rcpf((float)v.smin2);
+  // The margin of value_level below, with |lr| bounded for the whole vector: every
+  // radius coded by its estimate lies in [s_min, max r], and max r <= s_max (1 + 2^-11)
+  // unless s_max was clipped at 65504, so 0 <= lr <= 2 l2 + 0.0015 up to rounding,
+  // below 2 l2 + 1. Radii with lr past 2 l2 + 1 (clipped s_max only) have t >= 15.5 +
+  // 7.5 / l2 >= 15.6 (l2 < 48 for fp16 parameters), so both the estimate and the
+  // binary64 formula give level 15 after the clamp.
+  v.trust = 0.5f - (v.scale * (4e-6f + 1e-6f * (2.f * l2f + 1.f)) + 2e-5f);
   return v;
 }
 __device__ __forceinline__ int value_level(double r2, const ValueScale& v) {
@@ -187,12 +203,14 @@ __device__ __forceinline__ int value_level(double r2, const ValueScale& v) {
     // lr = log2(r^2 / s_min^2) <= 2 l2; t = 7.5 lr / l2 + 1/2. With absolute errors
     // <= 7e-7 (lr) and 4e-7 (l2), |dt| <= 7.5 (7e-7 + 2 * 4e-7) / l2 plus ~1e-6 of fp32
     // rounding; the margin below is more than twice that.
+    // The margin scale (4e-6 + 1e-6 |lr|) + 2e-5 is applied with |lr| at its bound for
+    // the vector (ValueScale::trust): the estimate is trusted only when the fractional
+    // part of t lies farther than that from 0 and 1.
     const float lr = __log2f((float)r2 * v.inv_smin2);
     const float t = fminf(lr * v.scale + 0.5f, 16.f);  // capped: r^2 past the fp32 range
     const float fl = floorf(t);
-    const float margin = v.scale * (4e-6f + 1e-6f * fabsf(lr)) + 2e-5f;
     rho = (int)fl;
-    if (__builtin_expect(fminf(t - fl, fl + 1.0f - t) < margin, 0))
+    if (__builtin_expect(!(fabsf(t - fl - 0.5f) <= v.trust), 0))
       rho = (int)floor(15.0 * log(sqrt(r2) / v.smin) / log(v.smax / v.smin) + 0.5);
     rho = min(max(rho, 0), 15);
   }

@@ -16,12 +16,20 @@
 //
 // Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens); a lane owns a
 // quarter of one vector (d/4 elements in interleaved 8-element chunks), so 16 tokens
-// are coded per step.
-// The transform's first log2(d/4) stages are in-lane; the last two exchange with
-// lanes xor 1 and xor 2 through DPP quad permutes. Per-vector maxima, minima and
-// parameters are reduced over the quad. Codes of the tile are staged in LDS as bytes
-// and then packed: key planes one lane per token, value planes one lane per pair,
-// matching the layout's word order so every store is a coalesced dword.
+// are coded per step: the token is the lane's position in its 16-lane row and the
+// quarter is the row.
+// The transform's first log2(d/4) stages are in-lane; the last two pair the rows
+// (quarter bit 0: rows 0 <-> 1 and 2 <-> 3; quarter bit 1: rows 0, 1 <-> 2, 3). Each of
+// those is taken on two of the lane's values at once with gfx950's row swaps
+// (v_permlane16_swap, v_permlane32_swap): after a swap of values s and s' between
+// partner lanes, each lane holds both operands of one butterfly (the lower lane's value
+// in the first register, the upper's in the second) and keeps both of its outputs, so
+// one swap per 32-bit word and one add or subtract per value replace two lane moves and
+// a multiply-add. The lanes' element sets change with it; for d = 128 each lane ends
+// with 32 consecutive elements. Per-vector maxima, minima and parameters are reduced
+// over the token's four lanes. Codes of the tile are staged in LDS as bytes and then
+// packed: key planes one lane per token, value planes one lane per pair, matching the
+// layout's word order so every store is a coalesced dword.
 #include <hip/hip_fp16.h>
 
 #include "kvq_codec_dev.h"
@@ -34,15 +42,34 @@ __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
   return (m.w[e >> 6] >> (e & 63)) & 1ull;
 }
 
-// Lane exchange inside a quad (lanes 4k..4k+3) of a double: xor 1 or xor 2.
-template <int CTRL>
-__device__ __forceinline__ double quad_xor(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+// Row-pair butterfly of two doubles x, y held by every lane, between the lanes of rows
+// that differ in bit 0 of the row index (ROWS32 false: v_permlane16_swap exchanges odd
+// rows of its first operand with even rows of its second) or in bit 1 (ROWS32 true:
+// v_permlane32_swap exchanges lanes 32-63 of its first operand with lanes 0-31 of its
+// second). After the swap the lower lane holds (own x, partner's x) and the upper lane
+// (partner's y, own y), both as (value of the lower lane, value of the upper lane), so
+// every lane forms sum and difference in the same way: the lower lane's outputs are
+// those of x's butterfly, the upper lane's those of y's.
+template <bool ROWS32>
+__device__ __forceinline__ void row_butterfly(double& x, double& y) {
+  const uint64_t a = (uint64_t)__double_as_longlong(x), b = (uint64_t)__double_as_longlong(y);
+  uint32_t lo0, lo1, hi0, hi1;
+  if constexpr (ROWS32) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)b, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+    lo0 = lo[0]; lo1 = lo[1]; hi0 = hi[0]; hi1 = hi[1];
+  } else {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+    lo0 = lo[0]; lo1 = lo[1]; hi0 = hi[0]; hi1 = hi[1];
+  }
+  const double u = __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0));
+  const double v = __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
+  x = u + v;
+  y = u - v;
 }
-constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 
 constexpr int kRow = 68;  // LDS row stride (bytes) of the per-token code staging
 
@@ -123,7 +150,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   __shared__ double2 s_kedge[256], s_vedge[256];  // bin edges (k + 1/2) 2 pi / n
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tq = lane >> 2, q = lane & 3;  // token within the step, quarter of the vector
+  const int tq = lane & 15, q = lane >> 4;  // token within the step, quarter of the vector
   for (int k = threadIdx.x; k < 256; k += kEncWaves * 64) {
     s_kedge[k] = bin_edge(k, a.n_k);
     s_vedge[k] = bin_edge(k, a.n_v);
@@ -162,7 +189,6 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
 #pragma unroll
   for (int k = 0; k < PL; ++k)
     hmask[k] = (((sbits >> (2 * k)) & 1u) << 15) | (((sbits >> (2 * k + 1)) & 1u) << 31);
-  const double qsgn1 = (q & 1) ? -1.0 : 1.0, qsgn2 = (q & 2) ? -1.0 : 1.0;
   const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;  // n / (2 pi)
   const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
 
@@ -229,10 +255,20 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
           y[i + hs] = u - v;
         }
       }
+      // Quarter bit 0 (element stride 8): local slots s and s + 8 (chunk bit 0). After
+      // it, slot 8 (2 m1 + c) + r of lane (q1, q0) holds element
+      // 32 (2 m1 + q0) + 8 (2 q1 + c) + r.
 #pragma unroll
-      for (int i = 0; i < E; ++i) y[i] = fma(y[i], qsgn1, quad_xor<kQuadXor1>(y[i]));
+      for (int i = 0; i < E; ++i)
+        if (!(i & 8)) row_butterfly<false>(y[i], y[i + 8]);
+      // Quarter bit 1 (element stride 16). d = 128: slots s and s + 16 (m1); after it
+      // slot s holds element 32 q + s. d = 64 (m1 = 0): slots s and s + 8 (c); after it
+      // slot 8 c + r holds element 32 q0 + 16 c + 8 q1 + r.
 #pragma unroll
-      for (int i = 0; i < E; ++i) y[i] = fma(y[i], qsgn2, quad_xor<kQuadXor2>(y[i]));
+      for (int i = 0; i < E; ++i) {
+        constexpr int kPart = E > 16 ? 16 : 8;
+        if (!(i & kPart)) row_butterfly<true>(y[i], y[i + kPart]);
+      }
 #pragma unroll
       for (int i = 0; i < E; ++i) y[i] *= a.inv_sqrt_d;
 
@@ -244,8 +280,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         mx = fmax(mx, r2[k]);
         mn = fmin(mn, r2[k]);
       }
-      mx = fmax(mx, quad_xor<kQuadXor1>(mx));
-      mx = fmax(mx, quad_xor<kQuadXor2>(mx));
+      mx = fmax(mx, shfl_xor_f64(mx, 16));
+      mx = fmax(mx, shfl_xor_f64(mx, 32));
 
       uint8_t cc[PL], rr[PL];
       if (kv == 0) {
@@ -253,30 +289,31 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         const auto edge = [&](int e) { return s_kedge[e]; };
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = (uint8_t)angle_code(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_k, kbpr, kbin,
-                                      edge);
-          rr[k] = (uint8_t)key_level(r2[k], ksc);
+          cc[k] = (uint8_t)angle_code<F32IN>(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_k, kbpr,
+                                             kbin, edge);
+          rr[k] = (uint8_t)key_level<F32IN>(r2[k], ksc);
         }
         if (act && q == 0) s_ks[j] = fp16_bits(ksc.s);
       } else {
-        mn = fmin(mn, quad_xor<kQuadXor1>(mn));
-        mn = fmin(mn, quad_xor<kQuadXor2>(mn));
+        mn = fmin(mn, shfl_xor_f64(mn, 16));
+        mn = fmin(mn, shfl_xor_f64(mn, 32));
         const ValueScale vsc = value_scale(mx, mn);
         const auto edge = [&](int e) { return s_vedge[e]; };
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          cc[k] = (uint8_t)angle_code(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_v, vbpr, vbin,
-                                      edge);
+          cc[k] = (uint8_t)angle_code<F32IN>(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_v, vbpr,
+                                             vbin, edge);
           rr[k] = (uint8_t)value_level(r2[k], vsc);
         }
         if (act && q == 0)
           s_vp[j] = (uint32_t)fp16_bits(vsc.smin) | ((uint32_t)fp16_bits(vsc.smax) << 16);
       }
       if (act) {
-        // local pair k is pair 16 (k / 4) + 4 q + k % 4 of the vector
+        // local pair k (slots 2k, 2k + 1) of the vector: 16 q + k for d = 128,
+        // 16 q0 + 8 (k / 4) + 4 q1 + k % 4 for d = 64 (the element maps above)
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
-          const int i = 16 * (k >> 2) + 4 * q + (k & 3);
+          const int i = D == 128 ? 16 * q + k : 16 * (q & 1) + 8 * (k >> 2) + 4 * (q >> 1) + (k & 3);
           if (kv == 0) {
             s_kc[j][i] = cc[k];
             s_kr[j][i] = rr[k];

@@ -173,8 +173,11 @@ def test_value_level_fast_path_equals_binary64():
                 t = np.minimum(fma32(lr, np.full_like(lr, scale), np.full_like(lr, f32(0.5))),
                                f32(16))
                 fl = np.floor(t)
-                margin = (scale * (f32(4e-6) + f32(1e-6) * np.abs(lr)) + f32(2e-5)).astype(np.float32)
-                trusted = np.minimum(t - fl, fl + 1 - t) >= margin
+                # the device bounds |lr| by 2 l2 + 1 for the whole vector
+                trust = (f32(0.5) - (scale * (f32(4e-6) + f32(1e-6) * (f32(2) * l2f + f32(1)))
+                                     + f32(2e-5))).astype(np.float32)
+                assert (np.abs(lr) <= 2 * l2f + 1).all()
+                trusted = np.abs((t - fl - f32(0.5)).astype(np.float32)) <= trust
                 level = np.clip(fl, 0, 15)
                 bad = trusted & (level != exact)
                 assert not bad.any(), (smin, smax, r[bad][:3])
