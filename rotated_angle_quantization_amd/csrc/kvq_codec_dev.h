@@ -210,8 +210,14 @@ __device__ __forceinline__ int value_level(double r2, const ValueScale& v) {
     const float t = fminf(lr * v.scale + 0.5f, 16.f);  // capped: r^2 past the fp32 range
     const float fl = floorf(t);
     rho = (int)fl;
-    if (__builtin_expect(!(fabsf(t - fl - 0.5f) <= v.trust), 0))
-      rho = (int)floor(15.0 * log(sqrt(r2) / v.smin) / log(v.smax / v.smin) + 0.5);
+    if (__builtin_expect(!(fabsf(t - fl - 0.5f) <= v.trust), 0)) {
+      // s_max passes through an empty asm statement here, so the compiler cannot hoist
+      // the binary64 log of s_max / s_min (shared by every pair of the vector) out of
+      // this rarely taken branch into the common path
+      double smax = v.smax;
+      asm volatile("" : "+v"(smax));
+      rho = (int)floor(15.0 * log(sqrt(r2) / v.smin) / log(smax / v.smin) + 0.5);
+    }
     rho = min(max(rho, 0), 15);
   }
   return rho;

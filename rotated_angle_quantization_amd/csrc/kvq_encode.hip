@@ -50,6 +50,17 @@ __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
 // (partner's y, own y), both as (value of the lower lane, value of the upper lane), so
 // every lane forms sum and difference in the same way: the lower lane's outputs are
 // those of x's butterfly, the upper lane's those of y's.
+// Maximum or minimum of x over the four rows' lanes at the same row position (the four
+// quarters of a token), by lane permutes.
+__device__ __forceinline__ double rows_max(double x) {
+  x = fmax(x, shfl_xor_f64(x, 16));
+  return fmax(x, shfl_xor_f64(x, 32));
+}
+__device__ __forceinline__ double rows_min(double x) {
+  x = fmin(x, shfl_xor_f64(x, 16));
+  return fmin(x, shfl_xor_f64(x, 32));
+}
+
 template <bool ROWS32>
 __device__ __forceinline__ void row_butterfly(double& x, double& y) {
   const uint64_t a = (uint64_t)__double_as_longlong(x), b = (uint64_t)__double_as_longlong(y);
@@ -280,8 +291,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         mx = fmax(mx, r2[k]);
         mn = fmin(mn, r2[k]);
       }
-      mx = fmax(mx, shfl_xor_f64(mx, 16));
-      mx = fmax(mx, shfl_xor_f64(mx, 32));
+      mx = rows_max(mx);
 
       uint8_t cc[PL], rr[PL];
       if (kv == 0) {
@@ -295,8 +305,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         }
         if (act && q == 0) s_ks[j] = fp16_bits(ksc.s);
       } else {
-        mn = fmin(mn, shfl_xor_f64(mn, 16));
-        mn = fmin(mn, shfl_xor_f64(mn, 32));
+        mn = rows_min(mn);
         const ValueScale vsc = value_scale(mx, mn);
         const auto edge = [&](int e) { return s_vedge[e]; };
 #pragma unroll
