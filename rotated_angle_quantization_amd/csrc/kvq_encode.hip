@@ -209,30 +209,24 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
     const int jr = min(jb + tq, j_hi - 1);
     return (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
   };
-  // fp16 input: the K and V words of the next step are loaded while this one is coded
-  uint32_t next_raw[2][PL];
-  auto load_raw = [&](int jb) {
-    const int64_t off = row_offset(jb);
+  // fp16 input: one buffer per plane; a plane's words of the next step are requested as
+  // soon as this step's have been widened, so they load while the rest is coded
+  uint32_t raw[2][PL];
+  auto load_raw = [&](int kv, int jb) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(
+        static_cast<const __half*>(kv == 0 ? kin : vin) + row_offset(jb));
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const uint32_t* p =
-          reinterpret_cast<const uint32_t*>(static_cast<const __half*>(kv == 0 ? kin : vin) + off);
-#pragma unroll
-      for (int k = 0; k < PL; ++k) next_raw[kv][k] = p[16 * (k >> 2) + (k & 3)];
-    }
+    for (int k = 0; k < PL; ++k) raw[kv][k] = p[16 * (k >> 2) + (k & 3)];
   };
-  if (!F32IN && j_lo < j_hi) load_raw(j_lo);
+  if (!F32IN && j_lo < j_hi) {
+    load_raw(0, j_lo);
+    load_raw(1, j_lo);
+  }
 
   for (int jb = j_lo; jb < j_hi; jb += TPS) {
     const int j = jb + tq;
     const bool act = j < j_hi;
     const int64_t row_off = row_offset(jb);
-    uint32_t raw[2][PL];
-#pragma unroll
-    for (int kv = 0; kv < 2; ++kv)
-#pragma unroll
-      for (int k = 0; k < PL; ++k) raw[kv][k] = next_raw[kv][k];
-    if (!F32IN && jb + TPS < j_hi) load_raw(jb + TPS);
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const void* src = kv == 0 ? kin : vin;
@@ -254,6 +248,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
           y[2 * k] = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
           y[2 * k + 1] = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
         }
+        // unconditional: past the range the clamped row is re-read (just loaded, so
+        // a cache hit), and a conditional load would make the buffer a copy
+        load_raw(kv, jb + TPS);
       }
       // Walsh-Hadamard: in-lane stages, then lanes xor 1 and xor 2 (natural order)
 #pragma unroll
