@@ -181,3 +181,29 @@ def test_value_level_fast_path_equals_binary64():
                 level = np.clip(fl, 0, 15)
                 bad = trusted & (level != exact)
                 assert not bad.any(), (smin, smax, r[bad][:3])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp16_pairs_inside_estimate_range(d):
+    """For fp16 inputs the encoder skips the estimate's range test: every nonzero
+    rotated component is a signed sum of fp16 values (multiples of 2^-24) scaled by
+    1/sqrt(d), and at most 65504 sqrt(d) in size. Checked on the extremes: one smallest
+    subnormal, a vector of +-65504, and random mixtures of tiny and huge values."""
+    from oracle import codec
+    rng = np.random.default_rng(11)
+    sg = codec.layer_signs(0, 0, d)
+    xs = [np.zeros(d), np.full(d, 65504.0), np.where(sg > 0, 65504.0, -65504.0)]
+    xs[0][rng.integers(d)] = 2.0 ** -24
+    for _ in range(200):
+        x = np.where(rng.random(d) < 0.5, 2.0 ** -24 * rng.integers(1, 4, d),
+                     65504.0 * rng.choice([-1.0, 1.0], d))
+        x[rng.random(d) < 0.7] = 0.0
+        xs.append(x.astype(np.float16).astype(np.float64))
+    for x in xs:
+        y = codec.rotate(x[None], sg)[0]
+        nz = np.abs(y[y != 0.0])
+        assert nz.size == 0 or (nz.min() >= 2.0 ** -60 and nz.max() <= 2.0 ** 60)
+        assert np.abs(y).max() <= 65504.0 * np.sqrt(d)
+        nzp = np.maximum(np.abs(y[0::2]), np.abs(y[1::2]))
+        nzp = nzp[nzp > 0]
+        assert nzp.size == 0 or nzp.min() >= 2.0 ** -24 / np.sqrt(d)

@@ -232,6 +232,11 @@ def test_degenerate_vectors(dev):
     sg = torch.tensor(oc.layer_signs(0, 0, d), device=dev, dtype=torch.float32)
     h = torch.tensor(oc.hadamard(d), device=dev, dtype=torch.float32)
     k[0, 6, 0] = sg * h[:, 9]  # rotates to a one-hot: angles on bin centres
+    # near the top of the fp16 range: radii past 65504 (the clipped s_max / key scale
+    # leave levels past the last one, clamped on both sides)
+    big = 60000.0 * torch.sign(torch.randn(2, 2, d, device=dev))
+    k[0, 7:9] = big[0]
+    v[0, 7:9] = big[1]
     q = torch.randn(1, 4, d, device=dev)
     run_full_check(dev, k.half(), v.half(), q.half(), d, 128, 64, tag="degenerate")
 
