@@ -232,11 +232,15 @@ def test_degenerate_vectors(dev):
     sg = torch.tensor(oc.layer_signs(0, 0, d), device=dev, dtype=torch.float32)
     h = torch.tensor(oc.hadamard(d), device=dev, dtype=torch.float32)
     k[0, 6, 0] = sg * h[:, 9]  # rotates to a one-hot: angles on bin centres
-    # near the top of the fp16 range: radii past 65504 (the clipped s_max / key scale
-    # leave levels past the last one, clamped on both sides)
-    big = 60000.0 * torch.sign(torch.randn(2, 2, d, device=dev))
-    k[0, 7:9] = big[0]
-    v[0, 7:9] = big[1]
+    # fp16 inputs near the top of the range: one-hot rotations whose radius (6000
+    # sqrt(128) = 67,882) is past the fp16 range, so the key scale and s_max are clipped
+    # at 65504 and the level estimates run past the last level (clamped on both sides),
+    # while the reconstructed elements (65504 / sqrt(128)) stay inside fp16; and +-4000
+    # sign vectors (large radii in every pair)
+    k[0, 7, 0] = sg * h[:, 5] * 6000.0
+    v[0, 7, 1] = sg * h[:, 12] * 6000.0
+    k[0, 8] = 4000.0 * torch.sign(torch.randn(2, d, device=dev))
+    v[0, 8] = 4000.0 * torch.sign(torch.randn(2, d, device=dev))
     q = torch.randn(1, 4, d, device=dev)
     run_full_check(dev, k.half(), v.half(), q.half(), d, 128, 64, tag="degenerate")
 
