@@ -10,11 +10,17 @@
 // transform), and the readings of the steps the page leaves open are stated at the
 // declarations in kvq.h.
 //
-// Kernels (one wave per token-head for the codec; the lane maps follow the data):
-//   encode     lane i holds elements 2i, 2i+1 through the binary64 transform; the unit
-//              vector is staged in LDS and lane j reads triplet j (or leftover coordinate
-//              j - T), takes its decisions in binary64 against the boundaries in LDS and
-//              ORs its field into the record's words in LDS; lane w stores word w.
+// Kernels (the lane maps follow the data):
+//   encode     d = 128: a wave per (batch, kv head, 64-token tile), sixteen token-heads
+//              per step with a quarter vector per lane, the transform's last two stages
+//              as row swaps; each lane then codes the triplets starting in its 32
+//              elements, in binary64, with branch-free searches of the boundaries in LDS
+//              (compiled for the 4/2/3 allocation, generic otherwise), and ORs the
+//              fields into the tokens' records in LDS. d = 64: a wave per token-head;
+//              lane i holds elements 2i, 2i+1 through the transform; the unit vector is
+//              staged in LDS and lane j reads triplet j (or leftover coordinate j - T),
+//              takes its decisions against the boundaries in LDS and ORs its field into
+//              the record's words in LDS; lane w stores word w.
 //   decode     lane j rebuilds its triplet (or leftover) in fp32 from the levels, the
 //              elements are permuted back to two per lane for the inverse transform.
 //   attention  split kernel (grid: splits x batch * kv heads, four waves, a wave per
@@ -96,12 +102,34 @@ __device__ __forceinline__ int nearest(const double* bounds, int n_levels, doubl
   return lo;
 }
 
+// The same count for 2^bits levels without a data-dependent loop: steps of
+// 2^(bits-1), .., 1, each taken when the boundary it lands on is still below x (the
+// index never passes 2^bits - 1, the last boundary's count). Straight-line code, so the
+// searches of different values overlap their LDS reads. BITS > 0 fixes the width at
+// compile time; BITS = 0 reads it from bits (steps past the width skipped, a uniform
+// test).
+template <int BITS>
+__device__ __forceinline__ int nearest_steps(const double* bounds, int bits, double x) {
+  int idx = 0;
+  if constexpr (BITS > 0) {
+#pragma unroll
+    for (int step = 1 << (BITS - 1); step >= 1; step >>= 1)
+      if (bounds[idx + step - 1] < x) idx += step;
+  } else {
+#pragma unroll
+    for (int step = 128; step >= 1; step >>= 1)
+      if ((step << 1) <= (1 << bits) && bounds[idx + step - 1] < x) idx += step;
+  }
+  return idx;
+}
+
 __device__ __forceinline__ double sgn64(double x) { return x < 0.0 ? -1.0 : 1.0; }
 __device__ __forceinline__ float sgn32(float x) { return x < 0.f ? -1.f : 1.f; }
 
 
 // ------------------------------------------------------------------------------ encode
 
+// d = 64 (and the reference layout of the decisions): one wave per token-head.
 template <int D, bool F32>
 __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cache, const void* k,
                                                          const void* v, int64_t sb, int64_t st,
@@ -208,6 +236,214 @@ __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cac
     asm volatile("" ::: "memory");
     if (lane < g.words) tp[(size_t)(kv * g.words + lane) * kTile + t] = rec[lane];
     asm volatile("" ::: "memory");  // the next plane's clear stays after this read
+  }
+}
+
+// Encode at d = 128, sixteen token-heads per wave. One wave per (batch, kv head, tile of
+// 64 tokens), coded in steps of 16 tokens: the token is the lane's position in its
+// 16-lane row and the row is the quarter of the vector. The binary64 transform runs as in
+// the angle encoder: in-lane butterflies for element strides 1, 2, 4, 32 and 64, then the
+// strides 8 and 16 as row swaps (v_permlane16_swap, v_permlane32_swap) on two of the
+// lane's values at once, after which lane row q holds elements 32 q .. 32 q + 31 of its
+// token. Triplet j (elements 3j .. 3j + 2) is coded by the row holding its first element:
+// rows 0 and 1 code 11 triplets each (their last one takes one or two elements of the next
+// row), rows 2 and 3 ten, and row 3 also the two leftover coordinates. The decisions are
+// those of tri_encode_kernel, in binary64: triplet norm rho = |c| / N, the octahedral
+// point from c / |c|_1 (the same point as from u = y / N: the map is scale-free), the
+// leftover coordinates y / N; each is located among the quantiser's boundaries in LDS.
+// Results can differ from a u = y / N evaluation only in the last bits, i.e. only for
+// values within rounding distance of a boundary. Fields are ORed into the tokens'
+// records in LDS, and a row of 16 lanes stores one record word of 16 consecutive slots.
+constexpr int kTriRowWaves = 4;
+
+template <bool ROWS32>
+__device__ __forceinline__ void tri_row_butterfly(double& x, double& y) {
+  const uint64_t a = (uint64_t)__double_as_longlong(x), b = (uint64_t)__double_as_longlong(y);
+  uint32_t lo0, lo1, hi0, hi1;
+  if constexpr (ROWS32) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)a, (uint32_t)b, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane32_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+    lo0 = lo[0]; lo1 = lo[1]; hi0 = hi[0]; hi1 = hi[1];
+  } else {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+    lo0 = lo[0]; lo1 = lo[1]; hi0 = hi[0]; hi1 = hi[1];
+  }
+  // (value of the lower lane, value of the upper lane) in every lane: see the encoder
+  const double u = __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0));
+  const double w = __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
+  x = u + w;
+  y = u - w;
+}
+
+// BD, BN, BR: the bit allocation fixed at compile time (the searches' step counts), or 0
+// for the widths of the descriptor.
+template <bool F32, int BD, int BN, int BR>
+__global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
+    TriArgs a, uint8_t* cache, const void* k, const void* v, int64_t sb, int64_t st, int64_t sh) {
+  constexpr int D = 128, E = 32, PL = 16, TPS = 16;
+  const TriGeom& g = a.g;
+  __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
+  __shared__ uint32_t s_rec_all[kTriRowWaves][TPS][kTriMaxRecordWords + 1];
+  const int bo = cb_bounds_off(g);
+  for (int i = threadIdx.x; i < g.nd - 1; i += kTriRowWaves * 64) s_bd[i] = a.cb[bo + i];
+  for (int i = threadIdx.x; i < g.nn - 1; i += kTriRowWaves * 64) s_bn[i] = a.cb[bo + g.nd - 1 + i];
+  for (int i = threadIdx.x; i < g.nr - 1; i += kTriRowWaves * 64)
+    s_br[i] = a.cb[bo + g.nd - 1 + g.nn - 1 + i];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tq = lane & 15, q = lane >> 4;  // token within the step, quarter of the vector
+  uint32_t(*s_rec)[kTriMaxRecordWords + 1] = s_rec_all[wave];
+  const int tile_lo = a.t0 / kTile;
+  const int tiles_touched = (a.t0 + a.ntok - 1) / kTile - tile_lo + 1;
+  const int task = blockIdx.x * kTriRowWaves + wave;
+  if (task >= a.batch * a.hkv * tiles_touched) return;  // no barrier follows
+  const int bh = task / tiles_touched, b = bh / a.hkv, h = bh % a.hkv;
+  const int tile = tile_lo + task % tiles_touched, tok_base = tile * kTile;
+  const int j_lo = max(a.t0 - tok_base, 0), j_hi = min(a.t0 + a.ntok - tok_base, kTile);
+  const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
+  uint32_t* tp = reinterpret_cast<uint32_t*>(
+      cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * tile_bytes);
+
+  // lane slots 8m + r hold elements 32m + 8q + r before the row stages; bit 8m + r of
+  // sbits is that element's sign, and for fp16 input hmask[k] flips the sign bits of the
+  // packed pair k
+  uint32_t sbits = 0;
+#pragma unroll
+  for (int m = 0; m < E / 8; ++m)
+    sbits |= (uint32_t)((a.sign.w[(32 * m + 8 * q) >> 6] >> ((32 * m + 8 * q) & 63)) & 0xFFu) << (8 * m);
+  uint32_t hmask[PL];
+#pragma unroll
+  for (int kk = 0; kk < PL; ++kk)
+    hmask[kk] = (((sbits >> (2 * kk)) & 1u) << 15) | (((sbits >> (2 * kk + 1)) & 1u) << 31);
+
+  // this row's triplets: the first is J0, its first element is local slot o
+  const int J0 = q == 0 ? 0 : q == 1 ? 11 : q == 2 ? 22 : 32;
+  const int ntri = q < 2 ? 11 : 10;
+  const int o = 3 * J0 - 32 * q;  // 0, 1, 2, 0
+
+  auto row_offset = [&](int jb) {
+    const int jr = min(jb + tq, j_hi - 1);
+    return (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
+  };
+  uint32_t raw[2][PL];
+  auto load_raw = [&](int kv, int jb) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(
+        static_cast<const __half*>(kv == 0 ? k : v) + row_offset(jb));
+#pragma unroll
+    for (int kk = 0; kk < PL; ++kk) raw[kv][kk] = p[16 * (kk >> 2) + (kk & 3)];
+  };
+  if (!F32) {
+    load_raw(0, j_lo);
+    load_raw(1, j_lo);
+  }
+
+  for (int jb = j_lo; jb < j_hi; jb += TPS) {
+    const int j = jb + tq;
+    const bool act = j < j_hi;
+    const int64_t row_off = row_offset(jb);
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {  // unrolled: raw[kv] stays in registers
+      double y[E + 3];
+      if (F32) {
+        const float* p = static_cast<const float*>(kv == 0 ? k : v) + row_off;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float f = p[32 * (e >> 3) + (e & 7)];
+          if (!act) f = 0.f;
+          if ((sbits >> e) & 1u) f = -f;
+          y[e] = (double)f;
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < PL; ++kk) {
+          const uint32_t w = (act ? raw[kv][kk] : 0u) ^ hmask[kk];
+          y[2 * kk] = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
+          y[2 * kk + 1] = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
+        }
+        load_raw(kv, jb + TPS);  // clamped row past the range: re-read, discarded
+      }
+#pragma unroll
+      for (int hs = 1; hs < E; hs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          if (i & hs) continue;
+          const double u = y[i], w = y[i + hs];
+          y[i] = u + w;
+          y[i + hs] = u - w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (!(i & 8)) tri_row_butterfly<false>(y[i], y[i + 8]);
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (!(i & 16)) tri_row_butterfly<true>(y[i], y[i + 16]);
+      // slot s now holds element 32 q + s
+      double n2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        y[i] *= a.inv_sqrt_d;
+        n2 = fma(y[i], y[i], n2);
+      }
+      n2 += shfl_xor_f64(n2, 16);
+      n2 += shfl_xor_f64(n2, 32);
+      const double nrm = sqrt(n2);
+      const double rn = nrm > 0.0 ? 1.0 / nrm : 0.0;
+      // the next row's first two elements (for the triplets that straddle rows)
+      y[E] = __shfl(y[0], (lane + 16) & 63, 64);
+      y[E + 1] = __shfl(y[1], (lane + 16) & 63, 64);
+      y[E + 2] = 0.0;
+
+      // the records of this step's tokens: word 0 starts as the fp16 bits of N
+      for (int i = lane; i < TPS * g.words; i += 64) {
+        const int tt = i / g.words, w = i - tt * g.words;
+        s_rec[tt][w] = 0u;
+      }
+      asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+      if (q == 0) s_rec[tq][0] = (uint32_t)fp16_bits(fp16_round_pos(fmin(nrm, kFp16Max)));
+      asm volatile("" ::: "memory");
+      auto put = [&](int f, uint32_t field) {
+        const int off = field_off(g, f), wd = field_width(g, f);
+        const int wi = off >> 5, sh = off & 31;
+        atomicOr(&s_rec[tq][wi], field << sh);
+        if (sh + wd > 32) atomicOr(&s_rec[tq][wi + 1], field >> (32 - sh));
+      };
+#pragma unroll
+      for (int i = 0; i < 11; ++i) {
+        if (i < ntri) {
+          double c[3];
+#pragma unroll
+          for (int m = 0; m < 3; ++m) {
+            const int s0 = 3 * i + m;  // element slot for o = 0; o = 1, 2 read one or two on
+            c[m] = o == 0 ? y[s0] : o == 1 ? y[s0 + 1] : y[s0 + 2];
+          }
+          const double rho = sqrt(fma(c[2], c[2], fma(c[1], c[1], c[0] * c[0]))) * rn;
+          const double l1 = fabs(c[0]) + fabs(c[1]) + fabs(c[2]);
+          const double rl = 1.0 / (l1 > 0.0 ? l1 : 1.0);
+          const double p1 = c[0] * rl, p2 = c[1] * rl;
+          const bool up = c[2] * rl >= 0.0;
+          const double sx = up ? p1 : (1.0 - fabs(p2)) * sgn64(p1);
+          const double tx = up ? p2 : (1.0 - fabs(p1)) * sgn64(p2);
+          const uint32_t cs = (uint32_t)nearest_steps<BD>(s_bd, g.bd, sx);
+          const uint32_t ct = (uint32_t)nearest_steps<BD>(s_bd, g.bd, tx);
+          const uint32_t cr = (uint32_t)nearest_steps<BN>(s_bn, g.bn, rho);
+          put(J0 + i, cs | (ct << (BD > 0 ? BD : g.bd)) | (cr << (2 * (BD > 0 ? BD : g.bd))));
+        }
+      }
+      if (q == 3) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          put(g.T + r, (uint32_t)nearest_steps<BR>(s_br, g.br, y[E - 2 + r] * rn));
+      }
+      asm volatile("" ::: "memory");
+      if (act)
+        for (int w = q; w < g.words; w += 4) tp[(size_t)(kv * g.words + w) * kTile + j] = s_rec[tq][w];
+      asm volatile("" ::: "memory");  // the next plane's clear stays after these reads
+    }
   }
 }
 
@@ -987,8 +1223,16 @@ kvq_status kvq_tri_encode(const kvq_tri_desc* d, void* cache, const double* cb, 
     if (f32) hipLaunchKernelGGL((tri_encode_kernel<64, true>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
     else hipLaunchKernelGGL((tri_encode_kernel<64, false>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
   } else {
-    if (f32) hipLaunchKernelGGL((tri_encode_kernel<128, true>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
-    else hipLaunchKernelGGL((tri_encode_kernel<128, false>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    // d = 128: one wave per (batch, kv head, touched tile), sixteen token-heads per step
+    const long long tiles = (long long)(t0 + ntok - 1) / kTile - t0 / kTile + 1;
+    const long long tasks = (long long)d->batch * d->num_kv_heads * tiles;
+    if (tasks > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+    const dim3 rgrid((unsigned)((tasks + kTriRowWaves - 1) / kTriRowWaves)), rblock(kTriRowWaves * 64);
+    const bool b423 = d->bits_dir == 4 && d->bits_norm == 2 && d->bits_rest == 3;
+    if (f32 && b423) hipLaunchKernelGGL((tri_encode_rows_kernel<true, 4, 2, 3>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    else if (f32) hipLaunchKernelGGL((tri_encode_rows_kernel<true, 0, 0, 0>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    else if (b423) hipLaunchKernelGGL((tri_encode_rows_kernel<false, 4, 2, 3>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    else hipLaunchKernelGGL((tri_encode_rows_kernel<false, 0, 0, 0>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
   }
   return tri_hip(hipGetLastError());
 }
