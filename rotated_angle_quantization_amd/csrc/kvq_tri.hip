@@ -129,7 +129,7 @@ __device__ __forceinline__ float sgn32(float x) { return x < 0.f ? -1.f : 1.f; }
 
 // ------------------------------------------------------------------------------ encode
 
-// d = 64 (and the reference layout of the decisions): one wave per token-head.
+// d = 64: one wave per token-head.
 template <int D, bool F32>
 __global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cache, const void* k,
                                                          const void* v, int64_t sb, int64_t st,
