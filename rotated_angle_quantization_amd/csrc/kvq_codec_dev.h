@@ -66,10 +66,12 @@ __device__ __forceinline__ float angle_f32(float a, float b) {
 }
 
 // Angle code: nearest of n centres 2 pi c / n, i.e. floor(theta n / (2 pi) + 1/2) mod n;
-// 0 for a zero pair. The fp32 estimate theta32 (error < 8e-7 rad) gives the centre cf
-// and the distance to the nearest bin edge through the residual theta32 - cf * (2 pi / n)
-// (rounding of the bin width adds < 4e-7 rad). When that distance is below kAngleMargin
-// the pair is compared in binary64 with the edge's direction (bedge[k] = (cos, sin) of
+// 0 for a zero pair. The fp32 estimate theta32 (error < 8e-7 rad) gives the position
+// x = theta32 n / (2 pi) in bins, the centre cf = rint(x) and the residual x - cf (exact);
+// x carries the estimate's error times n / (2 pi) plus < 2^-24 n (the fp32 factor and
+// product). When |x - cf| exceeds 1/2 - kAngleMargin n / (2 pi) (the trust bound, from
+// angle_trust), i.e. the pair may lie within kAngleMargin rad of a bin edge, it is
+// compared in binary64 with the edge's direction (bedge[k] = (cos, sin) of
 // (k + 1/2) 2 pi / n): on or past the edge means the upper bin, as the floor above gives
 // at an exact half. The error bound assumes the pair rounds to normal fp32 numbers well
 // inside the range, where the reciprocal is exact to an ulp: a pair whose larger
@@ -84,27 +86,31 @@ __device__ __forceinline__ float angle_f32(float a, float b) {
 // range test is skipped (the exact branch still scales, which then changes nothing).
 constexpr float kAngleMargin = 8e-6f;  // rad, > 6x the estimate's worst-case error
 constexpr float kAngleRangeLo = 0x1p-60f, kAngleRangeHi = 0x1p60f;
+// The bound on |x - cf| below which the estimate's code is kept (n / (2 pi) in fp32 given).
+__device__ __forceinline__ float angle_trust(float bins_per_rad_f) {
+  return 0.5f - kAngleMargin * bins_per_rad_f;
+}
 template <bool kWide = true, class Edge>  // edge(k) = (cos, sin) of (k + 1/2) 2 pi / n
 __device__ __forceinline__ int angle_code(double a, double b, bool zero, int n,
-                                          float bins_per_rad_f, float bin_rad_f,
+                                          float bins_per_rad_f, float trust,
                                           const Edge& edge) {
   float af = (float)a, bf = (float)b;
-  float th = angle_f32(af, bf);
-  float cf = rintf(th * bins_per_rad_f);
-  float res = fmaf(-cf, bin_rad_f, th);  // angle from the estimated centre
+  float x = angle_f32(af, bf) * bins_per_rad_f;  // position in bins
+  float cf = rintf(x);
+  float res = x - cf;  // from the estimated centre, in bins
   int c = (int)cf;  // in [-n/2, n/2]
   const float mxf = fmaxf(fabsf(af), fabsf(bf));
   const bool in_range = !kWide || (mxf >= kAngleRangeLo && mxf <= kAngleRangeHi);
-  const bool near_edge = !(0.5f * bin_rad_f - fabsf(res) >= kAngleMargin);  // NaN: near
+  const bool near_edge = !(fabsf(res) <= trust);  // NaN: near
   if (__builtin_expect((near_edge || !in_range) && !zero, 0)) {
     if (!in_range) {
       // larger component scaled into [1/2, 1): exact in binary64
       const double sc = pow2(-__builtin_amdgcn_frexp_exp(fmax(fabs(a), fabs(b))));
       af = (float)(a * sc);
       bf = (float)(b * sc);
-      th = angle_f32(af, bf);
-      cf = rintf(th * bins_per_rad_f);
-      res = fmaf(-cf, bin_rad_f, th);
+      x = angle_f32(af, bf) * bins_per_rad_f;
+      cf = rintf(x);
+      res = x - cf;
       c = (int)cf;
     }
     const int k = res > 0.f ? c : c - 1;  // edge between centres k and k + 1
@@ -155,7 +161,7 @@ __device__ __forceinline__ int key_level(double r2, const KeyScale& k) {
     float t = __builtin_amdgcn_sqrtf((float)r2) * k.sc255 + 0.5f;
     if (kWide) t = fminf(t, 256.f);
     const float m = rintf(t);
-    rho = (int)floorf(t);
+    rho = (int)t;  // t >= 1/2: truncation is the floor
     if (__builtin_expect(fabsf(t - m) < 5e-4f, 0)) {
       const double thr = ((double)m - 0.5) * k.s_255;
       rho = r2 >= thr * thr ? (int)m : (int)m - 1;
@@ -293,7 +299,7 @@ __device__ __forceinline__ void append_token(const CodecArgs& a, const TileGeom&
     }
   }
   const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;
-  const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
+  const float ktrust = angle_trust(kbpr), vtrust = angle_trust(vbpr);
 
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
@@ -319,7 +325,7 @@ __device__ __forceinline__ void append_token(const CodecArgs& a, const TileGeom&
       const KeyScale ksc = key_scale(mx);
       const int nk = a.n_k;
       const auto edge = [&](int e) { return bin_edge(e, nk); };
-      const int c = angle_code(y0, y1, r2 == 0.0, nk, kbpr, kbin, edge);
+      const int c = angle_code(y0, y1, r2 == 0.0, nk, kbpr, ktrust, edge);
       const int rho = key_level(r2, ksc);
       // key angle words: word w of the slot's bit string holds the pairs with bits in
       // [32w, 32w + 32), at most 32 / 6 + 2 of them; lane w gathers them (every lane
@@ -350,7 +356,7 @@ __device__ __forceinline__ void append_token(const CodecArgs& a, const TileGeom&
       const ValueScale vsc = value_scale(mx, mn);
       const int nv = a.n_v;
       const auto edge = [&](int e) { return bin_edge(e, nv); };
-      const uint32_t c = (uint32_t)angle_code(y0, y1, r2 == 0.0, nv, vbpr, vbin, edge);
+      const uint32_t c = (uint32_t)angle_code(y0, y1, r2 == 0.0, nv, vbpr, vtrust, edge);
       const uint32_t rho = (uint32_t)value_level(r2, vsc);
       if (store) {
         // this slot's bits in pair i's strings; the other slots' bits are kept

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   for (int k = 0; k < PL; ++k)
     hmask[k] = (((sbits >> (2 * k)) & 1u) << 15) | (((sbits >> (2 * k + 1)) & 1u) << 31);
   const float kbpr = (float)a.k_bins_per_rad, vbpr = (float)a.v_bins_per_rad;  // n / (2 pi)
-  const float kbin = (float)(1.0 / a.k_bins_per_rad), vbin = (float)(1.0 / a.v_bins_per_rad);
+  const float ktrust = angle_trust(kbpr), vtrust = angle_trust(vbpr);
 
   // Element offset of this lane's part of the row of step jb; lanes past the range
   // read the last valid row and discard it.
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
           cc[k] = (uint8_t)angle_code<F32IN>(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_k, kbpr,
-                                             kbin, edge);
+                                             ktrust, edge);
           rr[k] = (uint8_t)key_level<F32IN>(r2[k], ksc);
         }
         if (act && q == 0) s_ks[j] = fp16_bits(ksc.s);
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
           cc[k] = (uint8_t)angle_code<F32IN>(y[2 * k], y[2 * k + 1], r2[k] == 0.0, a.n_v, vbpr,
-                                             vbin, edge);
+                                             vtrust, edge);
           rr[k] = (uint8_t)value_level(r2[k], vsc);
         }
         if (act && q == 0)

@@ -106,12 +106,14 @@ def test_angle_code_fast_path_equals_binary64(n):
     a, b = np.cos(th) * 1.7, np.sin(th) * 1.7
     t = np.arctan2(b, a) * n / (2 * np.pi)
     exact = np.mod(np.floor(t + 0.5), n).astype(np.int64)
-    bpr, bin_rad = f32(n / (2 * np.pi)), f32(2 * np.pi / n)
+    bpr = f32(n / (2 * np.pi))
+    trust = (f32(0.5) - (f32(8e-6) * bpr).astype(np.float32)).astype(np.float32)
     for v in range(3):
         est = angle_f32(a, b, c, v)
-        cf = np.rint((est * bpr).astype(np.float32))
-        res = fma32(-cf, np.full_like(cf, bin_rad), est)
-        trusted = (f32(0.5) * bin_rad - np.abs(res)) >= f32(8e-6)
+        x = (est * bpr).astype(np.float32)  # position in bins
+        cf = np.rint(x)
+        res = (x - cf).astype(np.float32)
+        trusted = np.abs(res) <= trust
         code = np.mod(cf.astype(np.int64), n)
         assert trusted.mean() > 0.95
         bad = trusted & (code != exact)
