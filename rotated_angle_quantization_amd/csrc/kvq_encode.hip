@@ -42,14 +42,6 @@ __device__ __forceinline__ bool sign_neg(const SignMask& m, int e) {
   return (m.w[e >> 6] >> (e & 63)) & 1ull;
 }
 
-// Row-pair butterfly of two doubles x, y held by every lane, between the lanes of rows
-// that differ in bit 0 of the row index (ROWS32 false: v_permlane16_swap exchanges odd
-// rows of its first operand with even rows of its second) or in bit 1 (ROWS32 true:
-// v_permlane32_swap exchanges lanes 32-63 of its first operand with lanes 0-31 of its
-// second). After the swap the lower lane holds (own x, partner's x) and the upper lane
-// (partner's y, own y), both as (value of the lower lane, value of the upper lane), so
-// every lane forms sum and difference in the same way: the lower lane's outputs are
-// those of x's butterfly, the upper lane's those of y's.
 // Maximum or minimum of x over the four rows' lanes at the same row position (the four
 // quarters of a token), by lane permutes.
 __device__ __forceinline__ double rows_max(double x) {
@@ -61,6 +53,14 @@ __device__ __forceinline__ double rows_min(double x) {
   return fmin(x, shfl_xor_f64(x, 32));
 }
 
+// Row-pair butterfly of two doubles x, y held by every lane, between the lanes of rows
+// that differ in bit 0 of the row index (ROWS32 false: v_permlane16_swap exchanges odd
+// rows of its first operand with even rows of its second) or in bit 1 (ROWS32 true:
+// v_permlane32_swap exchanges lanes 32-63 of its first operand with lanes 0-31 of its
+// second). After the swap the lower lane holds (own x, partner's x) and the upper lane
+// (partner's y, own y), both as (value of the lower lane, value of the upper lane), so
+// every lane forms sum and difference in the same way: the lower lane's outputs are
+// those of x's butterfly, the upper lane's those of y's.
 template <bool ROWS32>
 __device__ __forceinline__ void row_butterfly(double& x, double& y) {
   const uint64_t a = (uint64_t)__double_as_longlong(x), b = (uint64_t)__double_as_longlong(y);
@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   const int j_lo = max(a.t0 - tok_base, 0);
   const int j_hi = toff >= 0 ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
 
-  // Lane q of a token's quad owns the 8-element chunks m*4 + q (elements
+  // The token's lane in row q owns the 8-element chunks m*4 + q (elements
   // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
-  // element strides 1, 2, 4 and 32, 64; strides 8 and 16 are the quad exchanges. Local
+  // element strides 1, 2, 4 and 32, 64; strides 8 and 16 are the row swaps. Local
   // bit 8m + r of sbits is the sign of element 32m + 8q + r; for fp16 input the per-pair
   // xor masks flip the fp16 sign bits (bits 15 and 31 of a packed pair).
   uint32_t sbits = 0;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
         // a cache hit), and a conditional load would make the buffer a copy
         load_raw(kv, jb + TPS);
       }
-      // Walsh-Hadamard: in-lane stages, then lanes xor 1 and xor 2 (natural order)
+      // Walsh-Hadamard: in-lane stages, then the two row stages
 #pragma unroll
       for (int hs = 1; hs < E; hs <<= 1) {
 #pragma unroll
