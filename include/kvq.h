@@ -58,8 +58,8 @@ typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
  * One layer's compressed cache. Plain data: read during a call, never retained.
  *  head_dim     d; 64 or 128 (a power of two; the pairing needs d even).
  *  num_kv_heads Hkv >= 1.  batch B >= 1.
- *  capacity     token slots per (batch, kv head), >= 1; rounded up to whole tiles
- *               of 64 slots in the byte layout.
+ *  capacity     token slots per (batch, kv head), in [1, 2^31 - 64]; rounded up to
+ *               whole tiles of 64 slots in the byte layout.
  *  n_bins_k/v   angle bins n for K and V, in [2, 256]; each code takes ceil(log2 n)
  *               bits (per-layer early boost = a different pair per layer).
  *  layer, seed  select the sign diagonal (see kvq_layer_signs).
@@ -430,7 +430,7 @@ uint32_t kvq_attn_num_splits(const kvq_layer_desc* desc, uint32_t num_q_heads,
 /*
  * One triplet-coded layer.
  *  head_dim           64 or 128.
- *  num_kv_heads, batch, capacity   as in kvq_layer_desc.
+ *  num_kv_heads, batch, capacity   as in kvq_layer_desc (capacity <= 2^31 - 64).
  *  bits_dir           bits of each of the two square coordinates, 1..6.
  *  bits_norm          bits of the triplet norm, 1..6.
  *  bits_rest          bits of each leftover coordinate, 1..8.

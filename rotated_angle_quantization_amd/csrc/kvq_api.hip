@@ -39,7 +39,9 @@ bool desc_ok(const kvq_layer_desc* d) {
   if (!d) return false;
   if (d->reserved != 0) return false;
   if (d->head_dim < 64 || d->head_dim > 256 || !is_pow2(d->head_dim)) return false;
-  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0) return false;
+  // token positions and tile counts are kept in int
+  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0 || d->capacity > kMaxCapacity)
+    return false;
   if (d->n_bins_k < 2 || d->n_bins_k > 256 || d->n_bins_v < 2 || d->n_bins_v > 256)
     return false;
   return true;

@@ -10,6 +10,8 @@
 namespace kvq {
 
 constexpr int kTile = KVQ_TILE_TOKENS;  // token slots per tile
+// Largest capacity a descriptor may state: slot and tile arithmetic is done in int.
+constexpr uint32_t kMaxCapacity = 0x7FFFFFFFu - (kTile - 1);
 constexpr int kMaxHeadDim = 128;
 
 // Angle code width for n bins: ceil(log2 n).

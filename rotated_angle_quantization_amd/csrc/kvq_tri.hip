@@ -1063,7 +1063,9 @@ struct LloydMax {
 bool tri_desc_ok(const kvq_tri_desc* d) {
   if (!d) return false;
   if (d->head_dim != 64 && d->head_dim != 128) return false;
-  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0) return false;
+  // token positions and tile counts are kept in int
+  if (d->num_kv_heads == 0 || d->batch == 0 || d->capacity == 0 || d->capacity > kMaxCapacity)
+    return false;
   if (d->bits_dir < 1 || d->bits_dir > 6 || d->bits_norm < 1 || d->bits_norm > 6) return false;
   if (d->bits_rest < 1 || d->bits_rest > 8) return false;
   return true;

@@ -54,7 +54,7 @@ def test_invalid_descriptors_size_zero():
     assert kvq.tile_bytes(128, 1, 64) == 0
     assert kvq.tile_bytes(128, 128, 257) == 0
     for bad in (dict(head_dim=48), dict(num_kv_heads=0), dict(batch=0), dict(capacity=0),
-                dict(n_bins_k=300), dict(reserved=1)):
+                dict(capacity=2**31 - 63), dict(n_bins_k=300), dict(reserved=1)):
         desc = kvq.make_desc(128, 8, 1, 64, 128, 64)
         for k, v in bad.items():
             setattr(desc, k, v)

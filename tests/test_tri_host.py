@@ -68,7 +68,8 @@ def test_invalid_descriptors_size_zero():
     bad = [kvq.make_tri_desc(96, 1, 1, 64, 2, 2, 2), kvq.make_tri_desc(128, 1, 1, 64, 0, 2, 2),
            kvq.make_tri_desc(128, 1, 1, 64, 7, 2, 2), kvq.make_tri_desc(128, 1, 1, 64, 2, 7, 2),
            kvq.make_tri_desc(128, 1, 1, 64, 2, 2, 9), kvq.make_tri_desc(128, 0, 1, 64, 2, 2, 2),
-           kvq.make_tri_desc(128, 1, 0, 64, 2, 2, 2), kvq.make_tri_desc(128, 1, 1, 0, 2, 2, 2)]
+           kvq.make_tri_desc(128, 1, 0, 64, 2, 2, 2), kvq.make_tri_desc(128, 1, 1, 0, 2, 2, 2),
+           kvq.make_tri_desc(128, 1, 1, 2**31 - 63, 2, 2, 2)]
     for desc in bad:
         assert kvq.tri_cache_bytes(desc) == 0, desc
         assert kvq.tri_record_words(desc) == 0, desc
