@@ -417,27 +417,38 @@ def stream_probe(kvq, caches, dev, reps=3):
     """Read-only streaming probe (kvq_probe_read) over the same cache buffers the
     attention sweep reads, one launch per layer, HIP events around the sweep: the
     bandwidth a plain read of this memory reaches on this GPU (context for the
-    roofline, no codec work)."""
+    roofline, no codec work). The sweep is also timed over the first quarter of each
+    buffer: the two sweep times give the probe's own streaming rate (bytes over the
+    difference in time) and its fixed time per launch, as `launch_breakdown` does for
+    attention."""
     import torch
 
     sink = torch.zeros(256, dtype=torch.uint8, device=dev)
-    nbytes = sum(c.numel() for c in caches)
 
-    def sweep():
-        for c in caches:
-            kvq.probe_read(c, sink)
-
-    sweep()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    def timed(bufs):
+        def sweep():
+            for c in bufs:
+                kvq.probe_read(c, sink)
         sweep()
-    e1.record()
-    torch.cuda.synchronize()
-    s = e0.elapsed_time(e1) * 1e-3 / reps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sweep()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    quarter = [c[: (c.numel() // 4) // 16 * 16] for c in caches]
+    nbytes = sum(c.numel() for c in caches)
+    qbytes = sum(c.numel() for c in quarter)
+    s, sq = timed(caches), timed(quarter)
+    stream = (nbytes - qbytes) / (s - sq) if s > sq else float("nan")
     return {"GBps": round(nbytes / s / 1e9, 2), "bytes_per_sweep": nbytes,
-            "launches_per_sweep": len(caches), "frac_of_peak": round(nbytes / s / 1e9 / HBM_PEAK_GBPS, 4)}
+            "launches_per_sweep": len(caches), "frac_of_peak": round(nbytes / s / 1e9 / HBM_PEAK_GBPS, 4),
+            "quarter_GBps": round(qbytes / sq / 1e9, 2),
+            "streaming_GBps": round(stream / 1e9, 1),
+            "fixed_us_per_launch": round((s - nbytes / stream) / len(caches) * 1e6, 2)}
 
 
 TRIPLET_BITS = (4, 2, 3)  # (bits per square coordinate, per triplet norm, per leftover)

@@ -512,7 +512,7 @@ kvq_status kvq_tri_attn_decode(const kvq_tri_desc* desc, const void* cache,
  * codec work): reads `bytes` of device memory at `buf` once with 16-byte loads, as a
  * plain streaming kernel would, and returns. `sink` is a device buffer of at least 256
  * bytes that the kernel may write to (in practice it never does: a store happens only
- * when the XOR of everything read equals one fixed 32-bit constant). buf 16-byte
+ * when the XOR of the words one lane read equals one fixed 32-bit constant). buf 16-byte
  * aligned, bytes a multiple of 16 (0 enqueues nothing). Errors: INVALID_ARGUMENT, HIP.
  * =================================================================================== */
 kvq_status kvq_probe_read(const void* buf, size_t bytes, void* sink, void* hip_stream);
