@@ -11,16 +11,12 @@
 // declarations in kvq.h.
 //
 // Kernels (the lane maps follow the data):
-//   encode     d = 128: a wave per (batch, kv head, 64-token tile), sixteen token-heads
-//              per step with a quarter vector per lane, the transform's last two stages
-//              as row swaps; each lane then codes the triplets starting in its 32
-//              elements, in binary64, with branch-free searches of the boundaries in LDS
-//              (compiled for the 4/2/3 allocation, generic otherwise), and ORs the
-//              fields into the tokens' records in LDS. d = 64: a wave per token-head;
-//              lane i holds elements 2i, 2i+1 through the transform; the unit vector is
-//              staged in LDS and lane j reads triplet j (or leftover coordinate j - T),
-//              takes its decisions against the boundaries in LDS and ORs its field into
-//              the record's words in LDS; lane w stores word w.
+//   encode     a wave per (batch, kv head, 64-token tile), sixteen token-heads per step
+//              with a quarter vector per lane through the binary64 transform (its
+//              cross-lane stages as row swaps); each lane then codes the triplets starting
+//              in its block of d/4 consecutive elements, in binary64, with branch-free
+//              searches of the boundaries in LDS (compiled for the 4/2/3 allocation,
+//              generic otherwise), and ORs the fields into the tokens' records in LDS.
 //   decode     lane j rebuilds its triplet (or leftover) in fp32 from the levels, the
 //              elements are permuted back to two per lane for the inverse transform.
 //   attention  split kernel (grid: splits x batch * kv heads, four waves, a wave per
@@ -91,18 +87,8 @@ struct TriArgs {
 
 __device__ inline int cb_bounds_off(const TriGeom& g) { return g.nd + g.nn + g.nr; }
 
-// Number of boundaries below x (the nearest level; the lower one at an exact midpoint).
-__device__ __forceinline__ int nearest(const double* bounds, int n_levels, double x) {
-  int lo = 0, hi = n_levels - 1;  // count in [lo, hi]
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (bounds[mid] < x) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
-// The same count for 2^bits levels without a data-dependent loop: steps of
+// Number of boundaries below x (the nearest level; the lower one at an exact midpoint),
+// for 2^bits levels, without a data-dependent loop: steps of
 // 2^(bits-1), .., 1, each taken when the boundary it lands on is still below x (the
 // index never passes 2^bits - 1, the last boundary's count). Straight-line code, so the
 // searches of different values overlap their LDS reads. BITS > 0 fixes the width at
@@ -129,125 +115,20 @@ __device__ __forceinline__ float sgn32(float x) { return x < 0.f ? -1.f : 1.f; }
 
 // ------------------------------------------------------------------------------ encode
 
-// d = 64: one wave per token-head.
-template <int D, bool F32>
-__global__ __launch_bounds__(256) void tri_encode_kernel(TriArgs a, uint8_t* cache, const void* k,
-                                                         const void* v, int64_t sb, int64_t st,
-                                                         int64_t sh) {
-  constexpr int P = D / 2;
-  const TriGeom& g = a.g;
-  __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
-  __shared__ uint32_t s_rec[4][kTriMaxRecordWords];  // a record being assembled, per wave
-  __shared__ double s_u[4][D];                         // a unit vector being split, per wave
-  const int bo = cb_bounds_off(g);
-  for (int i = threadIdx.x; i < g.nd - 1; i += 256) s_bd[i] = a.cb[bo + i];
-  for (int i = threadIdx.x; i < g.nn - 1; i += 256) s_bn[i] = a.cb[bo + g.nd - 1 + i];
-  for (int i = threadIdx.x; i < g.nr - 1; i += 256) s_br[i] = a.cb[bo + g.nd - 1 + g.nn - 1 + i];
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  // token-head index in 32 bits (the host keeps B * ntok * Hkv below 2^32)
-  const unsigned item = blockIdx.x * 4u + (unsigned)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const unsigned total = (unsigned)a.batch * (unsigned)a.ntok * (unsigned)a.hkv;
-  if (item >= total) return;
-  const int h = (int)(item % (unsigned)a.hkv);
-  const unsigned bj = item / (unsigned)a.hkv;
-  const int j = (int)(bj % (unsigned)a.ntok), b = (int)(bj / (unsigned)a.ntok);
-  const int slot = a.t0 + j, tile = slot / kTile, t = slot % kTile;
-  const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
-  uint32_t* tp = reinterpret_cast<uint32_t*>(
-      cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * tile_bytes);
-  const int i = lane & (P - 1);  // pair held by this lane
-  const int e0 = 2 * i;
-  const int nf = g.T + g.R;
-
-#pragma unroll 1
-  for (int kv = 0; kv < 2; ++kv) {
-    const char* src = static_cast<const char*>(kv == 0 ? k : v) +
-                      ((size_t)b * sb + (size_t)j * st + (size_t)h * sh) * (F32 ? 4 : 2);
-    double y0, y1;
-    if (F32) {
-      const float2 x = reinterpret_cast<const float2*>(src)[i];
-      y0 = x.x;
-      y1 = x.y;
-    } else {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(src)[i];
-      y0 = (double)__half2float(__ushort_as_half((uint16_t)(w & 0xFFFFu)));
-      y1 = (double)__half2float(__ushort_as_half((uint16_t)(w >> 16)));
-    }
-    if (sign_neg(a.sign, e0)) y0 = -y0;
-    if (sign_neg(a.sign, e0 + 1)) y1 = -y1;
-    {
-      const double u = y0, w = y1;
-      y0 = u + w;
-      y1 = u - w;
-    }
-#pragma unroll
-    for (int m = 1; m < P; m <<= 1) lane_stage(y0, y1, lane, m);
-    y0 *= a.inv_sqrt_d;
-    y1 *= a.inv_sqrt_d;
-    // vector norm (lanes of one half hold every pair once)
-    double n2 = fma(y1, y1, y0 * y0);
-#pragma unroll
-    for (int m = 1; m < P; m <<= 1) n2 += shfl_xor_f64(n2, m);
-    const double nrm = sqrt(n2);
-    const double u0 = nrm > 0.0 ? y0 / nrm : 0.0, u1 = nrm > 0.0 ? y1 / nrm : 0.0;
-    // lane f < T gathers triplet f, lane T + r the leftover coordinate 3T + r
-    const int f = lane < nf ? lane : 0;
-    const int base = f < g.T ? 3 * f : 3 * g.T + (f - g.T);
-    // the unit vector staged in the wave's LDS row (lane i writes elements 2i, 2i + 1),
-    // then each lane reads the three elements of its triplet
-    double* su = s_u[threadIdx.x >> 6];
-    if (lane < P) reinterpret_cast<double2*>(su)[i] = make_double2(u0, u1);
-    asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
-    double c[3];
-#pragma unroll
-    for (int m = 0; m < 3; ++m) c[m] = su[min(base + m, D - 1)];
-    asm volatile("" ::: "memory");  // the next plane's writes stay after these reads
-    uint32_t field = 0;
-    if (f < g.T) {
-      const double rho = sqrt(fma(c[2], c[2], fma(c[1], c[1], c[0] * c[0])));
-      const double l1 = fabs(c[0]) + fabs(c[1]) + fabs(c[2]);
-      const double dv = l1 > 0.0 ? l1 : 1.0;
-      const double p1 = c[0] / dv, p2 = c[1] / dv, p3 = c[2] / dv;
-      const double s = p3 >= 0.0 ? p1 : (1.0 - fabs(p2)) * sgn64(p1);
-      const double tt = p3 >= 0.0 ? p2 : (1.0 - fabs(p1)) * sgn64(p2);
-      const uint32_t cs = (uint32_t)nearest(s_bd, g.nd, s);
-      const uint32_t ct = (uint32_t)nearest(s_bd, g.nd, tt);
-      const uint32_t cr = (uint32_t)nearest(s_bn, g.nn, rho);
-      field = cs | (ct << g.bd) | (cr << (2 * g.bd));
-    } else {
-      field = (uint32_t)nearest(s_br, g.nr, c[0]);
-    }
-    // record words assembled in the wave's LDS row: lane w < words clears word w (word 0
-    // starts as the fp16 bits of N), then each field ORs itself into the one or two words
-    // it overlaps. A wave's LDS operations complete in order, so only the compiler has
-    // to keep the clear, the ORs and the read-back in order.
-    uint32_t* rec = s_rec[threadIdx.x >> 6];
-    if (lane < g.words)
-      rec[lane] = lane == 0 ? (uint32_t)fp16_bits(fp16_round_pos(fmin(nrm, kFp16Max))) : 0u;
-    asm volatile("" ::: "memory");
-    if (lane < nf) {
-      const int off = field_off(g, f), wd = field_width(g, f);
-      const int wi = off >> 5, sh = off & 31;
-      atomicOr(&rec[wi], field << sh);
-      if (sh + wd > 32) atomicOr(&rec[wi + 1], field >> (32 - sh));
-    }
-    asm volatile("" ::: "memory");
-    if (lane < g.words) tp[(size_t)(kv * g.words + lane) * kTile + t] = rec[lane];
-    asm volatile("" ::: "memory");  // the next plane's clear stays after this read
-  }
-}
-
-// Encode at d = 128, sixteen token-heads per wave. One wave per (batch, kv head, tile of
-// 64 tokens), coded in steps of 16 tokens: the token is the lane's position in its
-// 16-lane row and the row is the quarter of the vector. The binary64 transform runs as in
-// the angle encoder: in-lane butterflies for element strides 1, 2, 4, 32 and 64, then the
-// strides 8 and 16 as row swaps (v_permlane16_swap, v_permlane32_swap) on two of the
-// lane's values at once, after which lane row q holds elements 32 q .. 32 q + 31 of its
-// token. Triplet j (elements 3j .. 3j + 2) is coded by the row holding its first element:
-// rows 0 and 1 code 11 triplets each (their last one takes one or two elements of the next
-// row), rows 2 and 3 ten, and row 3 also the two leftover coordinates. The decisions are
+// Encode, sixteen token-heads per wave. One wave per (batch, kv head, tile of 64 tokens),
+// coded in steps of 16 tokens: the token is the lane's position in its 16-lane row and
+// the row is the quarter of the vector. The binary64 transform runs as in the angle
+// encoder: in-lane butterflies for element strides 1, 2, 4 and 32 (and 64), then the
+// stride 8 as a row swap (v_permlane16_swap) on two of the lane's values at once.
+// d = 128: the stride 16 is a row swap too (v_permlane32_swap), after which row q holds
+// elements 32 q .. 32 q + 31 of its token; block q is row q. d = 64: after the stride-8
+// swap, row (q1, q0) already holds elements 32 q0 + 16 q1 .. + 15 (block 2 q0 + q1), and
+// the stride 16 is a plain exchange between rows q1 = 0 and 1 (a swap of each value with
+// a copy of itself, then a signed add) that keeps those sets. Triplet j (elements
+// 3j .. 3j + 2) is coded by the lane whose block holds its first element; a block's last
+// triplet may take one or two elements of the next block (through a lane permute), and
+// the last block also codes the leftover coordinates. Triplets per block: 11, 11, 10, 10
+// at d = 128; 6, 5, 5, 5 at d = 64. The decisions are
 // those of tri_encode_kernel, in binary64: triplet norm rho = |c| / N, the octahedral
 // point from c / |c|_1 (the same point as from u = y / N: the map is scale-free), the
 // leftover coordinates y / N; each is located among the quantiser's boundaries in LDS.
@@ -280,10 +161,15 @@ __device__ __forceinline__ void tri_row_butterfly(double& x, double& y) {
 
 // BD, BN, BR: the bit allocation fixed at compile time (the searches' step counts), or 0
 // for the widths of the descriptor.
-template <bool F32, int BD, int BN, int BR>
+// spw: 16-token steps per wave, 4 (a whole tile) or 1 (a quarter tile each, for launches
+// with too few tiles to fill the GPU).
+template <int D, bool F32, int BD, int BN, int BR>
 __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
-    TriArgs a, uint8_t* cache, const void* k, const void* v, int64_t sb, int64_t st, int64_t sh) {
-  constexpr int D = 128, E = 32, PL = 16, TPS = 16;
+    TriArgs a, uint8_t* cache, const void* k, const void* v, int64_t sb, int64_t st, int64_t sh,
+    int spw) {
+  constexpr int E = D / 4, PL = E / 2, TPS = 16;
+  constexpr int T = D / 3, R = D - 3 * T;
+  constexpr int MAXT = D == 128 ? 11 : 6;  // triplets of the fullest block
   const TriGeom& g = a.g;
   __shared__ double s_bd[kTriMaxLevelsDir], s_bn[kTriMaxLevelsNorm], s_br[kTriMaxLevelsRest];
   __shared__ uint32_t s_rec_all[kTriRowWaves][TPS][kTriMaxRecordWords + 1];
@@ -299,11 +185,16 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
   uint32_t(*s_rec)[kTriMaxRecordWords + 1] = s_rec_all[wave];
   const int tile_lo = a.t0 / kTile;
   const int tiles_touched = (a.t0 + a.ntok - 1) / kTile - tile_lo + 1;
+  const int parts = 4 / spw;  // waves per tile
   const int task = blockIdx.x * kTriRowWaves + wave;
-  if (task >= a.batch * a.hkv * tiles_touched) return;  // no barrier follows
-  const int bh = task / tiles_touched, b = bh / a.hkv, h = bh % a.hkv;
-  const int tile = tile_lo + task % tiles_touched, tok_base = tile * kTile;
-  const int j_lo = max(a.t0 - tok_base, 0), j_hi = min(a.t0 + a.ntok - tok_base, kTile);
+  if (task >= a.batch * a.hkv * tiles_touched * parts) return;  // no barrier follows
+  const int tt_task = task / parts, part = task % parts;
+  const int bh = tt_task / tiles_touched, b = bh / a.hkv, h = bh % a.hkv;
+  const int tile = tile_lo + tt_task % tiles_touched, tok_base = tile * kTile;
+  // this wave's slots of the tile: the part's steps, within the encoded range
+  const int j_lo = max(max(a.t0 - tok_base, 0), part * spw * TPS);
+  const int j_hi = min(min(a.t0 + a.ntok - tok_base, kTile), (part + 1) * spw * TPS);
+  if (j_lo >= j_hi) return;
   const size_t tile_bytes = (size_t)2 * g.words * kTile * 4;
   uint32_t* tp = reinterpret_cast<uint32_t*>(
       cache + ((size_t)(b * a.hkv + h) * a.tiles_per_seq + tile) * tile_bytes);
@@ -320,10 +211,15 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
   for (int kk = 0; kk < PL; ++kk)
     hmask[kk] = (((sbits >> (2 * kk)) & 1u) << 15) | (((sbits >> (2 * kk + 1)) & 1u) << 31);
 
-  // this row's triplets: the first is J0, its first element is local slot o
-  const int J0 = q == 0 ? 0 : q == 1 ? 11 : q == 2 ? 22 : 32;
-  const int ntri = q < 2 ? 11 : 10;
-  const int o = 3 * J0 - 32 * q;  // 0, 1, 2, 0
+  // this lane's block of E consecutive elements, its triplets (the first is J0, whose
+  // first element is local slot o) and the row holding the next block
+  const int blk = D == 128 ? q : 2 * (q & 1) + (q >> 1);
+  const int J0 = D == 128 ? (blk == 0 ? 0 : blk == 1 ? 11 : blk == 2 ? 22 : 32)
+                          : (blk == 0 ? 0 : blk == 1 ? 6 : blk == 2 ? 11 : 16);
+  const int ntri = D == 128 ? (blk < 2 ? 11 : 10) : (blk == 0 ? 6 : 5);
+  const int o = 3 * J0 - E * blk;  // d = 128: 0, 1, 2, 0; d = 64: 0, 2, 1, 0
+  const int q_next = D == 128 ? ((q + 1) & 3) : (blk == 0 ? 2 : 1);  // blocks 2, 3 need none
+  const double qsgn = (q >> 1) ? -1.0 : 1.0;  // d = 64, stride 16: upper rows keep u - v
 
   auto row_offset = [&](int jb) {
     const int jr = min(jb + tq, j_hi - 1);
@@ -347,7 +243,7 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
     const int64_t row_off = row_offset(jb);
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {  // unrolled: raw[kv] stays in registers
-      double y[E + 3];
+      double y[E + 5];
       if (F32) {
         const float* p = static_cast<const float*>(kv == 0 ? k : v) + row_off;
 #pragma unroll
@@ -379,10 +275,25 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
 #pragma unroll
       for (int i = 0; i < E; ++i)
         if (!(i & 8)) tri_row_butterfly<false>(y[i], y[i + 8]);
+      if constexpr (D == 128) {
 #pragma unroll
-      for (int i = 0; i < E; ++i)
-        if (!(i & 16)) tri_row_butterfly<true>(y[i], y[i + 16]);
-      // slot s now holds element 32 q + s
+        for (int i = 0; i < E; ++i)
+          if (!(i & 16)) tri_row_butterfly<true>(y[i], y[i + 16]);
+      } else {
+        // each value against its partner in the other half of the wave: the swap leaves
+        // (lower lane's value, upper lane's value) in every lane
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const uint64_t u = (uint64_t)__double_as_longlong(y[i]);
+          const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+          const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                           false, false);
+          const double lw = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+          const double up = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+          y[i] = fma(up, qsgn, lw);
+        }
+      }
+      // slot s now holds element E blk + s
       double n2 = 0.0;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
@@ -393,10 +304,11 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
       n2 += shfl_xor_f64(n2, 32);
       const double nrm = sqrt(n2);
       const double rn = nrm > 0.0 ? 1.0 / nrm : 0.0;
-      // the next row's first two elements (for the triplets that straddle rows)
-      y[E] = __shfl(y[0], (lane + 16) & 63, 64);
-      y[E + 1] = __shfl(y[1], (lane + 16) & 63, 64);
-      y[E + 2] = 0.0;
+      // the next block's first two elements (for the triplets that straddle blocks)
+      y[E] = __shfl(y[0], tq + 16 * q_next, 64);
+      y[E + 1] = __shfl(y[1], tq + 16 * q_next, 64);
+#pragma unroll
+      for (int i = E + 2; i < E + 5; ++i) y[i] = 0.0;
 
       // the records of this step's tokens: word 0 starts as the fp16 bits of N
       for (int i = lane; i < TPS * g.words; i += 64) {
@@ -413,7 +325,7 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
         if (sh + wd > 32) atomicOr(&s_rec[tq][wi + 1], field >> (32 - sh));
       };
 #pragma unroll
-      for (int i = 0; i < 11; ++i) {
+      for (int i = 0; i < MAXT; ++i) {
         if (i < ntri) {
           double c[3];
 #pragma unroll
@@ -434,10 +346,10 @@ __global__ __launch_bounds__(kTriRowWaves * 64) void tri_encode_rows_kernel(
           put(J0 + i, cs | (ct << (BD > 0 ? BD : g.bd)) | (cr << (2 * (BD > 0 ? BD : g.bd))));
         }
       }
-      if (q == 3) {
+      if (blk == 3) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-          put(g.T + r, (uint32_t)nearest_steps<BR>(s_br, g.br, y[E - 2 + r] * rn));
+        for (int r = 0; r < R; ++r)
+          put(T + r, (uint32_t)nearest_steps<BR>(s_br, g.br, y[E - R + r] * rn));
       }
       asm volatile("" ::: "memory");
       if (act)
@@ -1216,26 +1128,33 @@ kvq_status kvq_tri_encode(const kvq_tri_desc* d, void* cache, const double* cb, 
   if (((uintptr_t)k % (2 * esz)) || ((uintptr_t)v % (2 * esz))) return KVQ_ERR_INVALID_ARGUMENT;
   if ((sb & 1) || (st & 1) || (sh & 1) || sb < 0 || st < 0 || sh < 0) return KVQ_ERR_INVALID_ARGUMENT;
   const TriArgs a = tri_args(d, cb, t0, ntok);
-  const long long items = (long long)d->batch * ntok * d->num_kv_heads;
-  if (items > 0xFFFFFF00LL) return KVQ_ERR_INVALID_ARGUMENT;
-  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  // one wave per (batch, kv head, touched tile), sixteen token-heads per step
+  const long long tiles = (long long)(t0 + ntok - 1) / kTile - t0 / kTile + 1;
+  const long long tile_tasks = (long long)d->batch * d->num_kv_heads * tiles;
+  // a whole tile per wave where there are enough tiles for 16 waves per compute unit,
+  // else a quarter tile per wave
+  const int spw = tile_tasks >= 4096 ? 4 : 1;
+  const long long tasks = tile_tasks * (4 / spw);
+  if (tasks > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
+  const dim3 rgrid((unsigned)((tasks + kTriRowWaves - 1) / kTriRowWaves)), rblock(kTriRowWaves * 64);
   hipStream_t s = (hipStream_t)stream;
   const bool f32 = in_dtype == KVQ_F32;
+  const bool b423 = d->bits_dir == 4 && d->bits_norm == 2 && d->bits_rest == 3;
+#define KVQ_TRI_ENC(DD, F, A, B, C)                                                              \
+  hipLaunchKernelGGL((tri_encode_rows_kernel<DD, F, A, B, C>), rgrid, rblock, 0, s, a,           \
+                     (uint8_t*)cache, k, v, sb, st, sh, spw)
   if (d->head_dim == 64) {
-    if (f32) hipLaunchKernelGGL((tri_encode_kernel<64, true>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
-    else hipLaunchKernelGGL((tri_encode_kernel<64, false>), grid, block, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    if (f32 && b423) KVQ_TRI_ENC(64, true, 4, 2, 3);
+    else if (f32) KVQ_TRI_ENC(64, true, 0, 0, 0);
+    else if (b423) KVQ_TRI_ENC(64, false, 4, 2, 3);
+    else KVQ_TRI_ENC(64, false, 0, 0, 0);
   } else {
-    // d = 128: one wave per (batch, kv head, touched tile), sixteen token-heads per step
-    const long long tiles = (long long)(t0 + ntok - 1) / kTile - t0 / kTile + 1;
-    const long long tasks = (long long)d->batch * d->num_kv_heads * tiles;
-    if (tasks > 0x7fffffffLL) return KVQ_ERR_INVALID_ARGUMENT;
-    const dim3 rgrid((unsigned)((tasks + kTriRowWaves - 1) / kTriRowWaves)), rblock(kTriRowWaves * 64);
-    const bool b423 = d->bits_dir == 4 && d->bits_norm == 2 && d->bits_rest == 3;
-    if (f32 && b423) hipLaunchKernelGGL((tri_encode_rows_kernel<true, 4, 2, 3>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
-    else if (f32) hipLaunchKernelGGL((tri_encode_rows_kernel<true, 0, 0, 0>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
-    else if (b423) hipLaunchKernelGGL((tri_encode_rows_kernel<false, 4, 2, 3>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
-    else hipLaunchKernelGGL((tri_encode_rows_kernel<false, 0, 0, 0>), rgrid, rblock, 0, s, a, (uint8_t*)cache, k, v, sb, st, sh);
+    if (f32 && b423) KVQ_TRI_ENC(128, true, 4, 2, 3);
+    else if (f32) KVQ_TRI_ENC(128, true, 0, 0, 0);
+    else if (b423) KVQ_TRI_ENC(128, false, 4, 2, 3);
+    else KVQ_TRI_ENC(128, false, 0, 0, 0);
   }
+#undef KVQ_TRI_ENC
   return tri_hip(hipGetLastError());
 }
 
