@@ -14,10 +14,11 @@
 // binary64. So the codes match a float64 reference except where a float64 angle
 // itself sits within rounding distance of a bin boundary.
 //
-// Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens); a lane owns a
-// quarter of one vector (d/4 elements in interleaved 8-element chunks), so 16 tokens
-// are coded per step: the token is the lane's position in its 16-lane row and the
-// quarter is the row.
+// Work split: one 64-lane wave per (batch, kv head, tile of 64 tokens), or, for launches
+// with fewer tiles than fill the GPU, one workgroup per tile (a 16-token step per wave);
+// a lane owns a quarter of one vector (d/4 elements in interleaved 8-element chunks), so
+// 16 tokens are coded per step: the token is the lane's position in its 16-lane row and
+// the quarter is the row.
 // The transform's first log2(d/4) stages are in-lane; the last two pair the rows
 // (quarter bit 0: rows 0 <-> 1 and 2 <-> 3; quarter bit 1: rows 0, 1 <-> 2, 3). Each of
 // those is taken on two of the lane's values at once with gfx950's row swaps
@@ -143,12 +144,17 @@ __device__ __forceinline__ uint32_t nibbles8(uint32_t lo, uint32_t hi) {
 
 constexpr int kEncWaves = 4;  // waves (tiles) per workgroup, sharing the edge tables
 
+// wg_tile = 0: each wave codes a tile of its own (four per workgroup). wg_tile = 1 (for
+// launches with too few tiles to fill the GPU): the four waves of a workgroup code one
+// tile together, a 16-token step each, staging into one shared set of code rows, and
+// wave 0 packs the tile after the barrier.
 template <int D, bool F32IN>
 __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, TileGeom g,
                                                     uint8_t* __restrict__ cache,
                                                     const void* __restrict__ kin,
                                                     const void* __restrict__ vin,
-                                                    int64_t sb, int64_t st, int64_t sh) {
+                                                    int64_t sb, int64_t st, int64_t sh,
+                                                    int wg_tile) {
   constexpr int P = D / 2;    // pairs per vector
   constexpr int E = D / 4;    // elements per lane
   constexpr int PL = E / 2;   // pairs per lane
@@ -167,14 +173,16 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
     s_vedge[k] = bin_edge(k, a.n_v);
   }
   __syncthreads();
-  uint8_t(*s_kc)[kRow] = s_code[wave][0];
-  uint8_t(*s_kr)[kRow] = s_code[wave][1];
-  uint8_t(*s_vc)[kRow] = s_code[wave][2];
-  uint8_t(*s_vr)[kRow] = s_code[wave][3];
-  uint16_t* s_ks = s_ks_all[wave];
-  uint32_t* s_vp = s_vp_all[wave];
-  // one tile per wave; waves past the last tile do no work (but take the barrier)
-  const int task = blockIdx.x * kEncWaves + wave;
+  const int slot = wg_tile ? 0 : wave;  // the staging rows of this wave's tile
+  uint8_t(*s_kc)[kRow] = s_code[slot][0];
+  uint8_t(*s_kr)[kRow] = s_code[slot][1];
+  uint8_t(*s_vc)[kRow] = s_code[slot][2];
+  uint8_t(*s_vr)[kRow] = s_code[slot][3];
+  uint16_t* s_ks = s_ks_all[slot];
+  uint32_t* s_vp = s_vp_all[slot];
+  // one tile per wave (or per workgroup); waves past the last tile do no work (but take
+  // the barrier)
+  const int task = wg_tile ? (int)blockIdx.x : (int)blockIdx.x * kEncWaves + wave;
   const int ntasks = a.batch * a.hkv * a.tiles_touched;
   const bool live = task < ntasks;
   const int tile_rel = task % a.tiles_touched;
@@ -186,6 +194,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   const long long toff = live ? tile_offset(a.pg, b, h, a.hkv, a.tiles_per_seq, tile, g.bytes) : -1;
   const int j_lo = max(a.t0 - tok_base, 0);
   const int j_hi = toff >= 0 ? min(a.t0 + a.ntok - tok_base, kTile) : j_lo;
+  // the slots this wave codes: the tile's range, or its step of it (possibly none)
+  const int js = wg_tile ? max(j_lo, TPS * wave) : j_lo;
+  const int je = wg_tile ? max(js, min(j_hi, TPS * wave + TPS)) : j_hi;
 
   // The token's lane in row q owns the 8-element chunks m*4 + q (elements
   // 32m + 8q + r, r < 8) in local slots 8m + r: the transform's in-lane stages are the
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
   // Element offset of this lane's part of the row of step jb; lanes past the range
   // read the last valid row and discard it.
   auto row_offset = [&](int jb) {
-    const int jr = min(jb + tq, j_hi - 1);
+    const int jr = min(jb + tq, je - 1);
     return (int64_t)b * sb + (int64_t)(tok_base + jr - a.t0) * st + (int64_t)h * sh + 8 * q;
   };
   // fp16 input: one buffer per plane; a plane's words of the next step are requested as
@@ -218,14 +229,14 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
 #pragma unroll
     for (int k = 0; k < PL; ++k) raw[kv][k] = p[16 * (k >> 2) + (k & 3)];
   };
-  if (!F32IN && j_lo < j_hi) {
-    load_raw(0, j_lo);
-    load_raw(1, j_lo);
+  if (!F32IN && js < je) {
+    load_raw(0, js);
+    load_raw(1, js);
   }
 
-  for (int jb = j_lo; jb < j_hi; jb += TPS) {
+  for (int jb = js; jb < je; jb += TPS) {
     const int j = jb + tq;
-    const bool act = j < j_hi;
+    const bool act = j < je;
     const int64_t row_off = row_offset(jb);
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
@@ -332,6 +343,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(CodecArgs a, Til
     }
   }
   __syncthreads();
+  if (wg_tile && wave != 0) return;  // no barrier follows
 
   uint8_t* tp = cache + (toff >= 0 ? toff : 0);
 
@@ -469,15 +481,19 @@ hipError_t launch_encode(const CodecArgs& a, int d, TileGeom geom, uint8_t* cach
   const long long blocks = (long long)a.batch * a.hkv * a.tiles_touched;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((blocks + kEncWaves - 1) / kEncWaves)), block(kEncWaves * 64);
+  // a tile per wave where there are tiles for 16 waves per compute unit, else a tile per
+  // workgroup (its four waves a step each)
+  const int wg_tile = blocks < 4096 ? 1 : 0;
+  const dim3 grid((unsigned)(wg_tile ? blocks : (blocks + kEncWaves - 1) / kEncWaves)),
+      block(kEncWaves * 64);
   if (d == 64 && f32_in)
-    hipLaunchKernelGGL((encode_kernel<64, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+    hipLaunchKernelGGL((encode_kernel<64, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh, wg_tile);
   else if (d == 64)
-    hipLaunchKernelGGL((encode_kernel<64, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+    hipLaunchKernelGGL((encode_kernel<64, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh, wg_tile);
   else if (d == 128 && f32_in)
-    hipLaunchKernelGGL((encode_kernel<128, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+    hipLaunchKernelGGL((encode_kernel<128, true>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh, wg_tile);
   else if (d == 128)
-    hipLaunchKernelGGL((encode_kernel<128, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh);
+    hipLaunchKernelGGL((encode_kernel<128, false>), grid, block, 0, stream, a, geom, cache, k, v, sb, st, sh, wg_tile);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
