@@ -80,12 +80,24 @@ CodecArgs codec_args(const kvq_layer_desc* d, uint32_t t0, uint32_t ntok) {
   return a;
 }
 
+// Code widths the decode-attention kernels read: 6 to 8 bits. Narrower codebooks
+// (n <= 32) are attended through a copy of the attended tiles re-packed at 6 bits
+// (launch_widen), placed in the workspace after the split partials.
+constexpr int kAttnMinBits = 6;
+int attn_bits(uint32_t n) {
+  const int b = code_bits(n);
+  return b < kAttnMinBits ? kAttnMinBits : b;
+}
+bool attn_widens(const kvq_layer_desc* d) {
+  return code_bits(d->n_bins_k) < kAttnMinBits || code_bits(d->n_bins_v) < kAttnMinBits;
+}
+
 // Decode-attention variant for this shape (see attn_mode in kvq_internal.h). Builds
 // with KVQ_ATTN_ALL_MODES compiled in every variant and read KVQ_ATTN_MODE (0-3, 5-7)
 // to force one, for comparisons.
 int key_table_mode(const kvq_layer_desc* d, uint32_t hq) {
   const int g = (int)(hq / d->num_kv_heads);
-  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
+  const int bk = attn_bits(d->n_bins_k), bv = attn_bits(d->n_bins_v);
 #ifdef KVQ_ATTN_ALL_MODES
   if (const char* e = getenv("KVQ_ATTN_MODE")) {
     const int m = atoi(e);
@@ -121,12 +133,13 @@ void split_plan(uint32_t units, uint32_t seq_len, bool key_table, int* nsplit,
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct AttnLayout {
-  size_t tickets, qrot, ml, acc, total;
+  size_t tickets, qrot, ml, acc, wide, total;
 };
 
 // Workspace: split tickets (must read zero before a call; every call leaves them zero),
-// the rotated queries, then the per-split partial results.
-AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit) {
+// the rotated queries, the per-split partial results, then (narrow codebooks only) the
+// widened copy of the attended tiles.
+AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit, uint32_t seq_len) {
   AttnLayout l;
   const size_t units = (size_t)d->batch * d->num_kv_heads;
   const size_t bh = (size_t)d->batch * hq;
@@ -135,6 +148,12 @@ AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit) {
   l.ml = align256(l.qrot + bh * d->head_dim * sizeof(float));
   l.acc = align256(l.ml + bh * (size_t)nsplit * 2 * sizeof(float));
   l.total = align256(l.acc + bh * (size_t)nsplit * d->head_dim * sizeof(float));
+  l.wide = l.total;
+  if (attn_widens(d)) {
+    const size_t ntiles = (seq_len + kTile - 1) / kTile;
+    const TileGeom gw = tile_geom((int)d->head_dim, attn_bits(d->n_bins_k), attn_bits(d->n_bins_v));
+    l.total = align256(l.wide + units * ntiles * (size_t)gw.bytes);
+  }
   return l;
 }
 
@@ -146,21 +165,21 @@ kvq_status attn_check(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
   const uint32_t g = hq / d->num_kv_heads;
   if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
-  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
-  if (bk < 6 || bk > 8 || bv < 6 || bv > 8) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
 kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, float scale,
-                     void* workspace, size_t workspace_bytes, AttnArgs* a) {
+                     void* workspace, size_t workspace_bytes, AttnArgs* a,
+                     uint8_t** wide = nullptr) {
   kvq_status st = attn_check(d, hq, seq_len);
   if (st != KVQ_OK) return st;
   int nsplit, tps;
   const int ktm = key_table_mode(d, hq);
   split_plan(d->batch * d->num_kv_heads, seq_len, ktm != 0, &nsplit, &tps);
-  const AttnLayout l = attn_layout(d, hq, nsplit);
+  const AttnLayout l = attn_layout(d, hq, nsplit, seq_len);
   if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < l.total)
     return KVQ_ERR_WORKSPACE;
+  if (wide) *wide = (uint8_t*)workspace + l.wide;
   a->batch = (int)d->batch;
   a->hkv = (int)d->num_kv_heads;
   a->hq = (int)hq;
@@ -172,8 +191,8 @@ kvq_status attn_args(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len, flo
   a->tiles_per_split = tps;
   a->n_k = (int)d->n_bins_k;
   a->n_v = (int)d->n_bins_v;
-  a->bk = code_bits(d->n_bins_k);
-  a->bv = code_bits(d->n_bins_v);
+  a->bk = attn_bits(d->n_bins_k);
+  a->bv = attn_bits(d->n_bins_v);
   a->key_table = ktm;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
   a->q_scale = (float)(sc * 1.4426950408889634 / 255.0);
@@ -212,10 +231,23 @@ kvq_status attn_run(const kvq_layer_desc* d, const void* cache, const Paging& pg
                     float scale, void* out, kvq_dtype out_dtype, void* ws, size_t ws_bytes,
                     void* stream, const AppendArgs& app = kNoAppend) {
   AttnArgs a;
-  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a);
+  uint8_t* wide = nullptr;
+  kvq_status st = attn_args(d, hq, seq_len, scale, ws, ws_bytes, &a, &wide);
   if (st != KVQ_OK) return st;
   st = attn_io_check(cache, q, q_dtype, out, out_dtype);
   if (st != KVQ_OK) return st;
+  if (attn_widens(d)) {
+    // a paged pool or a fused append would need the copy to follow the page table or
+    // take the new token: not served for narrow codebooks
+    if (pg.table || app.positions) return KVQ_ERR_UNSUPPORTED;
+    const hipError_t e = launch_widen((const uint8_t*)cache, a.tiles_per_seq, wide,
+                                      (int)d->head_dim, code_bits(d->n_bins_k),
+                                      code_bits(d->n_bins_v), a.batch * a.hkv, a.ntiles,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    a.tiles_per_seq = a.ntiles;
+    cache = wide;
+  }
   a.q = q;
   a.q_f32 = q_dtype == KVQ_F32;
   a.out = out;
@@ -433,7 +465,7 @@ uint32_t kvq_attn_num_splits(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_
 size_t kvq_attn_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint32_t seq_len) {
   const uint32_t s = kvq_attn_num_splits(d, hq, seq_len);
   if (!s) return 0;
-  return attn_layout(d, hq, (int)s).total;
+  return attn_layout(d, hq, (int)s, seq_len).total;
 }
 
 kvq_status kvq_attn_decode(const kvq_layer_desc* d, const void* cache, const void* q,

@@ -190,6 +190,12 @@ struct AppendArgs {
   double inv_sqrt_d, k_bins_per_rad, v_bins_per_rad;  // the layer's encode constants
 };
 
+// Copy of tiles [0, ntiles) of every (sequence, kv head) of a contiguous cache whose
+// angle codes are bk / bv bits wide, with each width below 6 re-packed at 6 bits, into
+// dst laid out [batch][kv head][ntiles][tile bytes at the new widths].
+hipError_t launch_widen(const uint8_t* src, int src_tiles_per_seq, uint8_t* dst, int d, int bk,
+                        int bv, int units, int ntiles, hipStream_t stream);
+
 hipError_t launch_attn_decode(const AttnArgs& a, const AppendArgs& app, int d,
                               const uint8_t* cache, hipStream_t stream);
 // rows = nq * group query rows per kv head (at most 32)

@@ -125,8 +125,19 @@ def test_attention_validation():
     assert _attn(desc, qdt=3) == INVALID
     assert _attn(desc, cache=None) == INVALID
     assert _attn(desc, cache=FAKE + 4) == INVALID  # cache must be 16-byte aligned
-    small = kvq.make_desc(128, 8, 2, 256, 32, 64)  # 5-bit key angle codes
-    assert _attn(small) == UNSUPPORTED
+    # 5-bit key angle codes: attended through a copy re-packed at 6 bits, placed in the
+    # workspace after the partials (2 tiles per (sequence, kv head) for 100 tokens)
+    small = kvq.make_desc(128, 8, 2, 256, 32, 64)
+    wide = kvq.make_desc(128, 8, 2, 256, 64, 64)
+    extra = kvq.attn_workspace_bytes(small, 32, 100) - kvq.attn_workspace_bytes(wide, 32, 100)
+    assert extra == 2 * 8 * 2 * kvq.tile_bytes(128, 64, 64)
+    assert _attn(small, ws_bytes=kvq.attn_workspace_bytes(small, 32, 100) - 1) == WORKSPACE
+    # a paged pool is not served at these widths (rejected before any device work)
+    paged = lambda desc: lib.kvq_attn_decode_paged(
+        ctypes.byref(desc), FAKE, ctypes.byref(kvq.Paging(FAKE, 4, 10)), FAKE, 0, 32, None,
+        100, 0.0, FAKE, 0, FAKE, 1 << 30, None)
+    assert paged(small) == UNSUPPORTED
+    assert paged(kvq.make_desc(128, 8, 2, 256, 128, 17)) == UNSUPPORTED  # 5-bit value codes
     d64 = kvq.make_desc(64, 4, 1, 256, 256, 33)  # 8-bit / 6-bit: supported shape
     assert _attn(d64, hq=32, ws=None) == WORKSPACE
 
@@ -282,6 +293,7 @@ def test_fused_append_attention_validation():
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(None, 4, 10))) == INVALID
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
     assert _fused(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
+    assert _fused(kvq.make_desc(128, 8, 2, 256, 128, 3)) == UNSUPPORTED  # 2-bit value codes
 
 
 def test_static_scratch_entry_point_rejects_before_any_device_work():
@@ -303,12 +315,14 @@ def test_static_scratch_entry_point_rejects_before_any_device_work():
 
 def test_sizes_are_zero_for_shapes_attention_does_not_serve():
     """Workspace and split helpers agree with kvq_attn_decode: 0 where it would return
-    UNSUPPORTED (5-bit codes, G = 16, d = 256) or INVALID."""
+    UNSUPPORTED (G = 16, d = 256) or INVALID; narrow codebooks are served."""
     ok = kvq.make_desc(128, 2, 1, 256, 128, 64)
     assert kvq.attn_workspace_bytes(ok, 8, 256) > 0
-    for desc, hq in ((kvq.make_desc(128, 2, 1, 256, 32, 64), 8),     # 5-bit key codes
-                     (kvq.make_desc(128, 2, 1, 256, 128, 17), 8),    # 5-bit value codes
-                     (kvq.make_desc(128, 2, 1, 256, 128, 64), 32),   # G = 16
+    for nk, nv in ((32, 64), (128, 17), (2, 2)):  # 5-bit keys, 5-bit values, 1-bit both
+        narrow = kvq.make_desc(128, 2, 1, 256, nk, nv)
+        assert kvq.attn_workspace_bytes(narrow, 8, 256) > kvq.attn_workspace_bytes(ok, 8, 256)
+        assert kvq.attn_num_splits(narrow, 8, 256) > 0
+    for desc, hq in ((kvq.make_desc(128, 2, 1, 256, 128, 64), 32),   # G = 16
                      (kvq.make_desc(256, 2, 1, 256, 128, 64), 8),    # d = 256
                      (kvq.make_desc(128, 2, 1, 256, 128, 64), 7)):   # Hq not a multiple
         assert kvq.attn_workspace_bytes(desc, hq, 256) == 0
@@ -318,7 +332,7 @@ def test_sizes_are_zero_for_shapes_attention_does_not_serve():
 
 def test_workspace_helper_reports_the_shape_status():
     with pytest.raises(kvq.KvqError, match="UNSUPPORTED"):
-        kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 32, 64), 8, 256, "cpu")
+        kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 128, 64), 32, 256, "cpu")  # G = 16
     with pytest.raises(kvq.KvqError, match="CAPACITY"):
         kvq.alloc_workspace(kvq.make_desc(128, 2, 1, 256, 128, 64), 8, 300, "cpu")
 

@@ -185,16 +185,50 @@ def test_attention_code_widths(dev, nk, nv):
     run_full_check(dev, k, v, q, d, nk, nv, layer=1, tag=f"n=({nk},{nv}) d{d}")
 
 
-@pytest.mark.parametrize("nk,nv", [(2, 3), (5, 17), (16, 8), (31, 32)])
-def test_encode_decode_small_codebooks(dev, nk, nv):
-    torch.manual_seed(nk * nv)
-    k = torch.randn(1, 100, 3, 128, device=dev).half()
-    v = torch.randn(1, 100, 3, 128, device=dev).half()
-    run_full_check(dev, k, v, None, 128, nk, nv, attn_checks=False, tag=f"n=({nk},{nv})")
-    desc = kvq.make_desc(128, 3, 1, 100, nk, nv)
-    cache = kvq.alloc_cache(desc, dev)
+@pytest.mark.parametrize("nk,nv,d,g", [(2, 3, 128, 4), (5, 17, 64, 2), (16, 8, 128, 8),
+                                        (31, 32, 128, 1), (32, 64, 128, 4), (200, 5, 64, 4)])
+def test_small_codebooks(dev, nk, nv, d, g):
+    """Codebooks of at most 32 bins (1- to 5-bit codes, K only, V only or both): codes,
+    dequantisation and attention (through the 6-bit widened copy) against the oracle,
+    over 100 tokens (a ragged second tile)."""
+    torch.manual_seed(nk * nv + d)
+    k = torch.randn(1, 100, 3, d, device=dev).half()
+    v = torch.randn(1, 100, 3, d, device=dev).half()
+    q = torch.randn(1, 3 * g, d, device=dev).half()
+    run_full_check(dev, k, v, q, d, nk, nv, tag=f"n=({nk},{nv}) d={d} G={g}")
+
+
+def test_small_codebooks_varlen_static_and_paged(dev):
+    """Narrow codebooks through the ragged-batch and allocation-free entry points (against
+    the oracle per sequence), and the paged form's UNSUPPORTED."""
+    d, hkv, g, nk, nv, t = 128, 2, 4, 24, 12, 200
+    torch.manual_seed(5)
+    k = torch.randn(3, t, hkv, d, device=dev).half()
+    v = torch.randn(3, t, hkv, d, device=dev).half()
+    q = torch.randn(3, hkv * g, d, device=dev).half()
+    desc = kvq.make_desc(d, hkv, 3, t, nk, nv)
+    cache = torch.zeros(kvq.cache_bytes(desc), dtype=torch.uint8, device=dev)
+    kvq.encode(desc, cache, k, v, 0)
+    torch.cuda.synchronize()
+    got = unpack(cache.cpu().numpy(), d, nk, nv, 3, hkv, t, 0, t)
+    kh, vh = oracle_dequant(got, oc.layer_signs(0, 0, d), nk, nv)
+    lens = [200, 65, 1]
+    out = kvq.attn_decode_varlen(desc, cache, q, torch.tensor(lens, dtype=torch.int32,
+                                                              device=dev), t,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        ref = oc.attention(np64(q[b:b + 1]), kh[b:b + 1, :n], vh[b:b + 1, :n])
+        compare_attention(np64(out[b:b + 1]), ref, f"narrow varlen b={b} len={n}")
+    st = kvq.attn_decode_static(desc, cache, q, 150, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    compare_attention(np64(st), oc.attention(np64(q), kh[:, :150], vh[:, :150]),
+                      "narrow static 150")
+    pages = torch.arange(12, dtype=torch.int32, device=dev).reshape(3, 4)
+    pool = torch.zeros(kvq.paged_pool_bytes(desc, 12), dtype=torch.uint8, device=dev)
     with pytest.raises(kvq.KvqError, match="UNSUPPORTED"):
-        kvq.attn_decode(desc, cache, torch.randn(1, 3, 128, device=dev).half(), 100)
+        kvq.attn_decode_paged(desc, pool, kvq.make_paging(pages, 12), q, t,
+                              seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev))
 
 
 @pytest.mark.parametrize("seq_len", [1, 63, 64, 65, 999, 1000])
