@@ -205,11 +205,15 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  * workspace: device buffer of at least kvq_attn_workspace_bytes(desc, Hq, seq_len)
  *   bytes, 256-byte aligned, owned by the caller. It must be zero-filled once after
  *   allocation; every call that completes leaves it ready for the next (its split
- *   counters back at zero). It holds the rotated queries and split partials. Calls
- *   that share one workspace must not run concurrently (one stream).
- * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; angle codes of 6 to 8 bits
- *   (n in [33, 256]) for K and V; 1 <= seq_len <= capacity. kvq_attn_workspace_bytes
- *   returns 0 for shapes outside this set (and for invalid arguments).
+ *   counters back at zero). It holds the rotated queries and split partials and, for a
+ *   layer with n <= 32 for K or V, a copy of the first ceil(seq_len / 64) tiles of every
+ *   (sequence, kv head) with those 1- to 5-bit angle codes re-packed at 6 bits (the
+ *   kernels read 6- to 8-bit codes; the copy is written by a launch of its own on the
+ *   same stream before the attention launch). Calls that share one workspace must not
+ *   run concurrently (one stream).
+ * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; every n in [2, 256] for K and V;
+ *   1 <= seq_len <= capacity. kvq_attn_workspace_bytes returns 0 for shapes outside
+ *   this set (and for invalid arguments).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
  */
 size_t kvq_attn_workspace_bytes(const kvq_layer_desc* desc, uint32_t num_q_heads,
@@ -315,7 +319,8 @@ kvq_status kvq_decode_paged(const kvq_layer_desc* desc, const void* pool,
 
 /* Decode attention over a paged cache; seq_lens may be null (every sequence attends to
  * max_seq_len tokens) or a device array of per-sequence lengths as for
- * kvq_attn_decode_varlen. Workspace as kvq_attn_decode at seq_len = max_seq_len. */
+ * kvq_attn_decode_varlen. Workspace as kvq_attn_decode at seq_len = max_seq_len.
+ * Layers with n <= 32 for K or V return UNSUPPORTED (no widened copy of a pool). */
 kvq_status kvq_attn_decode_paged(const kvq_layer_desc* desc, const void* pool,
                                  const kvq_paging* paging, const void* q, kvq_dtype q_dtype,
                                  uint32_t num_q_heads, const uint32_t* seq_lens,
@@ -351,6 +356,8 @@ kvq_status kvq_attn_multi_varlen(const kvq_layer_desc* desc, const void* cache, 
  * waves stream their tiles.
  * paging: null for a contiguous cache, else the pool's page table as for the *_paged
  * calls (cache is then the pool). Workspace as kvq_attn_decode at seq_len = max_seq_len.
+ * Layers with n <= 32 for K or V return UNSUPPORTED (the token would have to be coded
+ * into the widened copy as well): call kvq_append, then kvq_attn_decode_varlen.
  * Errors: as kvq_attn_decode (max_seq_len in [1, capacity]) and kvq_append.
  */
 kvq_status kvq_attn_decode_append(const kvq_layer_desc* desc, void* cache,

@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--tokens", type=int, default=4096)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--grid", default="64,128,256",
-                    help="codebook sizes; decode attention takes 6- to 8-bit codes (n in [33, 256])")
+                    help="codebook sizes (n in [2, 256]; n <= 32 is attended through a 6-bit copy)")
     ap.add_argument("--json", action="store_true")
     args = ap.parse_args()
     cfg = get(args.workload)
