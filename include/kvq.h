@@ -264,8 +264,10 @@ kvq_status kvq_attn_decode_varlen(const kvq_layer_desc* desc, const void* cache,
  * workspace: at least kvq_attn_multi_workspace_bytes(desc, Hq, num_queries, seq_len)
  *   bytes, 256-byte aligned, zero-filled once after allocation; every completed call
  *   leaves its split counters at zero. Calls sharing a workspace must not overlap.
- * Supported: d in {64, 128}; G in {1, 2, 4, 8}; num_queries * G <= 32; angle codes of 6
- *   to 8 bits for K and V; 1 <= num_queries <= seq_len <= capacity.
+ * Supported: d in {64, 128}; G in {1, 2, 4, 8}; num_queries * G <= 32; every n in
+ *   [2, 256] for K and V (n <= 32 through the widened copy described at
+ *   kvq_attn_workspace_bytes, after the partials in the workspace; not for the paged
+ *   form); 1 <= num_queries <= seq_len <= capacity.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, CAPACITY, WORKSPACE, HIP.
  */
 size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* desc, uint32_t num_q_heads,

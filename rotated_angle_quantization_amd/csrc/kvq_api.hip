@@ -271,8 +271,6 @@ kvq_status multi_check(const kvq_layer_desc* d, uint32_t hq, uint32_t nq, uint32
   if (!head_dim_supported(d->head_dim)) return KVQ_ERR_UNSUPPORTED;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
   if ((uint64_t)nq * g > kMultiMaxRows) return KVQ_ERR_UNSUPPORTED;
-  const int bk = code_bits(d->n_bins_k), bv = code_bits(d->n_bins_v);
-  if (bk < 6 || bk > 8 || bv < 6 || bv > 8) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -291,9 +289,11 @@ void multi_split_plan(uint32_t units, uint32_t seq_len, int* nsplit, int* tiles_
 }
 
 struct MultiLayout {
-  size_t tickets, ml, acc, total;
+  size_t tickets, ml, acc, wide, total;
 };
-MultiLayout multi_layout(const kvq_layer_desc* d, uint32_t rows, int nsplit) {
+// Split counters, partials, then (narrow codebooks) the widened tile copy, as for
+// decode attention.
+MultiLayout multi_layout(const kvq_layer_desc* d, uint32_t rows, int nsplit, uint32_t seq_len) {
   MultiLayout l;
   const size_t units = (size_t)d->batch * d->num_kv_heads;
   const size_t m = (size_t)multi_rows(rows);
@@ -301,6 +301,12 @@ MultiLayout multi_layout(const kvq_layer_desc* d, uint32_t rows, int nsplit) {
   l.ml = align256(units * sizeof(unsigned));
   l.acc = align256(l.ml + units * nsplit * m * 2 * sizeof(float));
   l.total = align256(l.acc + units * nsplit * m * d->head_dim * sizeof(float));
+  l.wide = l.total;
+  if (attn_widens(d)) {
+    const size_t ntiles = (seq_len + kTile - 1) / kTile;
+    const TileGeom gw = tile_geom((int)d->head_dim, attn_bits(d->n_bins_k), attn_bits(d->n_bins_v));
+    l.total = align256(l.wide + units * ntiles * (size_t)gw.bytes);
+  }
   return l;
 }
 
@@ -544,7 +550,7 @@ size_t kvq_attn_multi_workspace_bytes(const kvq_layer_desc* d, uint32_t hq, uint
   if (multi_check(d, hq, nq, seq_len) != KVQ_OK) return 0;
   int nsplit, tps;
   multi_split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
-  return multi_layout(d, nq * (hq / d->num_kv_heads), nsplit).total;
+  return multi_layout(d, nq * (hq / d->num_kv_heads), nsplit, seq_len).total;
 }
 
 }  // extern "C"
@@ -560,7 +566,7 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   int nsplit, tps;
   multi_split_plan(d->batch * d->num_kv_heads, seq_len, &nsplit, &tps);
   const uint32_t g = hq / d->num_kv_heads;
-  const MultiLayout l = multi_layout(d, nq * g, nsplit);
+  const MultiLayout l = multi_layout(d, nq * g, nsplit, seq_len);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < l.total) return KVQ_ERR_WORKSPACE;
   if (!cache || !q || !out || ((uintptr_t)cache % 16)) return KVQ_ERR_INVALID_ARGUMENT;
   if ((q_dtype != KVQ_F16 && q_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
@@ -580,8 +586,8 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   a.tiles_per_split = tps;
   a.n_k = (int)d->n_bins_k;
   a.n_v = (int)d->n_bins_v;
-  a.bk = code_bits(d->n_bins_k);
-  a.bv = code_bits(d->n_bins_v);
+  a.bk = attn_bits(d->n_bins_k);
+  a.bv = attn_bits(d->n_bins_v);
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d->head_dim);
   a.q_scale = (float)(sc * 1.4426950408889634);  // the key radius carries s / 255 here
   a.inv_sqrt_d = (float)(1.0 / sqrt((double)d->head_dim));
@@ -596,6 +602,16 @@ kvq_status multi_run(const kvq_layer_desc* d, const void* cache, const Paging& p
   a.part_acc = (float*)(base + l.acc);
   a.seq_lens = seq_lens;
   a.pg = pg;
+  if (attn_widens(d)) {
+    if (pg.table) return KVQ_ERR_UNSUPPORTED;  // no widened copy of a pool
+    const hipError_t e = launch_widen((const uint8_t*)cache, a.tiles_per_seq, (uint8_t*)ws + l.wide,
+                                      (int)d->head_dim, code_bits(d->n_bins_k),
+                                      code_bits(d->n_bins_v), a.batch * a.hkv, a.ntiles,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    a.tiles_per_seq = a.ntiles;
+    cache = (const uint8_t*)ws + l.wide;
+  }
   // one launch for up to 32 query rows: the 16-row kernel, or the 32-row one, which
   // reads the cache once for all of them
   const uint32_t per = 32 / g;

@@ -222,7 +222,14 @@ def test_attention_multi_validation():
     assert _multi(desc, ws_bytes=need - 1) == WORKSPACE
     assert _multi(desc, cache=FAKE + 4) == INVALID
     assert _multi(desc, q=FAKE + 2) == INVALID
-    assert _multi(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
+    # 5-bit key codes: the widened copy follows the partials in the workspace
+    small = kvq.make_desc(128, 8, 2, 256, 32, 64)
+    wide = kvq.make_desc(128, 8, 2, 256, 64, 64)
+    assert (kvq.attn_multi_workspace_bytes(small, 32, 4, 100)
+            - kvq.attn_multi_workspace_bytes(wide, 32, 4, 100)) == 2 * 8 * 2 * kvq.tile_bytes(128, 64, 64)
+    assert lib.kvq_attn_multi_paged(ctypes.byref(small), FAKE, ctypes.byref(kvq.Paging(FAKE, 4, 10)),
+                                    FAKE, 0, 32, 4, None, 100, 0.0, FAKE, 0, FAKE, 1 << 30,
+                                    None) == UNSUPPORTED
     assert kvq.attn_multi_workspace_bytes(desc, 32, 9, 100) == 0
 
 

@@ -80,6 +80,13 @@ def test_multi_query_code_widths_dtypes_and_scale(dev, nk, nv):
               scale=0.07)
 
 
+@pytest.mark.parametrize("d,g,nq,nk,nv", [(128, 4, 4, 32, 64), (64, 2, 8, 128, 5),
+                                           (128, 8, 3, 3, 17), (128, 1, 16, 24, 12)])
+def test_multi_query_narrow_codebooks(dev, d, g, nq, nk, nv):
+    """Codebooks of at most 32 bins (1- to 5-bit codes) through the 6-bit widened copy."""
+    run_multi(dev, d, g, nq, 333, nk=nk, nv=nv, cap=400)
+
+
 def test_multi_query_one_query_agrees_with_decode_attention(dev):
     """With one query token the result is single-query decode attention (fp16 matrix
     operands against the decode kernel's fp32 arithmetic: close, not bitwise)."""
