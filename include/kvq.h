@@ -206,7 +206,7 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  *   bytes, 256-byte aligned, owned by the caller. It must be zero-filled once after
  *   allocation; every call that completes leaves it ready for the next (its split
  *   counters back at zero). It holds the rotated queries and split partials and, for a
- *   layer with n <= 32 for K or V, a copy of the first ceil(seq_len / 64) tiles of every
+ *   layer with n <= 32 for K or V, B lengths and a copy of the first ceil(seq_len / 64) tiles of every
  *   (sequence, kv head) with those 1- to 5-bit angle codes re-packed at 6 bits (the
  *   kernels read 6- to 8-bit codes; the copy is written by a launch of its own on the
  *   same stream before the attention launch). Calls that share one workspace must not
@@ -358,8 +358,10 @@ kvq_status kvq_attn_multi_varlen(const kvq_layer_desc* desc, const void* cache, 
  * waves stream their tiles.
  * paging: null for a contiguous cache, else the pool's page table as for the *_paged
  * calls (cache is then the pool). Workspace as kvq_attn_decode at seq_len = max_seq_len.
- * Layers with n <= 32 for K or V return UNSUPPORTED (the token would have to be coded
- * into the widened copy as well): call kvq_append, then kvq_attn_decode_varlen.
+ * Layers with n <= 32 for K or V run as kvq_append, a launch that writes the lengths
+ * min(positions[b] + 1, max_seq_len) into the workspace, and kvq_attn_decode_varlen
+ * over the widened copy (same results, three launches; every argument is checked before
+ * the cache is written); with a paged pool they return UNSUPPORTED.
  * Errors: as kvq_attn_decode (max_seq_len in [1, capacity]) and kvq_append.
  */
 kvq_status kvq_attn_decode_append(const kvq_layer_desc* desc, void* cache,

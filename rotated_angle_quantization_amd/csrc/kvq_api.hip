@@ -133,12 +133,12 @@ void split_plan(uint32_t units, uint32_t seq_len, bool key_table, int* nsplit,
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct AttnLayout {
-  size_t tickets, qrot, ml, acc, wide, total;
+  size_t tickets, qrot, ml, acc, wide, lens, total;
 };
 
 // Workspace: split tickets (must read zero before a call; every call leaves them zero),
 // the rotated queries, the per-split partial results, then (narrow codebooks only) the
-// widened copy of the attended tiles.
+// widened copy of the attended tiles and the fused decode step's per-sequence lengths.
 AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit, uint32_t seq_len) {
   AttnLayout l;
   const size_t units = (size_t)d->batch * d->num_kv_heads;
@@ -148,11 +148,12 @@ AttnLayout attn_layout(const kvq_layer_desc* d, uint32_t hq, int nsplit, uint32_
   l.ml = align256(l.qrot + bh * d->head_dim * sizeof(float));
   l.acc = align256(l.ml + bh * (size_t)nsplit * 2 * sizeof(float));
   l.total = align256(l.acc + bh * (size_t)nsplit * d->head_dim * sizeof(float));
-  l.wide = l.total;
+  l.wide = l.lens = l.total;
   if (attn_widens(d)) {
     const size_t ntiles = (seq_len + kTile - 1) / kTile;
     const TileGeom gw = tile_geom((int)d->head_dim, attn_bits(d->n_bins_k), attn_bits(d->n_bins_v));
-    l.total = align256(l.wide + units * ntiles * (size_t)gw.bytes);
+    l.lens = align256(l.wide + units * ntiles * (size_t)gw.bytes);
+    l.total = align256(l.lens + (size_t)d->batch * sizeof(unsigned));
   }
   return l;
 }
@@ -528,6 +529,24 @@ kvq_status kvq_attn_decode_append(const kvq_layer_desc* d, void* cache,
   if (paging) {
     const kvq_status sp = paging_args(d, paging, &pg);
     if (sp != KVQ_OK) return sp;
+  }
+  if (attn_widens(d)) {
+    // narrow codebooks: kvq_append, the lengths positions + 1, then the ragged attention
+    // over the widened copy (every argument checked before the cache is written)
+    if (pg.table) return KVQ_ERR_UNSUPPORTED;
+    AttnArgs chk;
+    kvq_status s2 = attn_args(d, hq, max_seq_len, scale, ws, ws_bytes, &chk);
+    if (s2 == KVQ_OK) s2 = attn_io_check(cache, q, q_dtype, out, out_dtype);
+    if (s2 == KVQ_OK && !cache) s2 = KVQ_ERR_INVALID_ARGUMENT;
+    if (s2 != KVQ_OK) return s2;
+    s2 = append_impl(d, cache, kNoPaging, k, v, in_dtype, sb, sh, positions, stream);
+    if (s2 != KVQ_OK) return s2;
+    unsigned* lens = (unsigned*)((char*)ws + attn_layout(d, hq, chk.nsplit, max_seq_len).lens);
+    if (launch_lengths(positions, lens, (int)d->batch, max_seq_len, (hipStream_t)stream) !=
+        hipSuccess)
+      return KVQ_ERR_HIP;
+    return attn_run(d, cache, kNoPaging, q, q_dtype, hq, max_seq_len, lens, scale, out,
+                    out_dtype, ws, ws_bytes, stream);
   }
   const CodecArgs c = codec_args(d, 0, 1);
   AppendArgs app;

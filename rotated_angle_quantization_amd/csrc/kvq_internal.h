@@ -195,6 +195,9 @@ struct AppendArgs {
 // dst laid out [batch][kv head][ntiles][tile bytes at the new widths].
 hipError_t launch_widen(const uint8_t* src, int src_tiles_per_seq, uint8_t* dst, int d, int bk,
                         int bv, int units, int ntiles, hipStream_t stream);
+// lens[b] = min(positions[b] + 1, max_len) for b < batch (device arrays).
+hipError_t launch_lengths(const unsigned* positions, unsigned* lens, int batch, unsigned max_len,
+                          hipStream_t stream);
 
 hipError_t launch_attn_decode(const AttnArgs& a, const AppendArgs& app, int d,
                               const uint8_t* cache, hipStream_t stream);

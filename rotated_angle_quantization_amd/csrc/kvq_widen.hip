@@ -103,7 +103,25 @@ __global__ void __launch_bounds__(64) widen_kernel(const uint8_t* __restrict__ s
   }
 }
 
+// lens[b] = min(positions[b] + 1, max_len), without wrapping at 2^32 - 1.
+__global__ void lengths_kernel(const unsigned* __restrict__ positions, unsigned* __restrict__ lens,
+                               int batch, unsigned max_len) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) {
+    const unsigned p = positions[b];
+    lens[b] = p >= max_len ? max_len : p + 1u;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_lengths(const unsigned* positions, unsigned* lens, int batch, unsigned max_len,
+                          hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lengths_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream,
+                     positions, lens, batch, max_len);
+  return hipGetLastError();
+}
 
 hipError_t launch_widen(const uint8_t* src, int src_tiles_per_seq, uint8_t* dst, int d, int bk,
                         int bv, int units, int ntiles, hipStream_t stream) {

@@ -126,11 +126,12 @@ def test_attention_validation():
     assert _attn(desc, cache=None) == INVALID
     assert _attn(desc, cache=FAKE + 4) == INVALID  # cache must be 16-byte aligned
     # 5-bit key angle codes: attended through a copy re-packed at 6 bits, placed in the
-    # workspace after the partials (2 tiles per (sequence, kv head) for 100 tokens)
+    # workspace after the partials (2 tiles per (sequence, kv head) for 100 tokens), then
+    # 256 bytes for the fused step's sequence lengths
     small = kvq.make_desc(128, 8, 2, 256, 32, 64)
     wide = kvq.make_desc(128, 8, 2, 256, 64, 64)
     extra = kvq.attn_workspace_bytes(small, 32, 100) - kvq.attn_workspace_bytes(wide, 32, 100)
-    assert extra == 2 * 8 * 2 * kvq.tile_bytes(128, 64, 64)
+    assert extra == 2 * 8 * 2 * kvq.tile_bytes(128, 64, 64) + 256
     assert _attn(small, ws_bytes=kvq.attn_workspace_bytes(small, 32, 100) - 1) == WORKSPACE
     # a paged pool is not served at these widths (rejected before any device work)
     paged = lambda desc: lib.kvq_attn_decode_paged(
@@ -299,8 +300,14 @@ def test_fused_append_attention_validation():
     assert _fused(desc, q=None) == INVALID
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(None, 4, 10))) == INVALID
     assert _fused(desc, paging=ctypes.byref(kvq.Paging(FAKE, 3, 10))) == INVALID
-    assert _fused(kvq.make_desc(128, 8, 2, 256, 32, 64)) == UNSUPPORTED  # 5-bit key codes
-    assert _fused(kvq.make_desc(128, 8, 2, 256, 128, 3)) == UNSUPPORTED  # 2-bit value codes
+    # narrow codebooks: served on a contiguous cache (append, then the widened copy),
+    # not on a paged pool
+    pg4 = ctypes.byref(kvq.Paging(FAKE, 4, 10))
+    assert _fused(kvq.make_desc(128, 8, 2, 256, 32, 64), paging=pg4) == UNSUPPORTED  # 5-bit K
+    assert _fused(kvq.make_desc(128, 8, 2, 256, 128, 3), paging=pg4) == UNSUPPORTED  # 2-bit V
+    narrow = kvq.make_desc(128, 8, 2, 256, 32, 64)
+    assert _fused(narrow, ws_bytes=kvq.attn_workspace_bytes(narrow, 32, 100) - 1) == WORKSPACE
+    assert _fused(narrow, q=None) == INVALID
 
 
 def test_static_scratch_entry_point_rejects_before_any_device_work():

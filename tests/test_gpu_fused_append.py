@@ -53,9 +53,11 @@ def step_both(desc, cache, kn, vn, pos, q, maxlen, ws):
 
 
 # (d, G, n_K, n_V): half table (n a power of two), full table, no table (n_K = 200 does
-# not fit at G = 8), for d = 128 and d = 64
+# not fit at G = 8), for d = 128 and d = 64; then codebooks of at most 32 bins (append,
+# then attention over the 6-bit widened copy)
 CASES = [(128, 4, 128, 64), (128, 4, 100, 40), (128, 8, 200, 256), (64, 8, 128, 64),
-         (64, 1, 256, 128), (64, 4, 100, 40), (64, 8, 200, 100)]
+         (64, 1, 256, 128), (64, 4, 100, 40), (64, 8, 200, 100),
+         (128, 4, 32, 64), (64, 2, 100, 5), (128, 8, 3, 17)]
 
 
 @pytest.mark.parametrize("d,g,nk,nv", CASES)
