@@ -206,11 +206,11 @@ kvq_status kvq_decode(const kvq_layer_desc* desc, const void* cache, void* k_out
  *   bytes, 256-byte aligned, owned by the caller. It must be zero-filled once after
  *   allocation; every call that completes leaves it ready for the next (its split
  *   counters back at zero). It holds the rotated queries and split partials and, for a
- *   layer with n <= 32 for K or V, B lengths and a copy of the first ceil(seq_len / 64) tiles of every
- *   (sequence, kv head) with those 1- to 5-bit angle codes re-packed at 6 bits (the
- *   kernels read 6- to 8-bit codes; the copy is written by a launch of its own on the
- *   same stream before the attention launch). Calls that share one workspace must not
- *   run concurrently (one stream).
+ *   layer with n <= 32 for K or V, a copy of the first ceil(seq_len / 64) tiles of
+ *   every (sequence, kv head) with those 1- to 5-bit angle codes re-packed at 6 bits
+ *   (the kernels read 6- to 8-bit codes; the copy is written by a launch of its own on
+ *   the same stream before the attention launch) and B lengths for the fused step.
+ *   Calls that share one workspace must not run concurrently (one stream).
  * Supported: Hq = G * Hkv with G in {1, 2, 4, 8}; every n in [2, 256] for K and V;
  *   1 <= seq_len <= capacity. kvq_attn_workspace_bytes returns 0 for shapes outside
  *   this set (and for invalid arguments).
